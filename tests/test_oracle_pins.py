@@ -1,0 +1,516 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: expected values come from
+exact rational arithmetic (Python fractions), the pages' own rules and
+constants (tests/golden/format_constants.json, each entry cited), closed
+forms, or torch's float8_e4m3fn conversion.  A mistake in the oracle's
+exponent rule, rounding, tie handling, sign rule, nibble order, layout,
+paged addressing, gating or RoPE indexing fails at least one test below.
+
+Sources: [P1] docs page "vllm.v1.attention.ops.mxfp4_mla.store";
+[P2] docs page "vllm.models.deepseek_v41.common.ops.fused_compress_quant_cache";
+[P3] pull request "Add an mxfp4_mla KV cache for rope-free sparse MLA".
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.exact_ref import (
+    bf16_bits_of_fraction,
+    bf16_fraction,
+    ceil_log2,
+    f32_bits,
+    fp32_quotient_is_zero,
+    golden,
+    midpoint_index,
+)
+
+G = golden()
+MIDS = G["e2m1_midpoints"]
+STRICT = G["e2m1_midpoint_strict"]
+GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2),
+        Fraction(3), Fraction(4), Fraction(6)]
+TWO = Fraction(2)
+
+
+def expected_mxfp4_code(x: Fraction, xbits: int, e: int) -> int:
+    """Code of one element under scale 2^e: the pages' midpoint count on the
+    exact quotient, sign bit when the fp32 quotient is below zero."""
+    q = x / TWO ** e
+    if fp32_quotient_is_zero(x, e):
+        return 0
+    idx = midpoint_index(abs(q), MIDS, STRICT)
+    return idx | (8 if (xbits & 0x8000) else 0)
+
+
+def expected_scale_exponent(amax: Fraction) -> int:
+    """Smallest e with 2^e >= amax/6, floored at -126 (bit-pattern reading of a
+    subnormal amax/6)."""
+    return max(ceil_log2(amax / 6), -126)
+
+
+def flat_store(src: np.ndarray) -> np.ndarray:
+    n = src.shape[0]
+    cache = np.full(n * 272, 0xA5, dtype=np.uint8)
+    oracle.mxfp4_store(src, np.arange(n, dtype=np.int64), cache, 1, n, n)
+    return cache.reshape(n, 272)
+
+
+def nibble(rows: np.ndarray, token: int, elem: int) -> int:
+    b = int(rows[token, elem // 2])
+    return (b & 0xF) if elem % 2 == 0 else (b >> 4)
+
+
+# ---------------------------------------------------------------- constants
+
+def test_format_constants():
+    assert oracle.row_bytes(512) == G["row_bytes_512"] == 512 // 2 + 512 // 32
+    assert round(G["bf16_row_bytes_512"] / G["row_bytes_512"], 2) == float(G["capacity_ratio"])
+    assert oracle.row_bytes(128) == 68 and oracle.row_bytes(1024) == 544
+    assert oracle.row_bytes(100) < 0  # not a multiple of the group
+    # E2M1 grid: midpoints are exactly halfway between consecutive magnitudes.
+    assert [float((GRID[i] + GRID[i + 1]) / 2) for i in range(7)] == MIDS
+    assert float(GRID[-1]) == G["e2m1_max"]
+    # E4M3 extremes used by the variants.
+    assert oracle.e4m3_value(0x7E) == G["e4m3_max"]
+    assert oracle.e4m3_value(0x01) == G["nvfp4_scale_min"]  # 2^-9: least subnormal
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6              # least normal
+
+
+# ---------------------------------------------------------------- exponent + codes
+
+@pytest.fixture(scope="module")
+def solo_sweep():
+    """All 65,536 bf16 patterns, each alone in its group (rest +0)."""
+    pats = np.arange(65536, dtype=np.uint32).reshape(4096, 16)
+    src = np.zeros((4096, 512), dtype=np.uint16)
+    src[:, ::32] = pats.astype(np.uint16)
+    return pats, flat_store(src)
+
+
+def test_scale_exponent_exhaustive(solo_sweep):
+    pats, rows = solo_sweep
+    for t in range(4096):
+        for g in range(16):
+            p = int(pats[t, g])
+            x = bf16_fraction(p)
+            got = int(rows[t, 256 + g])
+            if x is None:
+                assert got == 0xFF, hex(p)  # reading R6
+            elif x == 0:
+                assert got == G["zero_group_scale_byte"], hex(p)
+            else:
+                assert got == expected_scale_exponent(abs(x)) + G["e8m0_bias"], hex(p)
+
+
+def test_bit_pattern_rule_agrees_with_definition():
+    """The store page computes the exponent on the fp32 bit pattern of
+    amax/6; for every positive finite bf16 amax it equals the exact
+    definition (floored at -126), so the reading of how amax/6 is formed
+    does not matter."""
+    for p in range(1, 0x7F80):
+        a = np.float32(float(bf16_fraction(p)))
+        bits = f32_bits(np.float32(a) / np.float32(6.0))
+        exp_field, mant = (bits >> 23) & 0xFF, bits & 0x7FFFFF
+        rule = exp_field - 127 + (1 if mant else 0)
+        assert rule == expected_scale_exponent(Fraction(float(a))), hex(p)
+        assert oracle.ceil_pow2_exponent(float(np.float32(a) / np.float32(6.0))) == rule
+
+
+def test_solo_codes_exhaustive(solo_sweep):
+    pats, rows = solo_sweep
+    for t in range(4096):
+        for g in range(16):
+            p = int(pats[t, g])
+            x = bf16_fraction(p)
+            got = nibble(rows, t, 32 * g)
+            if x is None or x == 0:
+                assert got == 0, hex(p)
+                continue
+            e = expected_scale_exponent(abs(x))
+            assert got == expected_mxfp4_code(x, p, e), hex(p)
+            # the amax element's magnitude lands in (3, 6] unless the floor hit
+            if abs(x) / 6 >= TWO ** -126:
+                assert got & 7 >= 5, hex(p)
+            # the other 31 elements are +0
+            assert all(nibble(rows, t, 32 * g + j) == 0 for j in range(1, 32))
+
+
+@pytest.mark.parametrize("k", [0, 125, -126, 17, -100])
+def test_anchored_sweep(k):
+    """Groups [6*2^k, x, ...] fix e = k; every finite bf16 x with
+    |x| <= 6*2^k is swept (k = 125 reaches the fp32 underflow region of the
+    quotient, k = -126 the subnormal inputs)."""
+    anchor = Fraction(6) * TWO ** k
+    abits = bf16_bits_of_fraction(anchor)
+    cands = [p for p in range(65536)
+             if bf16_fraction(p) is not None and abs(bf16_fraction(p)) <= anchor]
+    per = 31
+    ngroups = -(-len(cands) // per)
+    ntok = -(-ngroups // 16)
+    src = np.zeros((ntok, 512), dtype=np.uint16)
+    flat = src.reshape(-1, 32)
+    flat[:ngroups, 0] = abits
+    for i, p in enumerate(cands):
+        flat[i // per, 1 + i % per] = p
+    rows = flat_store(src)
+    for gi in range(ngroups):
+        t, g = divmod(gi, 16)
+        assert int(rows[t, 256 + g]) == k + 127
+        assert nibble(rows, t, 32 * g) == 7  # 6 * 2^k / 2^k = 6
+    for i, p in enumerate(cands):
+        gi = i // per
+        t, g = divmod(gi, 16)
+        elem = 32 * g + 1 + i % per
+        assert nibble(rows, t, elem) == expected_mxfp4_code(bf16_fraction(p), p, k), (hex(p), k)
+
+
+@pytest.mark.parametrize("j", [-124, -60, -3, 0, 1, 7, 64, 126])
+def test_powers_of_two(j):
+    """A power-of-two amax costs no exponent step: amax = 2^j encodes as
+    4.0 (code 6) with byte j-2+127; amax = 3*2^j as 6.0 (code 7) with byte
+    j-1+127 (a log2-based ceiling would give byte +1 and code 5)."""
+    src = np.zeros((1, 512), dtype=np.uint16)
+    src[0, 0] = bf16_bits_of_fraction(TWO ** j)
+    src[0, 32] = bf16_bits_of_fraction(-TWO ** j)
+    src[0, 64] = bf16_bits_of_fraction(3 * TWO ** j)
+    rows = flat_store(src)
+    assert rows[0, 256] == j - 2 + 127 and nibble(rows, 0, 0) == 6
+    assert rows[0, 257] == j - 2 + 127 and nibble(rows, 0, 32) == 6 | 8
+    assert rows[0, 258] == j - 1 + 127 and nibble(rows, 0, 64) == 7
+
+
+@pytest.mark.parametrize("k", [-120, -5, 0, 3, 100])
+def test_ties_to_even(k):
+    """Exact midpoints m*2^k (anchor 6*2^k) go to the even index of their
+    two neighbours: indices 0, 2, 2, 4, 4, 6, 6 for the seven midpoints."""
+    src = np.zeros((1, 512), dtype=np.uint16)
+    src[0, 0] = bf16_bits_of_fraction(6 * TWO ** k)
+    for i, m in enumerate(MIDS):
+        src[0, 1 + i] = bf16_bits_of_fraction(Fraction(m) * TWO ** k)
+        src[0, 9 + i] = bf16_bits_of_fraction(-Fraction(m) * TWO ** k)
+    rows = flat_store(src)
+    expect = [0, 2, 2, 4, 4, 6, 6]
+    for i in range(7):
+        assert nibble(rows, 0, 1 + i) == expect[i]
+        assert nibble(rows, 0, 9 + i) == expect[i] | 8
+
+
+def test_negative_zero_small_negatives_and_nibble_order():
+    """bf16 -0.0 gives code 0; a small negative gives code 8 [P1
+    `_quantize_e2m1`]; element 2i sits in the low nibble of byte i [P3
+    Details]."""
+    src = np.zeros((1, 512), dtype=np.uint16)
+    src[0, 0] = bf16_bits_of_fraction(Fraction(6))     # code 7, e = 0
+    src[0, 1] = bf16_bits_of_fraction(Fraction(1, 2))  # code 1
+    src[0, 2] = 0x8000                                 # -0.0 -> 0
+    src[0, 3] = 0xBC24                                 # about -0.01 -> 8
+    rows = flat_store(src)
+    assert rows[0, 0] == 0x17
+    assert rows[0, 1] == 0x80
+    assert rows[0, 256] == 127
+
+
+def test_all_zero_groups_and_nonfinite():
+    src = np.zeros((1, 512), dtype=np.uint16)
+    src[0, 32:64] = 0x8000           # all -0.0
+    src[0, 64] = 0x7F80              # +Inf with finite neighbours
+    src[0, 65] = 0x4000
+    src[0, 96] = 0x7FC1              # NaN
+    rows = flat_store(src)
+    assert rows[0, 256] == 127 and rows[0, 257] == 127
+    assert (rows[0, 16:32] == 0).all()
+    assert rows[0, 258] == 0xFF and (rows[0, 32:48] == 0).all()
+    assert rows[0, 259] == 0xFF and (rows[0, 48:64] == 0).all()
+
+
+def test_invariants_on_random_rows():
+    """On varied random rows: decoded magnitude never exceeds 6, the scale is
+    minimal (the amax element decodes to >= 3 times the scale unless the
+    -126 floor applies), scale bytes lie in [1, 253], and the error is at most
+    half the local E2M1 gap times the scale."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_t(2, size=(64, 512)) * np.exp2(rng.uniform(-130, 120, size=(64, 1)))
+    with np.errstate(over="ignore", under="ignore"):
+        xf = x.astype(np.float32)
+    bits = ((xf.view(np.uint32).astype(np.uint64) + 0x7FFF + ((xf.view(np.uint32) >> 16) & 1)) >> 16)
+    src = bits.astype(np.uint16)
+    src[(src & 0x7F80) == 0x7F80] = 0x3F80  # keep the rows finite
+    rows = flat_store(src)
+    for t in range(64):
+        for g in range(16):
+            byte = int(rows[t, 256 + g])
+            vals = [bf16_fraction(int(src[t, 32 * g + j])) for j in range(32)]
+            amax = max(abs(v) for v in vals)
+            if amax == 0:
+                assert byte == 127
+                continue
+            assert 1 <= byte <= 253
+            e = byte - 127
+            for j, v in enumerate(vals):
+                c = nibble(rows, t, 32 * g + j)
+                dq = GRID[c & 7] * (-1 if c & 8 else 1)
+                q = v / TWO ** e
+                assert abs(dq) <= 6
+                gap = Fraction(1, 2) if abs(q) <= 2 else (Fraction(1) if abs(q) <= 4 else Fraction(2))
+                assert abs(q - dq) <= gap / 2
+            top = max(range(32), key=lambda j: abs(vals[j]))
+            if amax / 6 >= TWO ** -126:
+                assert nibble(rows, t, 32 * g + top) & 7 >= 5
+
+
+# ---------------------------------------------------------------- layout
+
+def test_paged_addressing_pads_and_canaries():
+    """Row of slot s at ((s // B) * stride_rows + s % B) * 272 [P1
+    `store_mxfp4_mla`]; pads (-1) and slots past the last one write nothing;
+    every byte outside written rows keeps its canary."""
+    rng = np.random.default_rng(3)
+    nb, bs, stride = 5, 8, 24
+    src = (rng.integers(0, 0x7F00, size=(12, 512)) | (rng.integers(0, 2, size=(12, 512)) << 15)).astype(np.uint16)
+    slots = np.array([0, 7, 8, 15, 39, -1, 17, 40, 1000, 33, -5, 3], dtype=np.int64)
+    cache = np.full(((nb - 1) * stride + bs) * 272, 0xA5, dtype=np.uint8)
+    oracle.mxfp4_store(src, slots, cache, nb, bs, stride)
+    touched = np.zeros(cache.size, dtype=bool)
+    for t, s in enumerate(slots):
+        if s < 0 or s >= nb * bs:
+            continue
+        off = ((s // bs) * stride + s % bs) * 272
+        assert (cache[off:off + 272] == oracle.quantize_row(src[t])).all()
+        touched[off:off + 272] = True
+    assert (cache[~touched] == 0xA5).all()
+
+
+def test_strided_source_rows():
+    """The latent may be a row-strided view (e.g. the first 512 columns of a
+    [T, 576] tensor); only rows are strided."""
+    rng = np.random.default_rng(4)
+    wide = rng.integers(0, 0x7F00, size=(6, 576)).astype(np.uint16)
+    view = wide[:, :512]
+    cache = np.zeros(6 * 272, dtype=np.uint8)
+    oracle.mxfp4_store(view, np.arange(6, dtype=np.int64), cache, 1, 6, 6)
+    for t in range(6):
+        assert (cache[t * 272:(t + 1) * 272] == oracle.quantize_row(np.ascontiguousarray(view[t]))).all()
+
+
+# ---------------------------------------------------------------- dequant
+
+def test_dequant_table_exhaustive():
+    """All 16 codes x 256 scale bytes against the exact product
+    E2M1(code) * 2^(byte - 127) (+-Inf from 2^128, NaN for byte 0xFF)."""
+    for b in range(256):
+        for c in range(16):
+            got = oracle.dequant_bf16(c, b)
+            if b == 0xFF:
+                assert got == 0x7FC0
+                continue
+            v = GRID[c & 7] * (-1 if c & 8 else 1) * TWO ** (b - 127)
+            if c == 8:
+                assert got == 0x8000  # -0.0
+            else:
+                assert got == bf16_bits_of_fraction(v), (c, b)
+
+
+def test_round_trip_within_half_gap():
+    rng = np.random.default_rng(5)
+    src = (rng.standard_normal((16, 512)) * np.exp2(rng.uniform(-30, 30, (16, 1)))).astype(np.float32)
+    bits = (src.view(np.uint32) >> 16).astype(np.uint16)  # truncation is fine for test data
+    rows = flat_store(bits)
+    cache = rows.reshape(-1).copy()
+    out = oracle.mxfp4_gather_dequant(cache, 1, 16, 16, 512, np.arange(16, dtype=np.int64))
+    for t in range(16):
+        for g in range(16):
+            e = int(rows[t, 256 + g]) - 127
+            for j in range(32):
+                x = bf16_fraction(int(bits[t, 32 * g + j]))
+                d = bf16_fraction(int(out[t, 32 * g + j]))
+                q = abs(x) / TWO ** e
+                gap = Fraction(1, 2) if q <= 2 else (Fraction(1) if q <= 4 else Fraction(2))
+                assert abs(x - d) <= gap / 2 * TWO ** e
+
+
+def test_dequant_skips_bad_slots():
+    cache = np.zeros(4 * 272, dtype=np.uint8)
+    out = np.full((3, 512), 0x1234, dtype=np.uint16)
+    oracle.mxfp4_gather_dequant(cache, 1, 4, 4, 512, np.array([-1, 4, 2], dtype=np.int64), out)
+    assert (out[0] == 0x1234).all() and (out[1] == 0x1234).all() and (out[2] == 0).all()
+
+
+# ---------------------------------------------------------------- e4m3
+
+def _torch_e4m3(v: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_matches_torch():
+    """fp32 -> E4M3FN with round-to-nearest-even, subnormals and the sign of
+    zero, against torch's float8_e4m3fn over every bf16 value in [-448, 448],
+    every grid midpoint +-1 ulp, and random fp32 values."""
+    vals = []
+    h = np.arange(65536, dtype=np.uint32)
+    f = (h << 16).view(np.float32)
+    vals.append(f[np.isfinite(f) & (np.abs(f) <= 448)])
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    vals += [mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000))]
+    rng = np.random.default_rng(6)
+    vals.append((rng.uniform(-1, 1, 200000) * np.exp2(rng.uniform(-14, 9, 200000))).astype(np.float32))
+    v = np.concatenate(vals).astype(np.float32)
+    v = np.concatenate([v, -v])
+    v = v[np.abs(v) <= 448]
+    assert (oracle.e4m3_encode_array(v) == _torch_e4m3(v)).all()
+    assert oracle.e4m3_encode(-0.0) == 0x80 and oracle.e4m3_encode(0.0) == 0x00
+
+
+# ---------------------------------------------------------------- RoPE variants
+
+def _identity_table(rows=8):
+    t = np.zeros((rows, 64), dtype=np.float32)
+    t[:, :32] = 1.0
+    return t
+
+
+def _run_rope(fn, latent, positions, table, slots, block=4, nb=None, cr=4, width=528):
+    nb = nb or max(1, -(-int(max(slots.max(), 0) + 1) // block))
+    cache = np.full(nb * block * width, 0xA5, dtype=np.uint8)
+    fn(latent, positions, table, cache, block, nb, slots, cr)
+    return cache, nb
+
+
+def test_mxfp8_exponent_exhaustive_and_values():
+    """Every positive finite bf16 value as a group's only nonzero element,
+    through an identity rotation: scale byte = min(max(E + 127, 0), 254) with
+    E the exact ceiling of log2 of fp32(max(amax, fl(1e-4)) * fl(1/448))
+    (the fp32 product taken with numpy), value byte = torch's E4M3 of
+    fp32(amax * 2^-E)."""
+    pats = np.arange(1, 0x7F80, dtype=np.uint16)
+    n = -(-pats.size // 16)
+    latent = np.zeros((n, 512), dtype=np.uint16)
+    flat = latent.reshape(-1, 32)
+    flat[: pats.size, 0] = pats
+    positions = np.full(n, 3, dtype=np.int64)
+    slots = np.arange(n, dtype=np.int64)
+    block = 16
+    nb = -(-n // block)
+    cache = np.full(nb * block * 528, 0xA5, dtype=np.uint8)
+    oracle.mxfp8_rope_store(latent, positions, _identity_table(), cache, block, nb, slots, 4)
+    pages = cache.reshape(nb, block * 528)
+    inv448 = np.float32(1.0 / 448.0)
+    floor = np.float32(1e-4)
+    amax = np.maximum((pats.astype(np.uint32) << 16).view(np.float32), floor)
+    v = (amax * inv448).astype(np.float32)
+    E = np.array([ceil_log2(Fraction(float(x))) for x in v])
+    y = np.array([np.float32(float(bf16_fraction(int(p)) / TWO ** int(k))) for p, k in zip(pats, E)])
+    want_val = _torch_e4m3(y)
+    for i, p in enumerate(pats):
+        t, g = divmod(i, 16)
+        page, r = divmod(t, block)
+        sbyte = pages[page, block * 512 + r * 16 + g]
+        assert sbyte == min(max(int(E[i]) + 127, 0), 254), hex(p)
+        assert pages[page, r * 512 + 32 * g] == want_val[i], hex(p)
+
+
+def test_mxfp8_zero_group_byte_105():
+    latent = np.zeros((1, 512), dtype=np.uint16)
+    cache, _ = _run_rope(oracle.mxfp8_rope_store, latent, np.array([3], dtype=np.int64),
+                         _identity_table(), np.array([0], dtype=np.int64))
+    assert (cache[4 * 512: 4 * 512 + 16] == 105).all()
+    assert (cache[:512] == 0).all()
+
+
+def test_rope_exact_angles_pin_pairing_and_row():
+    """Rotations by exactly 90 and 180 degrees are permutations/negations of
+    the RoPE pairs: (e, o) -> (-o, e) and (-e, -o) on dims 448..511 only.
+    The table row is (position // CR) * CR: rows after it hold NaN and must not
+    be read."""
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal((1, 512)).astype(np.float32)
+    a[a == 0] = 1.0
+    ab = (a.view(np.uint32) >> 16).astype(np.uint16)
+    af = (ab.astype(np.uint32) << 16).view(np.float32)
+    table = np.full((96, 64), np.nan, dtype=np.float32)
+    table[40, :32], table[40, 32:] = 0.0, 1.0    # 90 degrees at row 40
+    table[60, :32], table[60, 32:] = -1.0, 0.0   # 180 degrees at row 60
+    table[80, :32], table[80, 32:] = 1.0, 0.0    # identity at row 80
+    b90 = af.copy()
+    b90[0, 448::2], b90[0, 449::2] = -af[0, 449::2], af[0, 448::2]
+    b180 = af.copy()
+    b180[0, 448:] = -af[0, 448:]
+    to_bits = lambda x: (x.view(np.uint32) >> 16).astype(np.uint16)
+    latent = np.concatenate([ab, to_bits(b90), ab, to_bits(b180)])
+    positions = np.array([43, 83, 63, 83], dtype=np.int64)  # bases 40, 80, 60, 80
+    slots = np.arange(4, dtype=np.int64)
+    for fn, width in ((oracle.mxfp8_rope_store, 528), (oracle.nvfp4_rope_store, 288)):
+        cache = np.full(4 * width, 0xA5, dtype=np.uint8)
+        fn(latent, positions, table, cache, 4, 1, slots, 4)
+        vb = 512 if width == 528 else 256
+        sb = 16 if width == 528 else 32
+        vals = cache[: 4 * vb].reshape(4, vb)
+        scales = cache[4 * vb:].reshape(4, sb)
+        assert (vals[0] == vals[1]).all() and (scales[0] == scales[1]).all()
+        assert (vals[2] == vals[3]).all() and (scales[2] == scales[3]).all()
+
+
+def test_rope_gate_and_canaries():
+    """Only tokens with a valid slot and (position + 1) % CR == 0 are written;
+    everything else keeps its canary."""
+    rng = np.random.default_rng(9)
+    latent = (rng.standard_normal((8, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    positions = np.array([3, 4, 7, 8, 11, 15, 1, 2], dtype=np.int64)
+    slots = np.array([0, 1, 2, 3, -1, 5, 6, 7], dtype=np.int64)
+    table = _identity_table(16)
+    for fn, width in ((oracle.mxfp8_rope_store, 528), (oracle.nvfp4_rope_store, 288)):
+        cache = np.full(2 * 4 * width, 0xA5, dtype=np.uint8)
+        fn(latent, positions, table, cache, 4, 2, slots, 4)
+        vb = 512 if width == 528 else 256
+        sb = width - vb
+        written = {0, 2, 5}  # positions 3, 7, 15 with valid slots
+        for s in range(8):
+            page, r = divmod(s, 4)
+            base = page * 4 * width
+            v = cache[base + r * vb: base + (r + 1) * vb]
+            sc = cache[base + 4 * vb + r * sb: base + 4 * vb + (r + 1) * sb]
+            if s in written:
+                assert not (v == 0xA5).all()
+            else:
+                assert (v == 0xA5).all() and (sc == 0xA5).all(), s
+
+
+def test_nvfp4_scales_and_codes():
+    """NVFP4 tile scale = torch E4M3 of clamp(fp32(amax * fl(1/6)), 2^-9, 448);
+    codes = the pages' midpoint count on the numpy fp32 quotient r / scale,
+    saturating at index 7, sign bit below zero."""
+    rng = np.random.default_rng(10)
+    n = 64
+    x = (rng.standard_normal((n, 512)) * np.exp2(rng.uniform(-16, 12, (n, 32)).repeat(16, 1)))
+    x = x.astype(np.float32)
+    x[0, :16] = 0.0
+    x[1, :16] = -0.0
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xf = (bits.astype(np.uint32) << 16).view(np.float32)
+    positions = np.full(n, 3, dtype=np.int64)
+    slots = np.arange(n, dtype=np.int64)
+    cache = np.full(n * 288, 0xA5, dtype=np.uint8)
+    oracle.nvfp4_rope_store(bits, positions, _identity_table(), cache, n, 1, slots, 4)
+    vals = cache[: n * 256].reshape(n, 256)
+    scales = cache[n * 256:].reshape(n, 32)
+    tiles = xf.reshape(n, 32, 16)
+    amax = np.abs(tiles).max(axis=2)
+    sf = np.clip((amax * np.float32(1.0 / 6.0)).astype(np.float32), np.float32(2.0 ** -9), np.float32(448))
+    s8 = _torch_e4m3(sf)
+    assert (scales == s8).all()
+    S = torch.from_numpy(s8).view(torch.float8_e4m3fn).float().numpy()
+    for t in range(n):
+        for k in range(32):
+            for j in range(16):
+                y = np.float32(tiles[t, k, j]) / np.float32(S[t, k])
+                yq = Fraction(float(y))
+                code = midpoint_index(abs(yq), MIDS, STRICT) | (8 if y < 0 else 0)
+                d = 16 * k + j
+                got = (vals[t, d // 2] >> (4 * (d % 2))) & 0xF
+                assert got == code, (t, k, j, float(y))
