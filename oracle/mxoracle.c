@@ -93,13 +93,16 @@ int orc_ceil_pow2_exponent(float v) {
  * Round a non-negative magnitude to the nearest point of the E2M1 magnitude
  * grid {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even grid index [P1
  * `_quantize_e2m1`: the midpoint count with alternating strict and non-strict
- * comparisons is exactly this rule].  Magnitudes above 6 go to index 7
- * (nearest point); +inf too.  Done by brute-force distance in double, which
- * is exact for every fp32 input.
+ * comparisons is exactly this rule].  At or above 6 the nearest point is 6,
+ * index 7 (the midpoint count also stops at 7), +inf included; this is
+ * decided before the distance search because a - 0.5 in double is no longer
+ * exact once a is about 2^53 or larger, and every distance would then tie.
+ * Below 6 the search by distance in double orders the candidates exactly for
+ * every fp32 input.
  */
 static int e2m1_nearest_index(double a) {
   static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-  if (isinf(a)) return 7;
+  if (a >= 6.0) return 7;
   int best = 0;
   double best_d = fabs(a - grid[0]);
   for (int i = 1; i < 8; ++i) {
@@ -155,6 +158,7 @@ uint8_t orc_e4m3_encode(float v) {
   if (isnan(v)) return 0x7F;
   uint8_t sign = signbit(v) ? 0x80 : 0x00;
   double a = fabs((double)v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
   int best = 0;
   double best_d = a; /* distance to code 0 (value 0) */
   for (int c = 1; c <= 0x7E; ++c) {

@@ -514,3 +514,31 @@ def test_nvfp4_scales_and_codes():
                 d = 16 * k + j
                 got = (vals[t, d // 2] >> (4 * (d % 2))) & 0xF
                 assert got == code, (t, k, j, float(y))
+
+
+def test_e2m1_saturates_for_huge_quotients():
+    """The pages' midpoint count gives index 7 to every magnitude above 5, so
+    huge quotients (an NVFP4 tile whose scale clamped at 448) saturate to
+    +-6, whatever their size; NaN codes 0 (reading R16)."""
+    for v in [5.0000005, 6.0, 6.5, 7.0, 1e6, 2.0 ** 60, 3.4e38, float("inf")]:
+        for s in (1.0, -1.0):
+            q = np.float32(s * v)
+            want = midpoint_index(abs(Fraction(float(q))) if np.isfinite(q) else Fraction(10 ** 40),
+                                  MIDS, STRICT) | (8 if q < 0 else 0)
+            assert oracle.e2m1_code(float(q)) == want == (7 | (8 if s < 0 else 0)), v
+    assert oracle.e2m1_code(float("nan")) == 0
+
+
+def test_nvfp4_huge_tiles_saturate():
+    """Tiles with amax far above 6 * 448: scale byte 0x7E (448) and every
+    element above 5 * 448 in magnitude codes +-6."""
+    latent = np.zeros((1, 512), dtype=np.uint16)
+    latent[0, :16] = 0x7F00      # 2^127
+    latent[0, 1] = 0xFF00        # -2^127
+    latent[0, 2] = 0x4500        # 2048 -> 2048 / 448 = 4.57 -> code 6
+    cache = np.full(288, 0xA5, dtype=np.uint8)
+    oracle.nvfp4_rope_store(latent, np.array([3], dtype=np.int64), _identity_table(), cache, 1, 1,
+                            np.array([0], dtype=np.int64), 4)
+    assert cache[256] == 0x7E
+    assert cache[0] == 0x7 | (0xF << 4)
+    assert cache[1] == 0x6 | (0x7 << 4)
