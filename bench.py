@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 paged-cache store on one MI355X.
+
+A step is one mxfp4_store launch over the whole batch: 4,500,000 tokens x
+512 bf16 (uniform in [-4, 4]) scattered to a random permutation of the slots
+of a flat 1.224 GB cache; inputs are resident in HBM before timing.  The
+gather-dequant and the two RoPE+quant inserts are timed after it, each on
+its own workload, and reported under "companions".
+
+Output: one JSON line (see the fields below).  `--sweep` prints further
+lines for the token-count / slot-pattern sweep with the Infinity Cache
+flushed between repetitions.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BYTES_PER_TOKEN = 1024 + 272 + 8  # latent read + row written + slot read
+BYTES_PER_PAD = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mxfp4_store_large_traffic.txt")
+STORE_SRC = os.path.join(ROOT, "mxfp4_paged_cache_store_amd", "csrc", "mxfp4_store.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--tokens", type=int, default=4_500_000)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-companions", action="store_true")
+    p.add_argument("--sweep", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=1_000_000)
+    return p.parse_args()
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(tokens: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source and this token count."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_digest(STORE_SRC):
+        return None
+    if int(kv.get("tokens", -1)) != tokens:
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def time_launches(fn, steps: int, warmup: int, torch):
+    """Wall time and HIP-event time of `steps` back-to-back launches on the
+    current stream (the one every launch here uses)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1000.0
+
+
+def cpu_baseline(sample: int):
+    import numpy as np
+
+    import oracle
+    from mxfp4_paged_cache_store_amd import workloads
+
+    threads = max(1, min(8, os.cpu_count() or 1))
+    src, slots = workloads.large_sample_host(sample)
+    cache = np.full(sample * 272, 0xA5, dtype=np.uint8)
+    t0 = time.perf_counter()
+    oracle.mxfp4_store(src, slots, cache, 1, sample, sample, threads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(sample / dt, 1),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{sample} tokens x 512 bf16 uniform in [-4, 4], random-permutation slots "
+                  f"into a flat cache (same distribution as the timed batch), "
+                  f"{threads} threads over contiguous token ranges, {dt:.2f} s",
+    }
+
+
+def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
+    out = {}
+    # gather-dequant of every slot of the large cache back to bf16
+    slots = torch.arange(n_tokens, dtype=torch.int64, device="cuda")
+    dq = torch.empty((n_tokens, 512), dtype=torch.bfloat16, device="cuda")
+    _, ev = time_launches(lambda: ops.mxfp4_gather_dequant(cache, 1, n_tokens, n_tokens, 512, slots, dq),
+                          max(3, steps // 3), warmup, torch)
+    per = ev / max(3, steps // 3)
+    out["mxfp4_gather_dequant"] = {
+        "workload": f"{n_tokens} slots of the flat cache -> bf16 [{n_tokens}, 512]",
+        "us_per_launch": round(per * 1e6, 2),
+        "slots_per_s": round(n_tokens / per, 1),
+        "GBps": round(n_tokens * 1304 / per / 1e9, 1),
+        "frac_hbm_peak": round(n_tokens * 1304 / per / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    del dq, slots
+    # RoPE inserts on the 16384-token, compress-ratio-4 workload
+    case = workloads.rope_case()
+    lat = torch.from_numpy(case.latent.view("int16")).cuda().view(torch.bfloat16)
+    pos = torch.from_numpy(case.positions).cuda()
+    cs = torch.from_numpy(case.cos_sin).cuda()
+    sl = torch.from_numpy(case.slots).cuda()
+    written = int(((case.positions + 1) % case.compress_ratio == 0).sum())
+    for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
+                            ("nvfp4_rope_store", ops.nvfp4_rope_store, 288)):
+        kv = torch.zeros((case.num_blocks, case.block, width), dtype=torch.uint8, device="cuda")
+        _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, case.compress_ratio), steps, warmup, torch)
+        per = ev / steps
+        nbytes = written * (1024 + 256 + 16 + width) + (case.latent.shape[0] - written) * 16
+        out[name] = {
+            "workload": f"{case.latent.shape[0]} tokens, CR {case.compress_ratio} ({written} written), "
+                        f"{width}-byte records",
+            "us_per_launch": round(per * 1e6, 2),
+            "GBps": round(nbytes / per / 1e9, 1),
+        }
+    return out
+
+
+def run_sweep(torch, ops):
+    """Store throughput vs token count and slot pattern, Infinity Cache
+    flushed (a 1 GiB write) before each repetition; median of 20."""
+    import statistics
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for n in (16384, 65536, 262144, 1048576, 4500000):
+        for pattern in ("runs", "random"):
+            src = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda").uniform_(-4, 4)
+            if pattern == "random":
+                slots = torch.randperm(n, device="cuda")
+            else:
+                slots = torch.arange(n, device="cuda", dtype=torch.int64)
+            cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
+            times = []
+            for _ in range(22):
+                flush.fill_(1)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ops.mxfp4_store(src, slots, cache, 1, n, n)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / 1000.0)
+            t = statistics.median(times[2:])
+            gbs = n * BYTES_PER_TOKEN / t / 1e9
+            print(json.dumps({"sweep": "mxfp4_store", "tokens": n, "slots": pattern,
+                              "us": round(t * 1e6, 2), "GBps": round(gbs, 1),
+                              "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                              "cache": "flushed"}), flush=True)
+            del src, slots, cache
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the store has "
+              "no cross-GPU step, so run it with --gpus 1 on each GPU's share", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mxfp4_paged_cache_store_amd import build, ops, workloads
+
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+
+    n = args.tokens
+    print(f"[bench] generating {n} tokens on the device", file=sys.stderr, flush=True)
+    src, slots = workloads.large_case_device(n)
+    cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
+    valid = n  # a permutation: no pad slots
+
+    def step():
+        ops.mxfp4_store(src, slots, cache, 1, n, n)
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    wall, ev = time_launches(step, args.steps, args.warmup, torch)
+    per_launch = ev / args.steps
+    algo_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
+    achieved = algo_bytes / per_launch / 1e9
+    traffic = measured_traffic(n)
+
+    result = {
+        "metric": "MXFP4 store tokens/s and effective HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": round(valid * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"mxfp4_store: {n} tokens x 512 bf16 uniform in [-4, 4], random-permutation "
+                        f"slots, flat cache of {n} x 272-byte rows, group 32",
+            "tokens": n,
+            "latent": 512,
+            "row_bytes": 272,
+            "parallelism": "single GPU",
+        },
+        "effective_GBps": round(valid * BYTES_PER_TOKEN * args.steps / wall / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes,
+            "kernel_us_per_launch": round(per_launch * 1e6, 2),
+        },
+    }
+    if not args.no_companions:
+        print("[bench] companions", file=sys.stderr, flush=True)
+        result["companions"] = companions(torch, ops, workloads, args.steps, args.warmup, cache, n)
+    del src, slots
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_sample)
+    print(json.dumps(result), flush=True)
+    if args.sweep:
+        del cache
+        torch.cuda.empty_cache()
+        run_sweep(torch, ops)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * mxstore.h -- C ABI of libmxstore.so: MXFP4 quantize-and-scatter store of
+ * an MLA latent into a paged KV cache, its gather-dequant companion, and the
+ * MXFP8 / NVFP4 RoPE+quant record inserts, as hand-written HIP kernels for
+ * gfx950 (MI355X).
+ *
+ * Sources (web pages; sections named):
+ *   [P1] docs page "vllm.v1.attention.ops.mxfp4_mla.store"
+ *   [P2] docs page "vllm.models.deepseek_v41.common.ops.fused_compress_quant_cache"
+ *   [P3] pull request "[ROCm][Attention] Add an mxfp4_mla KV cache for
+ *        rope-free sparse MLA (read/write path)"
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL is the default stream) and runs
+ *     asynchronously: the caller keeps every buffer alive until the stream
+ *     has passed the call.
+ *   - bf16 data is passed as its raw 16-bit patterns (uint16_t).
+ *   - Return value: MX_OK, or a negative MX_E_* code when an argument breaks
+ *     the contract stated below; nothing is launched then, and
+ *     mx_last_error() describes the first violated rule.  Data errors on the
+ *     device are never reported: a slot that is negative (PAD_SLOT_ID) or
+ *     past the last slot is skipped.
+ *   - num_tokens == 0 (or an empty slot list) launches nothing and returns
+ *     MX_OK [P1 `store_mxfp4_mla`; P2 `rope_quant_insert`].
+ *   - Two tokens mapping to the same slot race (which one lands is
+ *     unspecified).
+ */
+#ifndef MXSTORE_H
+#define MXSTORE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MX_OK 0
+#define MX_E_NULL (-1)   /* a required pointer is NULL                       */
+#define MX_E_SHAPE (-2)  /* latent / group / record width not supported      */
+#define MX_E_STRIDE (-3) /* a stride is inconsistent with the layout         */
+#define MX_E_ALIGN (-4)  /* a pointer or stride breaks the alignment rule    */
+#define MX_E_RANGE (-5)  /* a count is negative or too large                 */
+#define MX_E_ARG (-6)    /* another argument is invalid (compress ratio ...) */
+#define MX_E_LAUNCH (-7) /* the HIP launch itself failed                     */
+
+/*
+ * Bytes of one packed MXFP4 row: latent/2 code bytes + latent/group E8M0
+ * scale bytes [P1 module docstring `row_bytes`; P3 Overview: 272 for 512].
+ * Returns a negative MX_E_SHAPE when latent is not a positive multiple of
+ * group (group > 0).  Host-only, no device work.
+ */
+int64_t mx_row_bytes(int64_t latent, int32_t group);
+
+/*
+ * MXFP4 store [P1 `store_mxfp4_mla` and its helpers `_ceil_pow2_exponent`,
+ * `_quantize_e2m1`; P3 Details].  For each token t < num_tokens with slot
+ * s = slot_mapping[t] in [0, num_blocks * block_size):
+ *   per group of 32 latent values: amax in fp32; scale exponent e = smallest
+ *   integer with 2^e >= amax/6 (bit-pattern reading: floored at -126); an
+ *   all-zero group uses e = 0; a group holding NaN/Inf writes scale 0xFF and
+ *   zero codes; every value is divided by 2^e in fp32 and rounded to the
+ *   nearest E2M1 code (ties to even), sign bit set when the quotient is
+ *   below zero.
+ *   Row = [latent/2 code bytes (element 2i in the low nibble of byte i) |
+ *   latent/32 scale bytes (e + 127)], written at byte offset
+ *   ((s / block_size) * block_stride_rows + s % block_size) * row_bytes.
+ *
+ * src_bf16        [num_tokens, latent] bf16, row stride src_row_stride
+ *                 elements (>= latent), unit inner stride.  The base address
+ *                 must be 16-byte aligned and src_row_stride a multiple of 8.
+ * slot_mapping    int64 [num_tokens].
+ * cache           uint8, 4-byte aligned, holding at least
+ *                 ((num_blocks-1) * block_stride_rows + block_size) rows of
+ *                 row_bytes bytes.  A flat cache is num_blocks = 1,
+ *                 block_size = block_stride_rows = number of slots.
+ * latent          power of two in [128, 2048]; group must be 32 [P3 review:
+ *                 kv_lora_rank is a power of two >= 128; OCP block 32].
+ * block_stride_rows >= block_size; num_blocks * block_size < 2^32.
+ */
+int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                int64_t src_row_stride, const int64_t* slot_mapping,
+                uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                int64_t block_stride_rows, int32_t group, void* stream);
+
+/*
+ * MXFP4 gather-dequant [P3 Details, read path: unpack to bf16; Claims: the
+ * result equals the dequantized values stored as bf16].  For each i <
+ * num_slots_in_list with slot s = slots[i] in range, writes
+ * out[i, d] = bf16(E2M1(code_d) * 2^(scale_byte - 127)) for d < latent:
+ * exact, except that a product >= 2^128 gives +-Inf and scale byte 0xFF gives
+ * the quiet NaN 0x7FC0.  A slot out of range leaves row i of out untouched.
+ *
+ * cache           same layout and arguments as mxfp4_store (read only).
+ * slots           int64 [num_slots_in_list].
+ * out_bf16        [num_slots_in_list, latent] bf16, row stride
+ *                 out_row_stride elements (>= latent, multiple of 8),
+ *                 16-byte aligned base.
+ */
+int mxfp4_gather_dequant(const uint8_t* cache, int64_t num_blocks,
+                         int64_t block_size, int64_t block_stride_rows,
+                         int64_t latent, int32_t group, const int64_t* slots,
+                         int64_t num_slots_in_list, uint16_t* out_bf16,
+                         int64_t out_row_stride, void* stream);
+
+/*
+ * MXFP8 RoPE+quant insert, 528-byte record [P2
+ * `_rope_quant_insert_mxfp8_kernel`, `rope_quant_insert`].  Token t is
+ * written when s = slot_mapping[t] is in [0, num_blocks * cache_block) and
+ * (positions[t] + 1) % compress_ratio == 0.  Its 512 bf16 values are rotated
+ * GPT-J style on pairs (448+2i, 449+2i), i < 32, with cos/sin row
+ * r = (positions[t] / compress_ratio) * compress_ratio of cos_sin (cos in
+ * columns 0..31, sin in 32..63; a row outside [0, cos_rows) skips the
+ * token); with sanitize_nans, NaN becomes +0.  Per group of 32:
+ * amax = max(max|r|, 1e-4f); E = ceil(log2(fp32(amax * (1/448)))) taken
+ * exactly; values = E4M3(clamp(r * 2^-E, +-448)); scale = clamp(E + 127, 0,
+ * sanitize ? 254 : 255).  Page layout (page = s / cache_block, base
+ * cache + page * cache_block_stride):
+ *   [cache_block x 512 value bytes | cache_block x 16 scale bytes].
+ *
+ * latent_bf16     [>= num_tokens, 512] bf16, contiguous, 16-byte aligned.
+ * positions       int64 [num_tokens].
+ * cos_sin         fp32 [cos_rows, cos_stride >= 64] table.
+ * cache           uint8, 16-byte aligned; cache_block_stride (bytes) is a
+ *                 multiple of 16 and >= cache_block * 528.
+ * compress_ratio  >= 1 (the pages' wrapper allows 1 or 2; the kernel math
+ *                 holds for any ratio).
+ */
+int mxfp8_rope_store(const uint16_t* latent_bf16, const int64_t* positions,
+                     const float* cos_sin, int64_t cos_stride, int64_t cos_rows,
+                     uint8_t* cache, int64_t cache_block_stride,
+                     int64_t cache_block, int64_t num_blocks,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     int32_t compress_ratio, int32_t sanitize_nans,
+                     void* stream);
+
+/*
+ * NVFP4 RoPE+quant insert, 288-byte record [P2
+ * `_rope_quant_insert_nvfp4_kernel`, `rope_quant_insert`].  Same gate,
+ * rotation and sanitising as mxfp8_rope_store.  Per tile of 16:
+ * S8 = E4M3(clamp(fp32(amax * (1/6)), 2^-9, 448)); y = fp32(r / S8) with a
+ * correctly rounded division; code = nearest E2M1 (ties to even, |y| > 6
+ * saturates to 6, sign bit when y < 0); byte i = code(2i) | code(2i+1) << 4.
+ * Page layout: [cache_block x 256 value bytes | cache_block x 32 scale bytes].
+ * cache_block_stride (bytes) is a multiple of 16 and >= cache_block * 288.
+ */
+int nvfp4_rope_store(const uint16_t* latent_bf16, const int64_t* positions,
+                     const float* cos_sin, int64_t cos_stride, int64_t cos_rows,
+                     uint8_t* cache, int64_t cache_block_stride,
+                     int64_t cache_block, int64_t num_blocks,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     int32_t compress_ratio, int32_t sanitize_nans,
+                     void* stream);
+
+/* Message for the last nonzero status returned on this thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char* mx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXSTORE_H */

@@ -1,0 +1,38 @@
+"""MI355X-native MXFP4 paged KV-cache store.
+
+libmxstore.so (hand-written HIP for gfx950, C ABI in include/mxstore.h)
+quantizes a bf16 MLA latent to MXFP4 (E2M1 codes + one E8M0 scale per 32
+values, 272 bytes per 512-wide token) and scatters it into a paged cache; a
+gather-dequant companion unpacks slots back to bf16; two RoPE+quant inserts
+write the MXFP8 (528 B) and NVFP4 (288 B) compressed-cache records.
+"""
+
+from .ops import (
+    GROUP_SIZE,
+    MXFP8_RECORD_BYTES,
+    NVFP4_RECORD_BYTES,
+    mxfp4_gather_dequant,
+    mxfp4_store,
+    mxfp8_rope_store,
+    nvfp4_rope_store,
+    resolve_paged_view,
+    rope_quant_insert,
+    row_bytes,
+    store_mxfp4_mla,
+)
+from ._abi import MxError
+
+__all__ = [
+    "GROUP_SIZE",
+    "MXFP8_RECORD_BYTES",
+    "NVFP4_RECORD_BYTES",
+    "MxError",
+    "mxfp4_gather_dequant",
+    "mxfp4_store",
+    "mxfp8_rope_store",
+    "nvfp4_rope_store",
+    "resolve_paged_view",
+    "rope_quant_insert",
+    "row_bytes",
+    "store_mxfp4_mla",
+]

@@ -1,0 +1,53 @@
+// kernels.hpp -- argument blocks and launchers of the libmxstore kernels.
+// Host code (the C ABI) fills these after validating the caller's arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace mxs {
+
+struct StoreArgs {
+  const uint16_t* src;   // bf16 [num_tokens, latent], row stride src_stride
+  int64_t src_stride;    // elements, multiple of 8
+  const int64_t* slots;  // [num_tokens]
+  int64_t num_tokens;
+  uint8_t* cache;
+  SlotMap map;
+};
+
+struct DequantArgs {
+  const uint8_t* cache;
+  SlotMap map;
+  const int64_t* slots;  // [n]
+  int64_t n;
+  uint16_t* out;         // bf16 [n, latent], row stride out_stride
+  int64_t out_stride;    // elements, multiple of 8
+};
+
+struct RopeArgs {
+  const uint16_t* latent;  // bf16 [num_tokens, 512] contiguous
+  const int64_t* positions;
+  const float* cos_sin;
+  int64_t cos_stride;  // elements
+  int64_t cos_rows;
+  uint8_t* cache;
+  int64_t page_stride;  // bytes between pages of `block` tokens
+  uint32_t block;
+  int32_t block_shift;  // log2(block) or -1
+  uint32_t num_slots;   // num_blocks * block
+  const int64_t* slots;
+  int64_t num_tokens;
+  int32_t cr;
+  int32_t sanitize;
+};
+
+// Each returns the hipError_t of the launch.
+hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream);
+hipError_t launch_mxfp4_dequant(const DequantArgs& a, int latent, hipStream_t stream);
+hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream);
+
+}  // namespace mxs

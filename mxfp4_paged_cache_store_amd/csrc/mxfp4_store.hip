@@ -1,0 +1,205 @@
+// mxfp4_store.hip -- MXFP4 quantize-and-scatter of a bf16 MLA latent into a
+// paged KV cache, for gfx950.
+//
+// What is computed follows the store page ("vllm.v1.attention.ops.mxfp4_mla.
+// store": `_ceil_pow2_exponent`, `_quantize_e2m1`, `store_mxfp4_mla`) and the
+// pull request adding the mxfp4_mla cache (Overview, Details); how it is
+// computed is specific to CDNA4:
+//
+//   * One wavefront owns one 512-value slice of a token per pass: lane l
+//     loads 16 bytes (values 8l..8l+7) with a non-temporal dwordx4 load, so a
+//     pass reads one whole 1024-byte latent row, fully coalesced.  A wave
+//     issues the loads of TOKENS_PER_WAVE tokens before it computes any, to
+//     keep enough bytes in flight for HBM.
+//   * A 32-value group is exactly the 4 lanes of a DPP quad: the group amax
+//     is a packed-u16 max over the lane's |bf16| bit patterns followed by two
+//     quad_perm DPP maxes.  |bf16| bit patterns order like the magnitudes.
+//   * The scale exponent comes straight from the amax bit pattern with
+//     integer ops.  For a bf16 amax = 2^(E-127) * (1 + m/128), the smallest
+//     e with 2^e >= amax/6 is E - 129 when m <= 64 and E - 128 when m > 64
+//     (1 + m/128 > 1.5 exactly when m > 64, and amax/6 never rounds onto a
+//     power of two from above in fp32); it is floored at -126 as the fp32 bit
+//     pattern of a subnormal amax/6 reads.
+//   * Each value is multiplied by 2^-e in fp32 (the same single rounding as a
+//     division by 2^e, with gradual underflow), +0.0 is added so that a zero
+//     quotient carries no sign, and gfx950's v_cvt_scalef32_pk_fp4_f32 (scale
+//     1.0) rounds two quotients to E2M1 codes, nearest-even, sign kept:
+//     four conversions give the lane's 8 codes as one dword, which is code
+//     dword l of the row (low nibble = lower index).
+//   * The 16 scale bytes are gathered with row_shr DPP moves into four
+//     dwords held by lanes 12, 28, 44 and 60.  The row is written as whole
+//     dwords: 64 code dwords + 4 scale dwords, non-temporal.
+//   * Slots are read by the scalar unit, a whole wave's in one load.  A pad
+//     or out-of-range slot skips the token's load as well as its store: the
+//     load goes through a raw buffer descriptor whose range is the token's
+//     row, or empty for a skipped token (the hardware range check returns
+//     zeros without touching memory).  All addressing is 64-bit.
+#include "kernels.hpp"
+
+namespace mxs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTokensPerWave = 8;
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Largest |bf16| bit pattern over the lane's 8 values and its quad (32 values).
+__device__ __forceinline__ uint32_t group_amax_bits(const u32x4 w) {
+  const uint32_t m = 0x7FFF7FFFu;
+  uint32_t x = pk_max_u16(pk_max_u16(w.x & m, w.y & m), pk_max_u16(w.z & m, w.w & m));
+  x = pk_max_u16(x, __builtin_amdgcn_alignbit(x, x, 16)) & 0xFFFFu;
+  x = max(x, dpp<kQuadSwap1>(x));
+  x = max(x, dpp<kQuadSwap2>(x));
+  return x;
+}
+
+// 8 E2M1 codes of the lane's values divided by 2^e, where mul = 2^-e.
+__device__ __forceinline__ uint32_t encode8(const u32x4 w, float mul) {
+  float l0 = as_f32(w.x << 16) * mul, h0 = as_f32(w.x & 0xFFFF0000u) * mul;
+  float l1 = as_f32(w.y << 16) * mul, h1 = as_f32(w.y & 0xFFFF0000u) * mul;
+  float l2 = as_f32(w.z << 16) * mul, h2 = as_f32(w.z & 0xFFFF0000u) * mul;
+  float l3 = as_f32(w.w << 16) * mul, h3 = as_f32(w.w & 0xFFFF0000u) * mul;
+  // A quotient that is -0.0 (from -0.0 or from underflow) does not compare
+  // below zero and must encode as code 0; x + 0.0 maps -0.0 to +0.0 and
+  // leaves every other value unchanged.
+  l0 += 0.0f; h0 += 0.0f; l1 += 0.0f; h1 += 0.0f;
+  l2 += 0.0f; h2 += 0.0f; l3 += 0.0f; h3 += 0.0f;
+  uint32_t c = 0;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, l0, h0, 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, l1, h1, 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, l2, h2, 1.0f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, l3, h3, 1.0f, 3);
+  return c;
+}
+
+// Quantizes the 512-value slice held by the wave (16 bytes per lane) and
+// writes it into `row`: code dword `lane_in_tok` at code_base and, from the
+// lanes 12 mod 16, the 4 gathered scale bytes at scale_base.
+__device__ __forceinline__ void quantize_slice(const u32x4 w, int lane_in_tok,
+                                               uint8_t* code_base, uint8_t* scale_base,
+                                               bool store) {
+  const uint32_t amax = group_amax_bits(w);
+  const bool nonfinite = amax >= 0x7F80u;
+  int e = (int)(amax >> 7) - 129 + ((amax & 0x7Fu) > 64u ? 1 : 0);
+  e = max(e, -126);
+  if (amax == 0u || nonfinite) e = 0;
+  const uint32_t scale_byte = nonfinite ? 0xFFu : (uint32_t)(e + 127);
+  const float mul = as_f32((uint32_t)(127 - e) << 23);  // 2^-e, e in [-126, 126]
+
+  uint32_t codes = encode8(w, mul);
+  if (nonfinite) codes = 0u;
+
+  // Scale dword k = groups 4k..4k+3 = lanes 16k, 16k+4, 16k+8, 16k+12.
+  const uint32_t sdw = dpp<kRowShr12>(scale_byte) | (dpp<kRowShr8>(scale_byte) << 8) |
+                       (dpp<kRowShr4>(scale_byte) << 16) | (scale_byte << 24);
+  if (store) {
+    __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(code_base) + lane_in_tok);
+    if ((lane_in_tok & 15) == 12)
+      __builtin_nontemporal_store(sdw, reinterpret_cast<uint32_t*>(scale_base) + (lane_in_tok >> 4));
+  }
+}
+
+// LATENT: values per token (power of two, 128..2048).  A token occupies
+// min(LATENT/8, 64) lanes per pass; LATENT > 512 takes LATENT/512 passes.
+// kPow2: slot -> row by shift/mask (else a 32-bit division).
+template <int LATENT, bool kPow2>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(const StoreArgs a) {
+  constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
+  constexpr int kToksPerPass = kWave / kLanesPerTok;
+  constexpr int kSub = LATENT >= 512 ? LATENT / 512 : 1;
+  constexpr int64_t kPitch = LATENT / 2 + LATENT / 32;
+  constexpr int kToks = kTokensPerWave * kToksPerPass;  // tokens per wave
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok_in_pass = lane / kLanesPerTok;
+  const int lane_in_tok = lane % kLanesPerTok;
+  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kToks;
+
+  // Slots of the wave's tokens: one merged load when the wave is whole.
+  int64_t slot[kTokensPerWave];
+  if (wave_first + kToks <= a.num_tokens) {
+#pragma unroll
+    for (int p = 0; p < kTokensPerWave; ++p)
+      slot[p] = a.slots[wave_first + p * kToksPerPass + tok_in_pass];
+  } else {
+#pragma unroll
+    for (int p = 0; p < kTokensPerWave; ++p) {
+      const int64_t t = wave_first + p * kToksPerPass + tok_in_pass;
+      slot[p] = t < a.num_tokens ? a.slots[t] : -1;
+    }
+  }
+
+  u32x4 v[kTokensPerWave][kSub];
+  int64_t row_off[kTokensPerWave];
+#pragma unroll
+  for (int p = 0; p < kTokensPerWave; ++p) {
+    const int64_t t = wave_first + p * kToksPerPass + tok_in_pass;
+    const bool ok = slot[p] >= 0 && slot[p] < (int64_t)a.map.num_slots;
+    row_off[p] = ok ? a.map.row<kPow2>((uint32_t)slot[p]) * kPitch : -1;
+    if constexpr (kToksPerPass == 1) {
+      // Whole wave on one token: a raw buffer over its row, empty for a
+      // skipped token, so the load needs no branch.
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_at(a.src + (ok ? t * a.src_stride : 0), ok ? LATENT * 2 : 0);
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub)
+        v[p][sub] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (sub * 64 + lane_in_tok) * 16, 0, kBufNT));
+    } else {
+      if (ok) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.src + t * a.src_stride + lane_in_tok * 8);
+        v[p][0] = __builtin_nontemporal_load(src);
+      } else {
+        v[p][0] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+#pragma unroll
+  for (int p = 0; p < kTokensPerWave; ++p) {
+    const bool ok = row_off[p] >= 0;
+    uint8_t* row = a.cache + (ok ? row_off[p] : 0);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub)
+      quantize_slice(v[p][sub], lane_in_tok, row + sub * 256, row + LATENT / 2 + sub * 16, ok);
+  }
+}
+
+template <int LATENT>
+hipError_t launch_latent(const StoreArgs& a, hipStream_t stream) {
+  constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
+  constexpr int64_t kToksPerBlock =
+      (int64_t)kWavesPerBlock * kTokensPerWave * (kWave / kLanesPerTok);
+  const int64_t blocks = (a.num_tokens + kToksPerBlock - 1) / kToksPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (a.map.pow2)
+    hipLaunchKernelGGL((mxfp4_store_kernel<LATENT, true>), dim3((unsigned)blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mxfp4_store_kernel<LATENT, false>), dim3((unsigned)blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream) {
+  switch (latent) {
+    case 128: return launch_latent<128>(a, stream);
+    case 256: return launch_latent<256>(a, stream);
+    case 512: return launch_latent<512>(a, stream);
+    case 1024: return launch_latent<1024>(a, stream);
+    case 2048: return launch_latent<2048>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mxs

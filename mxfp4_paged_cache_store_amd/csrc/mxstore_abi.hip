@@ -1,0 +1,202 @@
+// mxstore_abi.hip -- the extern "C" boundary of libmxstore.so: argument
+// validation (mirroring the checks of the pages' Python wrappers, plus the
+// alignment and range rules the gfx950 kernels rely on) and the launch on the
+// caller's stream.  No allocation, no synchronisation.  Declarations and the
+// full contract are in include/mxstore.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/mxstore.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MX_OK;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int log2_exact(int64_t v) {
+  int k = 0;
+  while ((int64_t(1) << k) < v) ++k;
+  return k;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared checks of the paged MXFP4 layer view [store page, `store_mxfp4_mla`:
+// whole rows per block; block stride may exceed the block].
+int check_paged(int64_t latent, int32_t group, int64_t num_blocks, int64_t block_size,
+                int64_t block_stride_rows, mxs::SlotMap* map) {
+  if (group != 32) return fail(MX_E_SHAPE, "group must be 32 (one E8M0 scale per 32 values), got %d", group);
+  if (!is_pow2(latent) || latent < 128 || latent > 2048)
+    return fail(MX_E_SHAPE, "latent must be a power of two in [128, 2048], got %lld", (long long)latent);
+  if (num_blocks < 1 || block_size < 1)
+    return fail(MX_E_RANGE, "num_blocks (%lld) and block_size (%lld) must be >= 1",
+                (long long)num_blocks, (long long)block_size);
+  if (block_stride_rows < block_size)
+    return fail(MX_E_STRIDE, "block_stride_rows (%lld) is smaller than block_size (%lld)",
+                (long long)block_stride_rows, (long long)block_size);
+  if (num_blocks > (int64_t(0xFFFFFFFF) / block_size))
+    return fail(MX_E_RANGE, "num_blocks * block_size must stay below 2^32");
+  map->num_slots = (uint32_t)(num_blocks * block_size);
+  map->block_size = (uint32_t)block_size;
+  map->block_stride_rows = block_stride_rows;
+  if (num_blocks == 1 || block_stride_rows == block_size) {
+    // Contiguous blocks: the row is the slot itself.
+    map->block_shift = 32;
+    map->block_mask = 0xFFFFFFFFu;
+    map->pow2 = true;
+  } else if (is_pow2(block_size)) {
+    map->block_shift = (uint32_t)log2_exact(block_size);
+    map->block_mask = (uint32_t)block_size - 1u;
+    map->pow2 = true;
+  } else {
+    map->block_shift = 0;
+    map->block_mask = 0;
+    map->pow2 = false;
+  }
+  return MX_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MX_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_rope(const uint16_t* latent, const int64_t* positions, const float* cos_sin,
+               int64_t cos_stride, int64_t cos_rows, uint8_t* cache, int64_t page_stride,
+               int64_t block, int64_t num_blocks, const int64_t* slots, int64_t num_tokens,
+               int32_t cr, int64_t record, mxs::RopeArgs* a) {
+  if (num_tokens < 0) return fail(MX_E_RANGE, "num_tokens must be >= 0");
+  if (cr < 1) return fail(MX_E_ARG, "compress_ratio must be >= 1, got %d", cr);
+  if (block < 1 || num_blocks < 1) return fail(MX_E_RANGE, "cache_block and num_blocks must be >= 1");
+  if (num_blocks > (int64_t(0xFFFFFFFF) / block)) return fail(MX_E_RANGE, "num_blocks * cache_block must stay below 2^32");
+  if (page_stride < block * record || page_stride % 16)
+    return fail(MX_E_STRIDE, "cache_block_stride (%lld) must be a multiple of 16 and >= cache_block * %lld",
+                (long long)page_stride, (long long)record);
+  if (cos_stride < 64) return fail(MX_E_STRIDE, "cos_stride must be >= 64, got %lld", (long long)cos_stride);
+  if (cos_rows < 0) return fail(MX_E_RANGE, "cos_rows must be >= 0");
+  if (num_tokens > 0 && (!latent || !positions || !cos_sin || !cache || !slots))
+    return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(latent, 16) || !aligned(cache, 16) || !aligned(cos_sin, 4))
+    return fail(MX_E_ALIGN, "latent and cache must be 16-byte aligned, cos_sin 4-byte aligned");
+  a->latent = latent;
+  a->positions = positions;
+  a->cos_sin = cos_sin;
+  a->cos_stride = cos_stride;
+  a->cos_rows = cos_rows;
+  a->cache = cache;
+  a->page_stride = page_stride;
+  a->block = (uint32_t)block;
+  a->block_shift = is_pow2(block) ? log2_exact(block) : -1;
+  a->num_slots = (uint32_t)(num_blocks * block);
+  a->slots = slots;
+  a->num_tokens = num_tokens;
+  a->cr = cr;
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mx_row_bytes(int64_t latent, int32_t group) {
+  if (group <= 0 || latent <= 0 || latent % group) return MX_E_SHAPE;
+  return latent / 2 + latent / group;
+}
+
+int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                int64_t src_row_stride, const int64_t* slot_mapping, uint8_t* cache,
+                int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
+                int32_t group, void* stream) {
+  mxs::StoreArgs a{};
+  int rc = check_paged(latent, group, num_blocks, block_size, block_stride_rows, &a.map);
+  if (rc) return rc;
+  if (num_tokens < 0) return fail(MX_E_RANGE, "num_tokens must be >= 0");
+  if (src_row_stride < latent)
+    return fail(MX_E_STRIDE, "src_row_stride (%lld) is smaller than latent (%lld)",
+                (long long)src_row_stride, (long long)latent);
+  if (num_tokens == 0) return ok();
+  if (!src_bf16 || !slot_mapping || !cache) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(src_bf16, 16) || src_row_stride % 8)
+    return fail(MX_E_ALIGN, "latent rows must be 16-byte aligned (base %% 16 == 0, row stride %% 8 == 0)");
+  if (!aligned(cache, 4)) return fail(MX_E_ALIGN, "cache must be 4-byte aligned");
+  a.src = src_bf16;
+  a.src_stride = src_row_stride;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.cache = cache;
+  return launched(mxs::launch_mxfp4_store(a, (int)latent, (hipStream_t)stream), "mxfp4_store");
+}
+
+int mxfp4_gather_dequant(const uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                         int64_t block_stride_rows, int64_t latent, int32_t group,
+                         const int64_t* slots, int64_t num_slots_in_list, uint16_t* out_bf16,
+                         int64_t out_row_stride, void* stream) {
+  mxs::DequantArgs a{};
+  int rc = check_paged(latent, group, num_blocks, block_size, block_stride_rows, &a.map);
+  if (rc) return rc;
+  if (num_slots_in_list < 0) return fail(MX_E_RANGE, "num_slots_in_list must be >= 0");
+  if (out_row_stride < latent)
+    return fail(MX_E_STRIDE, "out_row_stride (%lld) is smaller than latent (%lld)",
+                (long long)out_row_stride, (long long)latent);
+  if (num_slots_in_list == 0) return ok();
+  if (!cache || !slots || !out_bf16) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(out_bf16, 16) || out_row_stride % 8)
+    return fail(MX_E_ALIGN, "output rows must be 16-byte aligned (base %% 16 == 0, row stride %% 8 == 0)");
+  if (!aligned(cache, 4)) return fail(MX_E_ALIGN, "cache must be 4-byte aligned");
+  a.cache = cache;
+  a.slots = slots;
+  a.n = num_slots_in_list;
+  a.out = out_bf16;
+  a.out_stride = out_row_stride;
+  return launched(mxs::launch_mxfp4_dequant(a, (int)latent, (hipStream_t)stream),
+                  "mxfp4_gather_dequant");
+}
+
+int mxfp8_rope_store(const uint16_t* latent_bf16, const int64_t* positions, const float* cos_sin,
+                     int64_t cos_stride, int64_t cos_rows, uint8_t* cache,
+                     int64_t cache_block_stride, int64_t cache_block, int64_t num_blocks,
+                     const int64_t* slot_mapping, int64_t num_tokens, int32_t compress_ratio,
+                     int32_t sanitize_nans, void* stream) {
+  mxs::RopeArgs a{};
+  int rc = check_rope(latent_bf16, positions, cos_sin, cos_stride, cos_rows, cache,
+                      cache_block_stride, cache_block, num_blocks, slot_mapping, num_tokens,
+                      compress_ratio, 528, &a);
+  if (rc) return rc;
+  if (num_tokens == 0) return ok();
+  a.sanitize = sanitize_nans ? 1 : 0;
+  return launched(mxs::launch_mxfp8_rope(a, (hipStream_t)stream), "mxfp8_rope_store");
+}
+
+int nvfp4_rope_store(const uint16_t* latent_bf16, const int64_t* positions, const float* cos_sin,
+                     int64_t cos_stride, int64_t cos_rows, uint8_t* cache,
+                     int64_t cache_block_stride, int64_t cache_block, int64_t num_blocks,
+                     const int64_t* slot_mapping, int64_t num_tokens, int32_t compress_ratio,
+                     int32_t sanitize_nans, void* stream) {
+  mxs::RopeArgs a{};
+  int rc = check_rope(latent_bf16, positions, cos_sin, cos_stride, cos_rows, cache,
+                      cache_block_stride, cache_block, num_blocks, slot_mapping, num_tokens,
+                      compress_ratio, 288, &a);
+  if (rc) return rc;
+  if (num_tokens == 0) return ok();
+  a.sanitize = sanitize_nans ? 1 : 0;
+  return launched(mxs::launch_nvfp4_rope(a, (hipStream_t)stream), "nvfp4_rope_store");
+}
+
+const char* mx_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+"""PyTorch-facing binding of libmxstore: tensors in, device pointers out.
+
+Every function here only checks tensor metadata and marshals pointers,
+sizes and the current HIP stream into the C ABI (include/mxstore.h); all of
+the arithmetic runs in the gfx950 kernels.  PyTorch provides device memory
+and streams, nothing else.
+
+Sources:
+  [P1] docs page "vllm.v1.attention.ops.mxfp4_mla.store", `store_mxfp4_mla`
+  [P2] docs page "vllm.models.deepseek_v41.common.ops.fused_compress_quant_cache",
+       `rope_quant_insert`
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+
+GROUP_SIZE = 32  # values per E8M0 scale (OCP MX block size)
+MXFP8_RECORD_BYTES = 528  # 512 E4M3 values + 16 UE8M0 scales [P2 `rope_quant_insert`]
+NVFP4_RECORD_BYTES = 288  # 256 bytes of E2M1 pairs + 32 E4M3 scales [P2 `rope_quant_insert`]
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _need_cuda(*tensors: torch.Tensor) -> None:
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("libmxstore works on device tensors only")
+
+
+def row_bytes(latent: int, group: int = GROUP_SIZE) -> int:
+    """Bytes of one packed MXFP4 row: latent/2 + latent/group."""
+    n = int(_abi.lib().mx_row_bytes(latent, group))
+    if n < 0:
+        raise ValueError(f"latent {latent} is not a positive multiple of group {group}")
+    return n
+
+
+# ------------------------------------------------------------------ C ABI names
+
+def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                num_blocks: int, block_size: int, block_stride_rows: int,
+                group: int = GROUP_SIZE, stream=None) -> None:
+    """``mxfp4_store`` of the C ABI.  ``src``: bf16 [T, latent], unit inner
+    stride; ``slot_mapping``: int64 [T] contiguous; ``cache``: uint8 storage
+    of the paged view (its data pointer is the cache base)."""
+    _need_cuda(src, slot_mapping, cache)
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    if cache.dtype != torch.uint8:
+        raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
+    num_tokens = slot_mapping.numel()
+    if num_tokens > src.shape[0]:
+        raise ValueError("slot_mapping has more entries than src has rows")
+    _abi.check(_abi.lib().mxfp4_store(
+        src.data_ptr(), num_tokens, src.shape[1], src.stride(0), slot_mapping.data_ptr(),
+        cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
+
+
+def mxfp4_gather_dequant(cache: torch.Tensor, num_blocks: int, block_size: int,
+                         block_stride_rows: int, latent: int, slots: torch.Tensor,
+                         out: torch.Tensor, group: int = GROUP_SIZE, stream=None) -> torch.Tensor:
+    """``mxfp4_gather_dequant`` of the C ABI; fills bf16 ``out`` [n, latent]."""
+    _need_cuda(cache, slots, out)
+    if slots.dtype != torch.int64 or not slots.is_contiguous():
+        raise ValueError("slots must be a contiguous int64 tensor")
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be a bf16 [n, latent] tensor with unit inner stride")
+    if out.shape[0] < slots.numel() or out.shape[1] != latent:
+        raise ValueError("out must have at least len(slots) rows of `latent` values")
+    _abi.check(_abi.lib().mxfp4_gather_dequant(
+        cache.data_ptr(), num_blocks, block_size, block_stride_rows, latent, group,
+        slots.data_ptr(), slots.numel(), out.data_ptr(), out.stride(0), _stream(stream)))
+    return out
+
+
+def _rope_args(latent, positions, cos_sin, kv_cache, slot_mapping, width):
+    _need_cuda(latent, positions, cos_sin, kv_cache, slot_mapping)
+    if latent.dtype != torch.bfloat16 or latent.dim() != 2 or latent.shape[1] != 512 \
+            or not latent.is_contiguous():
+        raise ValueError("latent must be a contiguous bf16 [tokens, 512] tensor")
+    if positions.dtype != torch.int64 or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int64 tensor")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.stride(1) != 1:
+        raise ValueError("cos_sin must be an fp32 [rows, >=64] table with unit inner stride")
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 3 or kv_cache.shape[2] != width \
+            or kv_cache.stride(2) != 1 or kv_cache.stride(1) != width:
+        raise ValueError(f"kv_cache must be uint8 [blocks, block, {width}] with contiguous pages")
+    num_tokens = slot_mapping.numel()
+    if num_tokens > min(latent.shape[0], positions.numel()):
+        raise ValueError("slot_mapping is longer than latent or positions")
+    return (latent.data_ptr(), positions.data_ptr(), cos_sin.data_ptr(), cos_sin.stride(0),
+            cos_sin.shape[0], kv_cache.data_ptr(), kv_cache.stride(0), kv_cache.shape[1],
+            kv_cache.shape[0], slot_mapping.data_ptr(), num_tokens)
+
+
+def mxfp8_rope_store(latent, positions, cos_sin, kv_cache, slot_mapping, compress_ratio,
+                     sanitize_nans: bool = True, stream=None) -> None:
+    """``mxfp8_rope_store`` of the C ABI; ``kv_cache`` is uint8 [blocks, B, 528]."""
+    args = _rope_args(latent, positions, cos_sin, kv_cache, slot_mapping, MXFP8_RECORD_BYTES)
+    _abi.check(_abi.lib().mxfp8_rope_store(*args, int(compress_ratio), int(bool(sanitize_nans)),
+                                           _stream(stream)))
+
+
+def nvfp4_rope_store(latent, positions, cos_sin, kv_cache, slot_mapping, compress_ratio,
+                     sanitize_nans: bool = True, stream=None) -> None:
+    """``nvfp4_rope_store`` of the C ABI; ``kv_cache`` is uint8 [blocks, B, 288]."""
+    args = _rope_args(latent, positions, cos_sin, kv_cache, slot_mapping, NVFP4_RECORD_BYTES)
+    _abi.check(_abi.lib().nvfp4_rope_store(*args, int(compress_ratio), int(bool(sanitize_nans)),
+                                           _stream(stream)))
+
+
+# ------------------------------------------------------------------ page-level API
+
+def resolve_paged_view(cache: torch.Tensor, latent: int, group: int = GROUP_SIZE):
+    """(num_blocks, block_size, block_stride_rows) of a cache tensor [P1
+    `store_mxfp4_mla`]: a 3-D paged [blocks, block, row_bytes] view whose block
+    stride is a whole number of rows, or any tensor viewable as flat rows."""
+    if cache.dtype != torch.uint8:
+        raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
+    pitch = row_bytes(latent, group)
+    if cache.dim() == 3:
+        num_blocks, block_size, width = cache.shape
+        if width != pitch or tuple(cache.stride()[1:]) != (pitch, 1) or cache.stride(0) % pitch:
+            raise ValueError(
+                f"paged cache {tuple(cache.shape)} with strides {cache.stride()} "
+                f"is not a whole number of {pitch}-byte rows per block")
+        return num_blocks, block_size, cache.stride(0) // pitch
+    flat = cache.view(-1)
+    if flat.numel() % pitch:
+        raise ValueError(f"cache of {flat.numel()} bytes is not a multiple of {pitch}")
+    n = flat.numel() // pitch
+    return 1, n, n
+
+
+def store_mxfp4_mla(kv_c_normed: torch.Tensor, slot_mapping: torch.Tensor,
+                    cache: torch.Tensor, group: int = GROUP_SIZE, stream=None) -> None:
+    """Quantize the MLA latent to MXFP4 and write it into the paged cache
+    [P1 `store_mxfp4_mla`]: same arguments and view resolution as the page's
+    wrapper; the work is one ``mxfp4_store`` launch."""
+    if kv_c_normed.dim() != 2:
+        raise ValueError(f"expected kv_c_normed=[tokens, latent], got {tuple(kv_c_normed.shape)}")
+    num_blocks, block_size, stride_rows = resolve_paged_view(cache, kv_c_normed.shape[1], group)
+    if slot_mapping.numel() == 0:
+        return
+    mxfp4_store(kv_c_normed, slot_mapping, cache, num_blocks, block_size, stride_rows,
+                group, stream)
+
+
+def rope_quant_insert(latent, positions, cos_sin_cache, kv_cache, slot_mapping,
+                      compress_ratio: int, sanitize_nans: bool = True, stream=None) -> None:
+    """GPT-J RoPE + quantized insert into a paged compressed cache whose
+    record width selects the format [P2 `rope_quant_insert`]: 528 -> MXFP8,
+    288 -> NVFP4.  Other widths (the 584-byte V4 record, bf16/fp8 plain rows)
+    are not provided by this library."""
+    width = kv_cache.shape[-1] if kv_cache.dim() == 3 else None
+    if kv_cache.dtype != torch.uint8 or width not in (MXFP8_RECORD_BYTES, NVFP4_RECORD_BYTES):
+        raise ValueError(f"unsupported paged KV record: dtype {kv_cache.dtype}, width {width}")
+    fn = mxfp8_rope_store if width == MXFP8_RECORD_BYTES else nvfp4_rope_store
+    fn(latent, positions, cos_sin_cache, kv_cache, slot_mapping, compress_ratio,
+       sanitize_nans, stream)

@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the tests and the benchmark.
+
+This module only draws random inputs and lays out caches; it holds none of
+the quantization arithmetic, and both the GPU path and the CPU oracle are fed
+from it.  Every recipe is deterministic in its seed (numpy PCG64 on the host;
+torch's Philox generator on the device for the 4.5M-token case, whose host
+copy the oracle reads).
+
+Shapes and value distributions follow the workloads the store is built for:
+a 512-wide post-RMSNorm MLA latent, group 32, 272-byte rows, paged caches of
+64-token blocks (optionally interleaved with other layers' pages), pad slots
+(-1), contiguous per-request slot runs (prefill) or scattered slots (decode).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+LATENT = 512
+ROW_BYTES = 272  # 512/2 code bytes + 512/32 scale bytes
+CANARY = 0xA5
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest-even) and return the 16-bit patterns.
+    Inputs are finite; this only shapes test data."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class StoreCase:
+    """One MXFP4 store workload (host arrays)."""
+    name: str
+    src: np.ndarray            # uint16 [T, 512] bf16 bits
+    slots: np.ndarray          # int64 [T]
+    num_blocks: int
+    block_size: int
+    block_stride_rows: int
+    cache_bytes: int           # size of the whole cache buffer
+    gather_slots: np.ndarray | None = None
+    notes: dict = field(default_factory=dict)
+
+    def fresh_cache(self) -> np.ndarray:
+        return np.full(self.cache_bytes, CANARY, dtype=np.uint8)
+
+
+# ------------------------------------------------------------------ config 0
+
+def tiny_case(seed: int = 0) -> StoreCase:
+    """64 tokens of N(0,1); flat cache of 128 slots; a permutation subset of
+    slots with 8 pads at random positions."""
+    rng = np.random.default_rng(seed)
+    src = f32_to_bf16_bits(rng.standard_normal((64, LATENT), dtype=np.float32))
+    slots = rng.permutation(128)[:64].astype(np.int64)
+    slots[rng.choice(64, 8, replace=False)] = -1
+    return StoreCase("tiny", src, slots, 1, 128, 128, 128 * ROW_BYTES)
+
+
+# ------------------------------------------------------------------ config 1
+
+_TIE_MULTIPLES = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float64)
+
+
+def decode_case(seed: int = 1, tokens: int = 256) -> StoreCase:
+    """Decode-shaped batch: Student-t(3) values times a per-row scale
+    2^U(-8, 8), with injected structure per 32-value group (each with
+    probability ~8%): exact powers of two (or 3 * 2^j) as the group maximum,
+    exact E2M1 ties (k-anchored groups: a +-6*2^k element plus +-m*2^k for the
+    midpoint multiples m), all-zero groups with mixed signed zeros, and tiny
+    negatives (below a quarter of the group's scale, and exactly a quarter),
+    some with extreme anchors (k = -126, -120, 20, 60, 125).  Paged cache of
+    4096 blocks x 64 slots with a block stride of 192 rows (two other layers
+    interleaved); distinct random slots with 10% pads."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(3, size=(tokens, LATENT)) * np.exp2(rng.uniform(-8, 8, size=(tokens, 1)))
+    x = x.astype(np.float64)
+    groups = x.reshape(tokens, LATENT // 32, 32)
+    kinds = rng.random(groups.shape[:2])
+    for t in range(tokens):
+        for g in range(LATENT // 32):
+            grp = groups[t, g]
+            r = kinds[t, g]
+            if r < 0.08:  # power of two (or three times one) as the amax
+                j = int(np.ceil(np.log2(np.max(np.abs(grp)) + 1e-30))) + int(rng.integers(1, 3))
+                mag = 2.0 ** j * (3.0 if rng.random() < 0.5 else 1.0)
+                grp[rng.integers(32)] = mag * rng.choice([-1.0, 1.0])
+            elif r < 0.16:  # exact ties
+                k = int(rng.integers(-10, 10))
+                grp[:] = rng.choice(_TIE_MULTIPLES, 32) * rng.choice([-1.0, 1.0], 32) * 2.0 ** k
+                grp[rng.integers(32)] = 6.0 * 2.0 ** k * rng.choice([-1.0, 1.0])
+            elif r < 0.24:  # all-zero group, mixed signs of zero
+                grp[:] = np.where(rng.random(32) < 0.5, -0.0, 0.0)
+            elif r < 0.32:  # tiny negatives under a known scale
+                k = int(rng.choice([-126, -120, -3, 0, 5, 20, 60, 125]))
+                scale = 2.0 ** k
+                grp[:] = rng.uniform(-6, 6, 32) * scale
+                grp[0] = 6.0 * scale
+                grp[1] = -0.25 * scale
+                grp[2:10] = -rng.uniform(0, 0.25, 8) * scale
+                grp[10] = -(2.0 ** (k - 140))  # tiny; still nonzero after division
+                grp[11] = -0.0
+                grp[12] = -(2.0 ** (k - 151))  # divided by 2^k: below half the least subnormal
+                grp[13] = -(2.0 ** (k - 149))  # divided by 2^k: the least fp32 subnormal
+    with np.errstate(over="ignore", under="ignore"):
+        src = f32_to_bf16_bits(x.astype(np.float32))
+    nb, bs, stride = 4096, 64, 192
+    slots = rng.choice(nb * bs, tokens, replace=False).astype(np.int64)
+    slots[rng.choice(tokens, tokens // 10, replace=False)] = -1
+    return StoreCase("decode", src, slots, nb, bs, stride, nb * stride * ROW_BYTES)
+
+
+# ------------------------------------------------------------------ config 2
+
+def prefill_case(seed: int = 2, tokens: int = 16384, requests: int = 32) -> StoreCase:
+    """Prefill chunk: N(0,1) times a per-row scale 2^U(-20, 20).  Paged cache
+    of 8192 blocks x 64 (contiguous blocks).  32 requests with lengths
+    U[448, 512), each a contiguous run of slots starting at the first slot of
+    a distinct random block (runs do not overlap); the batch is padded to
+    16384 tokens with -1."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((tokens, LATENT)) * np.exp2(rng.uniform(-20, 20, size=(tokens, 1)))
+    src = f32_to_bf16_bits(x.astype(np.float32))
+    nb, bs = 8192, 64
+    lengths = rng.integers(448, 512, size=requests)
+    starts = rng.choice(nb // 8, requests, replace=False) * 8  # 8 blocks = 512 slots apart
+    runs = [np.arange(s * bs, s * bs + n, dtype=np.int64) for s, n in zip(starts, lengths)]
+    valid = np.concatenate(runs)
+    assert valid.size <= tokens
+    slots = np.full(tokens, -1, dtype=np.int64)
+    slots[: valid.size] = valid
+    case = StoreCase("prefill", src, slots, nb, bs, bs, nb * bs * ROW_BYTES)
+    case.gather_slots = valid.copy()
+    return case
+
+
+# ------------------------------------------------------------------ config 3
+
+LARGE_TOKENS = 4_500_000
+
+
+def large_case_device(tokens: int = LARGE_TOKENS, seed: int = 3, device: str = "cuda"):
+    """4.5M tokens uniform in [-4, 4] (2.3e9 values, past 2^31) and a random
+    permutation of the 4.5M flat slots, drawn on the device with torch's
+    seeded generator.  Returns (src bf16 [T, 512], slots int64 [T])."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    src = torch.empty((tokens, LATENT), dtype=torch.bfloat16, device=device)
+    # fill in chunks to bound the fp32 temporary
+    chunk = 1 << 20
+    for lo in range(0, tokens, chunk):
+        hi = min(tokens, lo + chunk)
+        tmp = torch.empty((hi - lo, LATENT), dtype=torch.float32, device=device)
+        tmp.uniform_(-4.0, 4.0, generator=g)
+        src[lo:hi].copy_(tmp)
+        del tmp
+    slots = torch.randperm(tokens, generator=g, device=device, dtype=torch.int64)
+    return src, slots
+
+
+def large_sample_host(tokens: int, seed: int = 3) -> tuple[np.ndarray, np.ndarray]:
+    """A host-side batch with the large workload's distribution (uniform in
+    [-4, 4], random-permutation slots over `tokens` flat slots), used to time
+    the CPU oracle on a bounded sample."""
+    rng = np.random.default_rng(seed)
+    src = f32_to_bf16_bits(rng.uniform(-4, 4, size=(tokens, LATENT)).astype(np.float32))
+    slots = rng.permutation(tokens).astype(np.int64)
+    return src, slots
+
+
+# ------------------------------------------------------------------ config 4
+
+@dataclass
+class RopeCase:
+    latent: np.ndarray       # uint16 [T, 512]
+    positions: np.ndarray    # int64 [T]
+    cos_sin: np.ndarray      # fp32 [65536, 64]
+    slots: np.ndarray        # int64 [T]
+    block: int
+    num_blocks: int
+    compress_ratio: int
+
+
+def rope_cos_sin_table(rows: int = 65536, rot_dim: int = 64, theta: float = 10000.0) -> np.ndarray:
+    """GPT-J RoPE table: row p = [cos(p*w_j) for j<32 | sin(p*w_j) for j<32],
+    w_j = theta^(-2j/rot_dim); built in float64, rounded once to fp32."""
+    j = np.arange(rot_dim // 2, dtype=np.float64)
+    inv = theta ** (-2.0 * j / rot_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def rope_case(seed: int = 4, tokens: int = 16384, compress_ratio: int = 4) -> RopeCase:
+    """16384 tokens of N(0,1); positions U[0, 65536); compress ratio 4;
+    cache block 64 over 256 blocks; slots a random permutation of the
+    16384 slots."""
+    rng = np.random.default_rng(seed)
+    latent = f32_to_bf16_bits(rng.standard_normal((tokens, LATENT), dtype=np.float32))
+    positions = rng.integers(0, 65536, size=tokens, dtype=np.int64)
+    slots = rng.permutation(tokens).astype(np.int64)
+    return RopeCase(latent, positions, rope_cos_sin_table(), slots, 64, tokens // 64, compress_ratio)

@@ -1,0 +1,136 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/*.h declares, and rejects arguments outside the contract with the
+documented status before any device work (these calls never reach HIP)."""
+
+import glob
+import os
+import re
+
+import pytest
+
+from mxfp4_paged_cache_store_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(mxlib):
+    declared = declared_functions()
+    assert set(declared) == set(_abi.EXPORTED), declared
+    for name in declared:
+        assert hasattr(mxlib, name), name
+
+
+def test_row_bytes(mxlib):
+    assert mxlib.mx_row_bytes(512, 32) == 272
+    assert mxlib.mx_row_bytes(128, 32) == 68
+    assert mxlib.mx_row_bytes(1024, 32) == 544
+    assert mxlib.mx_row_bytes(100, 32) == _abi.MX_E_SHAPE
+    assert mxlib.mx_row_bytes(512, 0) == _abi.MX_E_SHAPE
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced
+
+
+def store(mxlib, **kw):
+    a = dict(src=FAKE, n=4, latent=512, stride=512, slots=FAKE, cache=FAKE, nb=1, bs=8,
+             bsr=8, group=32)
+    a.update(kw)
+    return mxlib.mxfp4_store(a["src"], a["n"], a["latent"], a["stride"], a["slots"], a["cache"],
+                             a["nb"], a["bs"], a["bsr"], a["group"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group=16), _abi.MX_E_SHAPE),
+    (dict(latent=500, stride=512), _abi.MX_E_SHAPE),
+    (dict(latent=64, stride=64), _abi.MX_E_SHAPE),
+    (dict(latent=4096, stride=4096), _abi.MX_E_SHAPE),
+    (dict(bsr=4), _abi.MX_E_STRIDE),
+    (dict(stride=256), _abi.MX_E_STRIDE),
+    (dict(n=-1), _abi.MX_E_RANGE),
+    (dict(nb=0), _abi.MX_E_RANGE),
+    (dict(nb=1 << 30, bs=64, bsr=64), _abi.MX_E_RANGE),
+    (dict(src=0), _abi.MX_E_NULL),
+    (dict(slots=0), _abi.MX_E_NULL),
+    (dict(src=FAKE + 8), _abi.MX_E_ALIGN),
+    (dict(stride=516), _abi.MX_E_ALIGN),
+    (dict(cache=FAKE + 2), _abi.MX_E_ALIGN),
+])
+def test_store_rejects(mxlib, kw, status):
+    assert store(mxlib, **kw) == status
+    assert mxlib.mx_last_error().decode()
+
+
+def test_store_zero_tokens_is_a_noop(mxlib):
+    # null pointers are fine when there is nothing to do; nothing is launched
+    assert store(mxlib, n=0, src=0, slots=0, cache=0) == _abi.MX_OK
+    assert mxlib.mx_last_error().decode() == ""
+
+
+def dequant(mxlib, **kw):
+    a = dict(cache=FAKE, nb=1, bs=8, bsr=8, latent=512, group=32, slots=FAKE, n=3, out=FAKE,
+             ostride=512)
+    a.update(kw)
+    return mxlib.mxfp4_gather_dequant(a["cache"], a["nb"], a["bs"], a["bsr"], a["latent"],
+                                      a["group"], a["slots"], a["n"], a["out"], a["ostride"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group=64), _abi.MX_E_SHAPE),
+    (dict(bsr=7), _abi.MX_E_STRIDE),
+    (dict(ostride=100), _abi.MX_E_STRIDE),
+    (dict(ostride=520 + 4), _abi.MX_E_ALIGN),
+    (dict(out=FAKE + 4), _abi.MX_E_ALIGN),
+    (dict(n=-2), _abi.MX_E_RANGE),
+    (dict(out=0), _abi.MX_E_NULL),
+])
+def test_dequant_rejects(mxlib, kw, status):
+    assert dequant(mxlib, **kw) == status
+
+
+def test_dequant_empty_list_is_a_noop(mxlib):
+    assert dequant(mxlib, n=0, cache=0, slots=0, out=0) == _abi.MX_OK
+
+
+def rope(mxlib, fn, **kw):
+    a = dict(latent=FAKE, pos=FAKE, cs=FAKE, cstride=64, crows=100, cache=FAKE, pstride=64 * 528,
+             block=64, nb=4, slots=FAKE, n=5, cr=4, san=1)
+    a.update(kw)
+    return getattr(mxlib, fn)(a["latent"], a["pos"], a["cs"], a["cstride"], a["crows"], a["cache"],
+                              a["pstride"], a["block"], a["nb"], a["slots"], a["n"], a["cr"],
+                              a["san"], None)
+
+
+@pytest.mark.parametrize("fn,width", [("mxfp8_rope_store", 528), ("nvfp4_rope_store", 288)])
+@pytest.mark.parametrize("kw,status", [
+    (dict(cr=0), _abi.MX_E_ARG),
+    (dict(pstride=100), _abi.MX_E_STRIDE),
+    (dict(cstride=32), _abi.MX_E_STRIDE),
+    (dict(block=0), _abi.MX_E_RANGE),
+    (dict(n=-1), _abi.MX_E_RANGE),
+    (dict(latent=0), _abi.MX_E_NULL),
+    (dict(cache=FAKE + 8), _abi.MX_E_ALIGN),
+])
+def test_rope_rejects(mxlib, fn, width, kw, status):
+    if "pstride" not in kw:
+        kw = dict(kw, pstride=64 * width)
+    assert rope(mxlib, fn, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["mxfp8_rope_store", "nvfp4_rope_store"])
+def test_rope_empty_is_a_noop(mxlib, fn):
+    assert rope(mxlib, fn, n=0, latent=0, pos=0, cs=0, cache=0, slots=0) == _abi.MX_OK
+
+
+def test_nvfp4_record_width_checked(mxlib):
+    # a 288-byte page stride is too small for the 528-byte record
+    assert rope(mxlib, "mxfp8_rope_store", pstride=64 * 288) == _abi.MX_E_STRIDE
