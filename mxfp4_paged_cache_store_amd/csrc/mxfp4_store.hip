@@ -28,7 +28,9 @@
 //     dword l of the row (low nibble = lower index).
 //   * The 16 scale bytes are gathered with row_shr DPP moves into four
 //     dwords held by lanes 12, 28, 44 and 60.  The row is written as whole
-//     dwords: 64 code dwords + 4 scale dwords, non-temporal.
+//     dwords: 64 code dwords + 4 scale dwords.  When a wave's tokens fill
+//     consecutive slots the stores are plain (L2 merges neighbouring rows
+//     into whole lines); scattered rows use non-temporal stores.
 //   * Slots are read by the scalar unit, a whole wave's in one load.  A pad
 //     or out-of-range slot skips the token's load as well as its store: the
 //     load goes through a raw buffer descriptor whose range is the token's
@@ -42,7 +44,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTokensPerWave = 8;
+constexpr int kTokensPerWave = 4;
 constexpr int kWavesPerBlock = 4;
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -79,12 +81,11 @@ __device__ __forceinline__ uint32_t encode8(const u32x4 w, float mul) {
   return c;
 }
 
-// Quantizes the 512-value slice held by the wave (16 bytes per lane) and
-// writes it into `row`: code dword `lane_in_tok` at code_base and, from the
-// lanes 12 mod 16, the 4 gathered scale bytes at scale_base.
-__device__ __forceinline__ void quantize_slice(const u32x4 w, int lane_in_tok,
-                                               uint8_t* code_base, uint8_t* scale_base,
-                                               bool store) {
+// Quantizes the 512-value slice held by the wave (16 bytes per lane):
+// returns the lane's code dword (codes of its 8 values) and, in `sdw`, the
+// scale dword that the lanes 12 mod 16 store (scale bytes of groups
+// 4k..4k+3 for lane 16k+12).
+__device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw) {
   const uint32_t amax = group_amax_bits(w);
   const bool nonfinite = amax >= 0x7F80u;
   int e = (int)(amax >> 7) - 129 + ((amax & 0x7Fu) > 64u ? 1 : 0);
@@ -97,13 +98,9 @@ __device__ __forceinline__ void quantize_slice(const u32x4 w, int lane_in_tok,
   if (nonfinite) codes = 0u;
 
   // Scale dword k = groups 4k..4k+3 = lanes 16k, 16k+4, 16k+8, 16k+12.
-  const uint32_t sdw = dpp<kRowShr12>(scale_byte) | (dpp<kRowShr8>(scale_byte) << 8) |
-                       (dpp<kRowShr4>(scale_byte) << 16) | (scale_byte << 24);
-  if (store) {
-    __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(code_base) + lane_in_tok);
-    if ((lane_in_tok & 15) == 12)
-      __builtin_nontemporal_store(sdw, reinterpret_cast<uint32_t*>(scale_base) + (lane_in_tok >> 4));
-  }
+  sdw = dpp<kRowShr12>(scale_byte) | (dpp<kRowShr8>(scale_byte) << 8) |
+        (dpp<kRowShr4>(scale_byte) << 16) | (scale_byte << 24);
+  return codes;
 }
 
 // LATENT: values per token (power of two, 128..2048).  A token occupies
@@ -163,13 +160,52 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
     }
   }
 
+  // A wave whose tokens fill consecutive slots writes adjacent rows: plain
+  // stores let L2 assemble whole lines from them.  Scattered rows are
+  // streamed with non-temporal stores instead (measured faster for rows
+  // whose neighbours are written at unrelated times).
+  bool run = true;
+#pragma unroll
+  for (int p = 1; p < kTokensPerWave; ++p) run = run && slot[p] == slot[p - 1] + kToksPerPass;
+  run = run && row_off[0] >= 0 && row_off[kTokensPerWave - 1] >= 0;
+
 #pragma unroll
   for (int p = 0; p < kTokensPerWave; ++p) {
-    const bool ok = row_off[p] >= 0;
-    uint8_t* row = a.cache + (ok ? row_off[p] : 0);
+    if constexpr (kToksPerPass == 1) {
+      // Raw buffer over the token's row (empty when skipped): the hardware
+      // range check drops the stores of a skipped token and of every lane
+      // but the scale lanes at the out-of-range offset kDrop.  The two cache
+      // policies are distinct instructions, so they stay separate.
+      constexpr uint32_t kDrop = 0x7FFFFFF0u;
+      const bool ok = row_off[p] >= 0;
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_at(a.cache + (ok ? row_off[p] : 0), ok ? (uint32_t)kPitch : 0u);
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub)
-      quantize_slice(v[p][sub], lane_in_tok, row + sub * 256, row + LATENT / 2 + sub * 16, ok);
+      for (int sub = 0; sub < kSub; ++sub) {
+        uint32_t sdw;
+        const uint32_t codes = quantize_slice(v[p][sub], sdw);
+        const uint32_t code_off = sub * 256 + lane_in_tok * 4;
+        const uint32_t scale_off =
+            (lane_in_tok & 15) == 12 ? LATENT / 2 + sub * 16 + (lane_in_tok >> 4) * 4 : kDrop;
+        if (run) {
+          __builtin_amdgcn_raw_buffer_store_b32(codes, rs, code_off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(codes, rs, code_off, 0, kBufNT);
+          __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, kBufNT);
+        }
+      }
+    } else {
+      uint32_t sdw;
+      const uint32_t codes = quantize_slice(v[p][0], sdw);
+      if (row_off[p] < 0) continue;
+      uint32_t* code_dst = reinterpret_cast<uint32_t*>(a.cache + row_off[p]) + lane_in_tok;
+      if (run) *code_dst = codes; else __builtin_nontemporal_store(codes, code_dst);
+      if ((lane_in_tok & 15) == 12) {
+        uint32_t* scale_dst = reinterpret_cast<uint32_t*>(a.cache + row_off[p] + LATENT / 2) + (lane_in_tok >> 4);
+        if (run) *scale_dst = sdw; else __builtin_nontemporal_store(sdw, scale_dst);
+      }
+    }
   }
 }
 

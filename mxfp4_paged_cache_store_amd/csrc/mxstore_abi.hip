@@ -6,7 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/mxstore.h"
+#include "mxstore.h"
 #include "kernels.hpp"
 
 namespace {
