@@ -1,11 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP4 paged-cache store on one MI355X.
 
-A step is one mxfp4_store launch over the whole batch: 4,500,000 tokens x
-512 bf16 (uniform in [-4, 4]) scattered to a random permutation of the slots
-of a flat 1.224 GB cache; inputs are resident in HBM before timing.  The
-gather-dequant and the two RoPE+quant inserts are timed after it, each on
-its own workload, and reported under "companions".
+A step is one MXFP4 store of the whole batch: 4,500,000 tokens x 512 bf16
+(uniform in [-4, 4]) into a random permutation of the slots of a flat
+1.224 GB cache; inputs are resident in HBM before timing.  For this dense
+scattered batch the library advises its slot-order form, so a step is
+mxfp4_build_inverse + mxfp4_store_by_slot; the scatter form (mxfp4_store) is
+timed beside it.  The roofline entry is for the dominant kernel (the
+slot-order store), timed alone with HIP events.  The gather-dequant and the
+two RoPE+quant inserts are timed after it, each on its own workload, and
+reported under "companions".
 
 Output: one JSON line (see the fields below).  `--sweep` prints further
 lines for the token-count / slot-pattern sweep with the Infinity Cache
@@ -27,6 +31,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BYTES_PER_TOKEN = 1024 + 272 + 8  # latent read + row written + slot read
 BYTES_PER_PAD = 8
+# The slot-order store reads one int32 inverse entry per slot instead of the
+# 8-byte slot of each token.
+BY_SLOT_BYTES_PER_TOKEN = 1024 + 272
+BY_SLOT_BYTES_PER_SLOT = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mxfp4_store_large_traffic.txt")
 STORE_SRC = os.path.join(ROOT, "mxfp4_paged_cache_store_amd", "csrc", "mxfp4_store.hip")
 
@@ -41,6 +49,9 @@ def parse():
     p.add_argument("--no-companions", action="store_true")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1_000_000)
+    p.add_argument("--scatter", action="store_true", help="time the scatter form as the step")
+    p.add_argument("--counters", action="store_true",
+                   help="for rocprofv3 --pmc: a 1 GiB copy (calibration) then 3 steps, no JSON")
     return p.parse_args()
 
 
@@ -49,9 +60,10 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(tokens: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source and this token count."""
+def measured_traffic(tokens: int, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source and this token
+    count."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -61,7 +73,7 @@ def measured_traffic(tokens: int):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256_16") != source_digest(STORE_SRC):
         return None
-    if int(kv.get("tokens", -1)) != tokens:
+    if int(kv.get("tokens", -1)) != tokens or kv.get("kernel") != kernel:
         return None
     return int(float(kv["hbm_bytes_per_launch"]))
 
@@ -147,11 +159,13 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
 
 
 def run_sweep(torch, ops):
-    """Store throughput vs token count and slot pattern, Infinity Cache
-    flushed (a 1 GiB write) before each repetition; median of 20."""
+    """Store throughput vs token count and slot pattern, both forms, with the
+    Infinity Cache flushed before each repetition by reading a 1 GiB buffer
+    (a write-flush would leave dirty lines to be written back during the
+    timed kernel); median of 20."""
     import statistics
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     for n in (16384, 65536, 262144, 1048576, 4500000):
         for pattern in ("runs", "random"):
             src = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda").uniform_(-4, 4)
@@ -160,24 +174,32 @@ def run_sweep(torch, ops):
             else:
                 slots = torch.arange(n, device="cuda", dtype=torch.int64)
             cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
-            times = []
-            for _ in range(22):
-                flush.fill_(1)
-                torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                ops.mxfp4_store(src, slots, cache, 1, n, n)
-                e1.record()
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1) / 1000.0)
-            t = statistics.median(times[2:])
-            gbs = n * BYTES_PER_TOKEN / t / 1e9
-            print(json.dumps({"sweep": "mxfp4_store", "tokens": n, "slots": pattern,
-                              "us": round(t * 1e6, 2), "GBps": round(gbs, 1),
-                              "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                              "cache": "flushed"}), flush=True)
-            del src, slots, cache
+            inv = torch.empty(n, dtype=torch.int32, device="cuda")
+            forms = {"scatter": lambda: ops.mxfp4_store(src, slots, cache, 1, n, n)}
+            if ops.mxfp4_slot_order_advised(n, 512, 1, n):
+                def slot_order():
+                    ops.mxfp4_build_inverse(slots, 1, n, inv)
+                    ops.mxfp4_store_by_slot(src, n, inv, cache, 1, n, n)
+                forms["slot_order"] = slot_order
+            for form, fn in forms.items():
+                times = []
+                for _ in range(22):
+                    flush.sum()
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1) / 1000.0)
+                t = statistics.median(times[2:])
+                gbs = n * BYTES_PER_TOKEN / t / 1e9
+                print(json.dumps({"sweep": "mxfp4_store", "form": form, "tokens": n, "slots": pattern,
+                                  "us": round(t * 1e6, 2), "GBps": round(gbs, 1),
+                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                  "cache": "flushed"}), flush=True)
+            del src, slots, cache, inv
 
 
 def main():
@@ -202,16 +224,50 @@ def main():
     src, slots = workloads.large_case_device(n)
     cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
     valid = n  # a permutation: no pad slots
+    num_slots = n
+    slot_order = ops.mxfp4_slot_order_advised(n, 512, 1, num_slots) and not args.scatter
+    inv = torch.empty(num_slots, dtype=torch.int32, device="cuda")
 
-    def step():
-        ops.mxfp4_store(src, slots, cache, 1, n, n)
+    def scatter_step():
+        ops.mxfp4_store(src, slots, cache, 1, num_slots, num_slots)
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    def store_by_slot():
+        ops.mxfp4_store_by_slot(src, n, inv, cache, 1, num_slots, num_slots)
+
+    def slot_order_step():
+        ops.mxfp4_build_inverse(slots, 1, num_slots, inv)
+        store_by_slot()
+
+    step = slot_order_step if slot_order else scatter_step
+
+    if args.counters:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)  # calibration: 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        print("[bench] counters run done", file=sys.stderr, flush=True)
+        return
+
+    print(f"[bench] timing {args.steps} steps ({'slot order' if slot_order else 'scatter'})",
+          file=sys.stderr, flush=True)
     wall, ev = time_launches(step, args.steps, args.warmup, torch)
-    per_launch = ev / args.steps
-    algo_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
+    step_s = ev / args.steps
+    if slot_order:
+        kernel = "mxfp4_store_by_slot_kernel<512>"
+        _, kev = time_launches(store_by_slot, args.steps, args.warmup, torch)
+        per_launch = kev / args.steps
+        algo_bytes = valid * BY_SLOT_BYTES_PER_TOKEN + num_slots * BY_SLOT_BYTES_PER_SLOT
+    else:
+        kernel = "mxfp4_store_kernel<512>"
+        per_launch = step_s
+        algo_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
+    _, sev = time_launches(scatter_step, args.steps, args.warmup, torch)
+    scatter_s = sev / args.steps
     achieved = algo_bytes / per_launch / 1e9
-    traffic = measured_traffic(n)
+    traffic = measured_traffic(n, kernel)
 
     result = {
         "metric": "MXFP4 store tokens/s and effective HBM GB/s (% of MI355X peak), 1 GPU",
@@ -232,11 +288,14 @@ def main():
             "tokens": n,
             "latent": 512,
             "row_bytes": 272,
+            "form": "slot order (build_inverse + store_by_slot)" if slot_order else "scatter (mxfp4_store)",
             "parallelism": "single GPU",
         },
         "effective_GBps": round(valid * BYTES_PER_TOKEN * args.steps / wall / 1e9, 1),
+        "frac_hbm_peak_whole_step": round(valid * BYTES_PER_TOKEN / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
+            "kernel": kernel,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -245,11 +304,17 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
             "kernel_us_per_launch": round(per_launch * 1e6, 2),
         },
+        "scatter_form": {
+            "kernel": "mxfp4_store_kernel<512>",
+            "us_per_launch": round(scatter_s * 1e6, 2),
+            "GBps": round(valid * BYTES_PER_TOKEN / scatter_s / 1e9, 1),
+            "frac_hbm_peak": round(valid * BYTES_PER_TOKEN / scatter_s / 1e9 / HBM_PEAK_GBS, 4),
+        },
     }
     if not args.no_companions:
         print("[bench] companions", file=sys.stderr, flush=True)
         result["companions"] = companions(torch, ops, workloads, args.steps, args.warmup, cache, n)
-    del src, slots
+    del src, slots, inv
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample)

@@ -85,6 +85,55 @@ int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
                 int64_t block_stride_rows, int32_t group, void* stream);
 
 /*
+ * Slot-order form of the MXFP4 store, in two calls.  For a batch that fills
+ * most of the cache's slots in scattered order (e.g. a random permutation),
+ * scattered 272-byte row writes are what limits mxfp4_store: DRAM serves
+ * scattered 1 KiB reads at nearly full speed but scattered sub-line writes at
+ * well under half.  The slot-order form inverts the scatter: an inverse map
+ * inverse[s] = token of slot s (or -1) is built once per slot mapping -- it
+ * serves every layer that stores with that mapping in the step -- and the
+ * store then walks the slots in order, gathers each slot's latent row and
+ * writes the rows sequentially.  It writes exactly the bytes mxfp4_store
+ * writes (for a slot used by several tokens, one of them lands in both).
+ */
+
+/* Bytes of the inverse map: one int32 per slot (num_blocks * block_size),
+ * rounded up to 16.  MX_E_RANGE if num_blocks or block_size < 1 or the slot
+ * count reaches 2^32.  Host-only. */
+int64_t mxfp4_inverse_bytes(int64_t num_blocks, int64_t block_size);
+
+/* 1 when the slot-order form is expected to beat mxfp4_store for this shape:
+ * latent in {512, 1024, 2048}, 2^16 <= num_tokens < 2^31 and num_tokens >=
+ * half the slots; else 0.  Host-only heuristic (measured on MI355X), no
+ * device work. */
+int mxfp4_slot_order_advised(int64_t num_tokens, int64_t latent,
+                             int64_t num_blocks, int64_t block_size);
+
+/*
+ * Build the inverse map of a slot mapping: inverse[s] = -1 for every slot,
+ * then inverse[slot_mapping[t]] = t for every t < num_tokens whose slot is in
+ * [0, num_blocks * block_size).  inverse: device int32 buffer of at least
+ * mxfp4_inverse_bytes(num_blocks, block_size) bytes, 16-byte aligned,
+ * overwritten.  num_tokens < 2^31.  Two launches on `stream`.
+ */
+int mxfp4_build_inverse(const int64_t* slot_mapping, int64_t num_tokens,
+                        int64_t num_blocks, int64_t block_size, int32_t* inverse,
+                        int64_t inverse_bytes, void* stream);
+
+/*
+ * MXFP4 store in slot order: same arguments and result as mxfp4_store, with
+ * the slot mapping replaced by its inverse map (built by mxfp4_build_inverse
+ * for the same num_blocks and block_size; entries outside [0, num_tokens) are
+ * skipped).  latent must be 512, 1024 or 2048; inverse 16-byte aligned.  One
+ * launch over all num_blocks * block_size slots, so it is meant for batches
+ * that cover a large share of them (mxfp4_slot_order_advised).
+ */
+int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                        int64_t src_row_stride, const int32_t* inverse,
+                        uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                        int64_t block_stride_rows, int32_t group, void* stream);
+
+/*
  * MXFP4 gather-dequant [P3 Details, read path: unpack to bf16; Claims: the
  * result equals the dequantized values stored as bf16].  For each i <
  * num_slots_in_list with slot s = slots[i] in range, writes

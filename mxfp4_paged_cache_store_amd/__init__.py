@@ -13,6 +13,10 @@ from .ops import (
     NVFP4_RECORD_BYTES,
     mxfp4_gather_dequant,
     mxfp4_store,
+    mxfp4_build_inverse,
+    mxfp4_inverse_bytes,
+    mxfp4_slot_order_advised,
+    mxfp4_store_by_slot,
     mxfp8_rope_store,
     nvfp4_rope_store,
     resolve_paged_view,
@@ -29,6 +33,10 @@ __all__ = [
     "MxError",
     "mxfp4_gather_dequant",
     "mxfp4_store",
+    "mxfp4_build_inverse",
+    "mxfp4_inverse_bytes",
+    "mxfp4_slot_order_advised",
+    "mxfp4_store_by_slot",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
     "resolve_paged_view",

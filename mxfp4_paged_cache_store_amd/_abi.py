@@ -25,6 +25,10 @@ MX_E_LAUNCH = -7
 EXPORTED = (
     "mx_row_bytes",
     "mxfp4_store",
+    "mxfp4_inverse_bytes",
+    "mxfp4_slot_order_advised",
+    "mxfp4_build_inverse",
+    "mxfp4_store_by_slot",
     "mxfp4_gather_dequant",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
@@ -61,6 +65,14 @@ def lib() -> ctypes.CDLL:
         L.mx_row_bytes.argtypes = [_i64, _i32]
         L.mxfp4_store.restype = ctypes.c_int
         L.mxfp4_store.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
+        L.mxfp4_inverse_bytes.restype = _i64
+        L.mxfp4_inverse_bytes.argtypes = [_i64, _i64]
+        L.mxfp4_slot_order_advised.restype = ctypes.c_int
+        L.mxfp4_slot_order_advised.argtypes = [_i64, _i64, _i64, _i64]
+        L.mxfp4_build_inverse.restype = ctypes.c_int
+        L.mxfp4_build_inverse.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
+        L.mxfp4_store_by_slot.restype = ctypes.c_int
+        L.mxfp4_store_by_slot.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
         L.mxfp4_gather_dequant.restype = ctypes.c_int
         L.mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp]
         for name in ("mxfp8_rope_store", "nvfp4_rope_store"):

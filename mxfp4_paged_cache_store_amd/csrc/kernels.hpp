@@ -46,6 +46,12 @@ struct RopeArgs {
 
 // Each returns the hipError_t of the launch.
 hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream);
+// Slot-order form: inverse[s] = token of slot s or -1 (num_slots int32,
+// 16-byte aligned), then the gather-store over all slots.
+hipError_t launch_build_inverse(const int64_t* slots, int64_t num_tokens, uint32_t num_slots,
+                                int32_t* inverse, hipStream_t stream);
+hipError_t launch_mxfp4_store_by_slot(const StoreArgs& a, int latent, const int32_t* inverse,
+                                      hipStream_t stream);
 hipError_t launch_mxfp4_dequant(const DequantArgs& a, int latent, hipStream_t stream);
 hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream);

@@ -209,6 +209,103 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
   }
 }
 
+// ---------------------------------------------------------------------------
+// Slot-order form.  For a batch that fills most of the cache's slots in a
+// scattered order (e.g. a random permutation), scattered 272-byte row writes
+// are the bottleneck: DRAM serves random 1 KiB reads at nearly full speed but
+// random sub-line writes at well under half.  So the scatter is inverted:
+// inv[s] = t is built once per slot mapping (it serves every layer that
+// stores with that mapping), then waves walk slots in order, gather the token
+// row inv[s] (or nothing) and write rows sequentially.  The bytes written are
+// identical to the scatter form (for duplicate slots either form keeps one of
+// the tokens).
+
+constexpr int kSlotsPerWave = 8;
+
+__global__ __launch_bounds__(256) void fill_inverse(int32_t* __restrict__ inv, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    *reinterpret_cast<u32x4*>(inv + i) = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  } else {
+    for (int64_t k = i; k < n; ++k) inv[k] = -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void invert_slots(const int64_t* __restrict__ slots, int64_t n,
+                                                    int32_t* __restrict__ inv, uint32_t num_slots) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int64_t s = slots[t];
+  if (s >= 0 && s < (int64_t)num_slots) inv[s] = (int32_t)t;
+}
+
+template <int LATENT, bool kPow2>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_kernel(
+    const StoreArgs a, const int32_t* __restrict__ inv) {
+  static_assert(LATENT >= 512, "slot order is used for latents of 512 and more");
+  constexpr int kSub = LATENT / 512;
+  constexpr int64_t kPitch = LATENT / 2 + LATENT / 32;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t s0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kSlotsPerWave;
+  const int64_t num_slots = a.map.num_slots;
+
+  int32_t tok[kSlotsPerWave];
+  if (s0 + kSlotsPerWave <= num_slots) {
+#pragma unroll
+    for (int p = 0; p < kSlotsPerWave; ++p) tok[p] = inv[s0 + p];
+  } else {
+#pragma unroll
+    for (int p = 0; p < kSlotsPerWave; ++p) tok[p] = s0 + p < num_slots ? inv[s0 + p] : -1;
+  }
+  // An entry is a token of this batch or -1; anything else is skipped.
+#pragma unroll
+  for (int p = 0; p < kSlotsPerWave; ++p)
+    if ((int64_t)tok[p] >= a.num_tokens) tok[p] = -1;
+
+  u32x4 v[kSlotsPerWave][kSub];
+#pragma unroll
+  for (int p = 0; p < kSlotsPerWave; ++p) {
+    const bool ok = tok[p] >= 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_at(a.src + (ok ? (int64_t)tok[p] * a.src_stride : 0), ok ? LATENT * 2 : 0);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub)
+      v[p][sub] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (sub * 64 + lane) * 16, 0, kBufNT));
+  }
+
+  constexpr uint32_t kDrop = 0x7FFFFFF0u;
+#pragma unroll
+  for (int p = 0; p < kSlotsPerWave; ++p) {
+    const bool ok = tok[p] >= 0;
+    const int64_t row_off = ok ? a.map.row<kPow2>((uint32_t)(s0 + p)) * kPitch : 0;
+    const __amdgpu_buffer_rsrc_t rs = buffer_at(a.cache + row_off, ok ? (uint32_t)kPitch : 0u);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+      uint32_t sdw;
+      const uint32_t codes = quantize_slice(v[p][sub], sdw);
+      const uint32_t scale_off = (lane & 15) == 12 ? LATENT / 2 + sub * 16 + (lane >> 4) * 4 : kDrop;
+      // Rows go out in slot order, so plain stores let L2 merge neighbours.
+      __builtin_amdgcn_raw_buffer_store_b32(codes, rs, sub * 256 + lane * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, 0);
+    }
+  }
+}
+
+template <int LATENT>
+hipError_t launch_by_slot(const StoreArgs& a, const int32_t* inv, hipStream_t stream) {
+  constexpr int64_t kPerBlock = (int64_t)kWavesPerBlock * kSlotsPerWave;
+  const unsigned blocks = (unsigned)(((int64_t)a.map.num_slots + kPerBlock - 1) / kPerBlock);
+  if (a.map.pow2)
+    hipLaunchKernelGGL((mxfp4_store_by_slot_kernel<LATENT, true>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, a, inv);
+  else
+    hipLaunchKernelGGL((mxfp4_store_by_slot_kernel<LATENT, false>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, a, inv);
+  return hipGetLastError();
+}
+
 template <int LATENT>
 hipError_t launch_latent(const StoreArgs& a, hipStream_t stream) {
   constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
@@ -226,6 +323,26 @@ hipError_t launch_latent(const StoreArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_build_inverse(const int64_t* slots, int64_t num_tokens, uint32_t num_slots,
+                                int32_t* inverse, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_inverse, dim3((unsigned)(((int64_t)num_slots + 1023) / 1024)), dim3(256), 0,
+                     stream, inverse, (int64_t)num_slots);
+  if (num_tokens > 0)
+    hipLaunchKernelGGL(invert_slots, dim3((unsigned)((num_tokens + 255) / 256)), dim3(256), 0, stream,
+                       slots, num_tokens, inverse, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_store_by_slot(const StoreArgs& a, int latent, const int32_t* inverse,
+                                      hipStream_t stream) {
+  switch (latent) {
+    case 512: return launch_by_slot<512>(a, inverse, stream);
+    case 1024: return launch_by_slot<1024>(a, inverse, stream);
+    case 2048: return launch_by_slot<2048>(a, inverse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream) {
   switch (latent) {

@@ -109,6 +109,34 @@ int check_rope(const uint16_t* latent, const int64_t* positions, const float* co
   return MX_OK;
 }
 
+
+// Argument checks shared by mxfp4_store and mxfp4_store_by_slot; `index` is
+// the slot list or the inverse map (only checked for NULL here).  Returns
+// MX_OK with `a` filled (a->slots left unset), or an error status; *empty is
+// set for num_tokens == 0.
+int check_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                int64_t src_row_stride, const void* index, uint8_t* cache,
+                int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
+                int32_t group, mxs::StoreArgs* a, bool* empty) {
+  int rc = check_paged(latent, group, num_blocks, block_size, block_stride_rows, &a->map);
+  if (rc) return rc;
+  if (num_tokens < 0) return fail(MX_E_RANGE, "num_tokens must be >= 0");
+  if (src_row_stride < latent)
+    return fail(MX_E_STRIDE, "src_row_stride (%lld) is smaller than latent (%lld)",
+                (long long)src_row_stride, (long long)latent);
+  *empty = num_tokens == 0;
+  if (*empty) return MX_OK;
+  if (!src_bf16 || !index || !cache) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(src_bf16, 16) || src_row_stride % 8)
+    return fail(MX_E_ALIGN, "latent rows must be 16-byte aligned (base %% 16 == 0, row stride %% 8 == 0)");
+  if (!aligned(cache, 4)) return fail(MX_E_ALIGN, "cache must be 4-byte aligned");
+  a->src = src_bf16;
+  a->src_stride = src_row_stride;
+  a->num_tokens = num_tokens;
+  a->cache = cache;
+  return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,23 +151,62 @@ int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
                 int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
                 int32_t group, void* stream) {
   mxs::StoreArgs a{};
-  int rc = check_paged(latent, group, num_blocks, block_size, block_stride_rows, &a.map);
+  bool empty = false;
+  int rc = check_store(src_bf16, num_tokens, latent, src_row_stride, slot_mapping, cache,
+                       num_blocks, block_size, block_stride_rows, group, &a, &empty);
   if (rc) return rc;
-  if (num_tokens < 0) return fail(MX_E_RANGE, "num_tokens must be >= 0");
-  if (src_row_stride < latent)
-    return fail(MX_E_STRIDE, "src_row_stride (%lld) is smaller than latent (%lld)",
-                (long long)src_row_stride, (long long)latent);
-  if (num_tokens == 0) return ok();
-  if (!src_bf16 || !slot_mapping || !cache) return fail(MX_E_NULL, "null device pointer");
-  if (!aligned(src_bf16, 16) || src_row_stride % 8)
-    return fail(MX_E_ALIGN, "latent rows must be 16-byte aligned (base %% 16 == 0, row stride %% 8 == 0)");
-  if (!aligned(cache, 4)) return fail(MX_E_ALIGN, "cache must be 4-byte aligned");
-  a.src = src_bf16;
-  a.src_stride = src_row_stride;
+  if (empty) return ok();
   a.slots = slot_mapping;
-  a.num_tokens = num_tokens;
-  a.cache = cache;
   return launched(mxs::launch_mxfp4_store(a, (int)latent, (hipStream_t)stream), "mxfp4_store");
+}
+
+int64_t mxfp4_inverse_bytes(int64_t num_blocks, int64_t block_size) {
+  if (num_blocks < 1 || block_size < 1 || num_blocks > (int64_t(0xFFFFFFFF) / block_size))
+    return MX_E_RANGE;
+  return ((num_blocks * block_size * 4 + 15) / 16) * 16;
+}
+
+int mxfp4_slot_order_advised(int64_t num_tokens, int64_t latent, int64_t num_blocks,
+                             int64_t block_size) {
+  if (latent < 512 || latent > 2048 || !is_pow2(latent)) return 0;
+  if (mxfp4_inverse_bytes(num_blocks, block_size) < 0) return 0;
+  // The slot order pays for its inverse once a batch is large enough to
+  // stream from HBM and covers at least half of the slots.
+  const int64_t num_slots = num_blocks * block_size;
+  return num_tokens >= (int64_t(1) << 16) && num_tokens <= 0x7FFFFFFF && 2 * num_tokens >= num_slots;
+}
+
+int mxfp4_build_inverse(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                        int64_t block_size, int32_t* inverse, int64_t inverse_bytes, void* stream) {
+  const int64_t need = mxfp4_inverse_bytes(num_blocks, block_size);
+  if (need < 0) return fail(MX_E_RANGE, "num_blocks and block_size must be >= 1 with fewer than 2^32 slots");
+  if (num_tokens < 0 || num_tokens > 0x7FFFFFFF)
+    return fail(MX_E_RANGE, "num_tokens must be in [0, 2^31)");
+  if (inverse_bytes < need)
+    return fail(MX_E_RANGE, "inverse holds %lld bytes, needs %lld", (long long)inverse_bytes, (long long)need);
+  if (!inverse || (num_tokens > 0 && !slot_mapping)) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(inverse, 16)) return fail(MX_E_ALIGN, "inverse must be 16-byte aligned");
+  return launched(mxs::launch_build_inverse(slot_mapping, num_tokens,
+                                            (uint32_t)(num_blocks * block_size), inverse,
+                                            (hipStream_t)stream),
+                  "mxfp4_build_inverse");
+}
+
+int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                        int64_t src_row_stride, const int32_t* inverse, uint8_t* cache,
+                        int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
+                        int32_t group, void* stream) {
+  mxs::StoreArgs a{};
+  bool empty = false;
+  int rc = check_store(src_bf16, num_tokens, latent, src_row_stride, inverse, cache, num_blocks,
+                       block_size, block_stride_rows, group, &a, &empty);
+  if (rc) return rc;
+  if (latent < 512)
+    return fail(MX_E_SHAPE, "the slot-order store needs latent >= 512, got %lld", (long long)latent);
+  if (empty) return ok();
+  if (!aligned(inverse, 16)) return fail(MX_E_ALIGN, "inverse must be 16-byte aligned");
+  return launched(mxs::launch_mxfp4_store_by_slot(a, (int)latent, inverse, (hipStream_t)stream),
+                  "mxfp4_store_by_slot");
 }
 
 int mxfp4_gather_dequant(const uint8_t* cache, int64_t num_blocks, int64_t block_size,

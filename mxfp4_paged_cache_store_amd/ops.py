@@ -65,6 +65,54 @@ def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tens
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
 
 
+def mxfp4_inverse_bytes(num_blocks: int, block_size: int) -> int:
+    """``mxfp4_inverse_bytes`` of the C ABI."""
+    n = int(_abi.lib().mxfp4_inverse_bytes(num_blocks, block_size))
+    if n < 0:
+        raise ValueError("num_blocks and block_size must be >= 1 with fewer than 2^32 slots")
+    return n
+
+
+def mxfp4_slot_order_advised(num_tokens: int, latent: int, num_blocks: int, block_size: int) -> bool:
+    """``mxfp4_slot_order_advised`` of the C ABI."""
+    return bool(_abi.lib().mxfp4_slot_order_advised(num_tokens, latent, num_blocks, block_size))
+
+
+def mxfp4_build_inverse(slot_mapping: torch.Tensor, num_blocks: int, block_size: int,
+                        inverse: torch.Tensor, stream=None) -> torch.Tensor:
+    """``mxfp4_build_inverse`` of the C ABI; ``inverse`` is a device int32
+    tensor of at least num_blocks * block_size entries."""
+    _need_cuda(slot_mapping, inverse)
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    if inverse.dtype != torch.int32 or not inverse.is_contiguous():
+        raise ValueError("inverse must be a contiguous int32 tensor")
+    _abi.check(_abi.lib().mxfp4_build_inverse(
+        slot_mapping.data_ptr(), slot_mapping.numel(), num_blocks, block_size,
+        inverse.data_ptr(), inverse.numel() * 4, _stream(stream)))
+    return inverse
+
+
+def mxfp4_store_by_slot(src: torch.Tensor, num_tokens: int, inverse: torch.Tensor,
+                        cache: torch.Tensor, num_blocks: int, block_size: int,
+                        block_stride_rows: int, group: int = GROUP_SIZE, stream=None) -> None:
+    """``mxfp4_store_by_slot`` of the C ABI: the store in slot order, from the
+    inverse map of the batch's slot mapping."""
+    _need_cuda(src, inverse, cache)
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
+    if inverse.dtype != torch.int32 or not inverse.is_contiguous() \
+            or inverse.numel() < num_blocks * block_size:
+        raise ValueError("inverse must be a contiguous int32 tensor with one entry per slot")
+    if cache.dtype != torch.uint8:
+        raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
+    if num_tokens > src.shape[0]:
+        raise ValueError("num_tokens exceeds the rows of src")
+    _abi.check(_abi.lib().mxfp4_store_by_slot(
+        src.data_ptr(), num_tokens, src.shape[1], src.stride(0), inverse.data_ptr(),
+        cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
+
+
 def mxfp4_gather_dequant(cache: torch.Tensor, num_blocks: int, block_size: int,
                          block_stride_rows: int, latent: int, slots: torch.Tensor,
                          out: torch.Tensor, group: int = GROUP_SIZE, stream=None) -> torch.Tensor:
@@ -144,17 +192,28 @@ def resolve_paged_view(cache: torch.Tensor, latent: int, group: int = GROUP_SIZE
 
 
 def store_mxfp4_mla(kv_c_normed: torch.Tensor, slot_mapping: torch.Tensor,
-                    cache: torch.Tensor, group: int = GROUP_SIZE, stream=None) -> None:
+                    cache: torch.Tensor, group: int = GROUP_SIZE, stream=None,
+                    inverse: torch.Tensor | None = None) -> None:
     """Quantize the MLA latent to MXFP4 and write it into the paged cache
     [P1 `store_mxfp4_mla`]: same arguments and view resolution as the page's
-    wrapper; the work is one ``mxfp4_store`` launch."""
+    wrapper.  The work is one ``mxfp4_store`` launch; when an int32
+    ``inverse`` buffer is given and the library advises the slot-order form
+    for this shape, it is ``mxfp4_build_inverse`` + ``mxfp4_store_by_slot``
+    instead (same bytes)."""
     if kv_c_normed.dim() != 2:
         raise ValueError(f"expected kv_c_normed=[tokens, latent], got {tuple(kv_c_normed.shape)}")
     num_blocks, block_size, stride_rows = resolve_paged_view(cache, kv_c_normed.shape[1], group)
-    if slot_mapping.numel() == 0:
+    num_tokens = slot_mapping.numel()
+    if num_tokens == 0:
         return
-    mxfp4_store(kv_c_normed, slot_mapping, cache, num_blocks, block_size, stride_rows,
-                group, stream)
+    if inverse is not None and mxfp4_slot_order_advised(num_tokens, kv_c_normed.shape[1],
+                                                        num_blocks, block_size):
+        mxfp4_build_inverse(slot_mapping, num_blocks, block_size, inverse, stream)
+        mxfp4_store_by_slot(kv_c_normed, num_tokens, inverse, cache, num_blocks, block_size,
+                            stride_rows, group, stream)
+    else:
+        mxfp4_store(kv_c_normed, slot_mapping, cache, num_blocks, block_size, stride_rows,
+                    group, stream)
 
 
 def rope_quant_insert(latent, positions, cos_sin_cache, kv_cache, slot_mapping,

@@ -134,3 +134,60 @@ def test_rope_empty_is_a_noop(mxlib, fn):
 def test_nvfp4_record_width_checked(mxlib):
     # a 288-byte page stride is too small for the 528-byte record
     assert rope(mxlib, "mxfp8_rope_store", pstride=64 * 288) == _abi.MX_E_STRIDE
+
+
+def test_inverse_bytes_and_advice(mxlib):
+    assert mxlib.mxfp4_inverse_bytes(1, 4_500_000) == 18_000_000
+    assert mxlib.mxfp4_inverse_bytes(1000, 150) == 600_000
+    assert mxlib.mxfp4_inverse_bytes(3, 3) == 48           # 36 rounded up to 16
+    assert mxlib.mxfp4_inverse_bytes(0, 5) == _abi.MX_E_RANGE
+    assert mxlib.mxfp4_inverse_bytes(1 << 30, 64) == _abi.MX_E_RANGE
+    adv = mxlib.mxfp4_slot_order_advised
+    assert adv(4_500_000, 512, 1, 4_500_000) == 1
+    assert adv(100_000, 1024, 1000, 150) == 1 and adv(100_000, 2048, 1000, 150) == 1
+    assert adv(16_384, 512, 8192, 64) == 0      # sparse prefill: scatter
+    assert adv(65_535, 512, 1, 65_535) == 0     # small batch: scatter
+    assert adv(100_000, 256, 1, 100_000) == 0   # latent below 512
+    assert adv(100_000, 512, 1, 200_001) == 0   # under half of the slots
+
+
+def build_inverse(mxlib, **kw):
+    a = dict(slots=FAKE, n=10, nb=2, bs=8, inv=FAKE, nbytes=64)
+    a.update(kw)
+    return mxlib.mxfp4_build_inverse(a["slots"], a["n"], a["nb"], a["bs"], a["inv"], a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nbytes=60), _abi.MX_E_RANGE),
+    (dict(n=-1), _abi.MX_E_RANGE),
+    (dict(n=1 << 31), _abi.MX_E_RANGE),
+    (dict(nb=0), _abi.MX_E_RANGE),
+    (dict(inv=0), _abi.MX_E_NULL),
+    (dict(slots=0), _abi.MX_E_NULL),
+    (dict(inv=FAKE + 4), _abi.MX_E_ALIGN),
+])
+def test_build_inverse_rejects(mxlib, kw, status):
+    assert build_inverse(mxlib, **kw) == status
+
+
+def store_by_slot(mxlib, **kw):
+    a = dict(src=FAKE, n=4, latent=512, stride=512, inv=FAKE, cache=FAKE, nb=1, bs=8, bsr=8, group=32)
+    a.update(kw)
+    return mxlib.mxfp4_store_by_slot(a["src"], a["n"], a["latent"], a["stride"], a["inv"], a["cache"],
+                                     a["nb"], a["bs"], a["bsr"], a["group"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(latent=256, stride=256), _abi.MX_E_SHAPE),
+    (dict(group=16), _abi.MX_E_SHAPE),
+    (dict(inv=0), _abi.MX_E_NULL),
+    (dict(inv=FAKE + 8), _abi.MX_E_ALIGN),
+    (dict(bsr=4), _abi.MX_E_STRIDE),
+    (dict(n=-3), _abi.MX_E_RANGE),
+])
+def test_store_by_slot_rejects(mxlib, kw, status):
+    assert store_by_slot(mxlib, **kw) == status
+
+
+def test_store_by_slot_empty_is_a_noop(mxlib):
+    assert store_by_slot(mxlib, n=0, src=0, inv=0, cache=0) == _abi.MX_OK

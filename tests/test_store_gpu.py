@@ -188,24 +188,102 @@ def test_page_api_views(device):
 
 def test_large_int64_addressing(device):
     """4.5M tokens x 512 (2.3e9 values, past 2^31), random-permutation slots
-    into a flat 1.224 GB cache, compared byte for byte with the oracle; run
-    in the launch configuration the benchmark times."""
+    into a flat 1.224 GB cache, in both the scatter form and the slot-order
+    form (the one the benchmark times), each compared byte for byte with the
+    oracle."""
     n = workloads.LARGE_TOKENS
     log(f"store large: {n} tokens (generating on device)")
     src, slots = workloads.large_case_device(n)
     cache = torch.full((n * 272,), 0xA5, dtype=torch.uint8, device=device)
     ops.mxfp4_store(src, slots, cache, 1, n, n)
     torch.cuda.synchronize()
+    got_scatter = cache.cpu().numpy()
+    assert ops.mxfp4_slot_order_advised(n, 512, 1, n)
+    inv = torch.empty(n, dtype=torch.int32, device=device)
+    cache.fill_(0xA5)
+    log("store large: slot-order form")
+    ops.mxfp4_build_inverse(slots, 1, n, inv)
+    ops.mxfp4_store_by_slot(src, n, inv, cache, 1, n, n)
+    torch.cuda.synchronize()
+    got_slot_order = cache.cpu().numpy()
+    del cache, inv
     log("store large: copying back and running the oracle")
-    got = cache.cpu().numpy()
-    del cache
     src_host = src.view(torch.int16).cpu().numpy().view(np.uint16)
     slots_host = slots.cpu().numpy()
     del src, slots
     torch.cuda.empty_cache()
     want = np.full(n * 272, 0xA5, dtype=np.uint8)
     oracle.mxfp4_store(src_host, slots_host, want, 1, n, n, threads=oracle_threads())
-    assert (got == want).all(), first_mismatch(got, want, 272)
+    assert (got_scatter == want).all(), first_mismatch(got_scatter, want, 272)
+    assert (got_slot_order == want).all(), first_mismatch(got_slot_order, want, 272)
     # tokens past 2^31 / 512 really were written (the permutation covers every slot)
     tail = slots_host[(1 << 31) // 512:]
-    assert not (got.reshape(n, 272)[tail[:1000]] == 0xA5).all(axis=1).any()
+    assert not (want.reshape(n, 272)[tail[:1000]] == 0xA5).all(axis=1).any()
+
+
+@pytest.mark.parametrize("latent,nb,bs,stride,ntok", [
+    (512, 1000, 150, 200, 100_000),    # non-power-of-two block, interleaved blocks
+    (512, 4096, 64, 64, 200_000),      # contiguous power-of-two blocks
+    (512, 2048, 64, 96, 131_072),      # power-of-two block, interleaved
+    (1024, 800, 128, 128, 70_000),
+])
+def test_slot_order_form(device, latent, nb, bs, stride, ntok):
+    """build_inverse + store_by_slot over dense scattered batches (with pads
+    and out-of-range slots) writes the same bytes as the oracle; one inverse
+    serves two layers that share the slot mapping."""
+    rng = np.random.default_rng(ntok + latent)
+    num_slots = nb * bs
+    assert ops.mxfp4_slot_order_advised(ntok, latent, nb, bs)
+    slots = rng.choice(num_slots, ntok, replace=False).astype(np.int64)
+    slots[rng.random(ntok) < 0.03] = -1
+    slots[:5] = [num_slots, num_slots + 7, 10**13, -2, -(2**40)]
+    pitch = latent // 2 + latent // 32
+    inv = torch.empty(ops.mxfp4_inverse_bytes(nb, bs) // 4, dtype=torch.int32, device=device)
+    log(f"store slot order latent={latent} nb={nb} bs={bs} stride={stride} ntok={ntok}")
+    ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
+    for layer in range(2):
+        x = rng.standard_normal((ntok, latent)) * np.exp2(rng.uniform(-12, 12, size=(ntok, 1)))
+        src = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        host = np.full(((nb - 1) * stride + bs) * pitch, 0xA5, dtype=np.uint8)
+        dev_cache = u8_dev(host, device)
+        ops.mxfp4_store_by_slot(bf16_dev(src, device), ntok, inv, dev_cache, nb, bs, stride)
+        torch.cuda.synchronize()
+        got = dev_cache.cpu().numpy()
+        oracle.mxfp4_store(src, slots, host, nb, bs, stride, threads=oracle_threads())
+        assert (got == host).all(), (layer, first_mismatch(got, host, pitch))
+
+
+def test_page_api_with_inverse(device):
+    """store_mxfp4_mla with an inverse buffer: slot order for a dense batch,
+    the scatter form for a sparse one; both match the oracle."""
+    rng = np.random.default_rng(22)
+    for ntok, nslots in ((1 << 17, 1 << 17), (70_000, 1 << 20)):
+        src = (rng.standard_normal((ntok, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        slots = rng.choice(nslots, ntok, replace=False).astype(np.int64)
+        inv = torch.empty(nslots, dtype=torch.int32, device=device)
+        cache = torch.full((nslots * 272,), 0xA5, dtype=torch.uint8, device=device)
+        log(f"store page API with inverse: {ntok} tokens, {nslots} slots")
+        ops.store_mxfp4_mla(bf16_dev(src, device), i64_dev(slots, device), cache, inverse=inv)
+        torch.cuda.synchronize()
+        host = np.full(nslots * 272, 0xA5, dtype=np.uint8)
+        oracle.mxfp4_store(src, slots, host, 1, nslots, nslots, threads=oracle_threads())
+        assert (cache.cpu().numpy() == host).all()
+
+
+def test_inverse_map_contents(device):
+    """The inverse map itself: -1 everywhere except at the batch's valid
+    slots, which hold their token index."""
+    rng = np.random.default_rng(23)
+    nb, bs, n = 37, 33, 900
+    slots = rng.choice(nb * bs, n, replace=False).astype(np.int64)
+    slots[::17] = -1
+    slots[5] = nb * bs
+    inv = torch.full((nb * bs + 4,), 12345, dtype=torch.int32, device=device)
+    ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
+    torch.cuda.synchronize()
+    want = np.full(nb * bs, -1, dtype=np.int32)
+    ok = (slots >= 0) & (slots < nb * bs)
+    want[slots[ok]] = np.flatnonzero(ok)
+    got = inv.cpu().numpy()
+    assert (got[: nb * bs] == want).all()
+    assert (got[nb * bs:] == 12345).all()  # nothing past the map
