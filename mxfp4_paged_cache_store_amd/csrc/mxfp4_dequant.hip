@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_dequant_kernel(c
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tok_in_pass = lane / kLanesPerTok;
   const int lane_in_tok = lane % kLanesPerTok;
-  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kToks;
+  const int64_t wave_first = ((int64_t)xcd_contiguous_block() * kWavesPerBlock + wave) * kToks;
 
   uint32_t codes[kSlotsPerWave][kSub];
   uint32_t sdw[kSlotsPerWave][kSub];

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tok_in_pass = lane / kLanesPerTok;
   const int lane_in_tok = lane % kLanesPerTok;
-  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kToks;
+  const int64_t wave_first = ((int64_t)xcd_contiguous_block() * kWavesPerBlock + wave) * kToks;
 
   // Slots of the wave's tokens: one merged load when the wave is whole.
   int64_t slot[kTokensPerWave];
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_ke
   constexpr int64_t kPitch = LATENT / 2 + LATENT / 32;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t s0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kSlotsPerWave;
+  const int64_t s0 = ((int64_t)xcd_contiguous_block() * kWavesPerBlock + wave) * kSlotsPerWave;
   const int64_t num_slots = a.map.num_slots;
 
   int32_t tok[kSlotsPerWave];

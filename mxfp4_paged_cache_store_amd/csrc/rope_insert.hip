@@ -35,7 +35,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTokensPerWave = 4;
+constexpr int kTokensPerWave = 1;  // measured: more waves beat a per-wave token loop
 constexpr int kWavesPerBlock = 4;
 
 // Gate + rotation for one token.  Returns false (uniformly) when the token is
