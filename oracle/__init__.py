@@ -8,6 +8,9 @@ the HIP library (``mxfp4_paged_cache_store_amd``) and never imports it.
 The arithmetic lives in ``mxoracle.c`` (plain scalar C, built with gcc
 ``-O2 -ffp-contract=off``, no fast-math); this module only builds it and
 marshals numpy arrays.  Each C function cites the page section it follows.
+``Oracle(path)`` binds one build; the module-level functions use the build of
+``mxoracle.c`` itself (the tests also bind deliberately broken builds to show
+that the pins catch them).
 """
 
 from __future__ import annotations
@@ -20,11 +23,11 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "mxoracle.c")
+SRC = os.path.join(_HERE, "mxoracle.c")
 _BUILD_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD_DIR, "libmxoracle.so")
 
-_lib = None
+_default = None
 _lock = threading.Lock()
 
 _i64 = ctypes.c_int64
@@ -32,55 +35,45 @@ _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
 
 
-def build() -> str:
-    """Compile mxoracle.c into oracle/_build/libmxoracle.so (always rebuilds)."""
-    os.makedirs(_BUILD_DIR, exist_ok=True)
-    tmp = _LIB_PATH + ".tmp"
+def build(src: str = SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle C source into a shared library (always rebuilds)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
     cmd = [
         "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
-        "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm",
+        "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm",
     ]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
-def _load():
-    global _lib
-    with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(_LIB_PATH) or (
-            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
-        ):
-            build()
-        lib = ctypes.CDLL(_LIB_PATH)
-        lib.orc_row_bytes.restype = _i64
-        lib.orc_row_bytes.argtypes = [_i64, _i32]
-        lib.orc_ceil_pow2_exponent.restype = ctypes.c_int
-        lib.orc_ceil_pow2_exponent.argtypes = [ctypes.c_float]
-        lib.orc_e2m1_code.restype = ctypes.c_int
-        lib.orc_e2m1_code.argtypes = [ctypes.c_float]
-        lib.orc_e4m3_encode.restype = ctypes.c_uint8
-        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
-        lib.orc_e4m3_value.restype = ctypes.c_double
-        lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
-        lib.orc_e4m3_encode_array.restype = None
-        lib.orc_e4m3_encode_array.argtypes = [_vp, _i64, _vp]
-        lib.orc_mxfp4_dequant_bf16.restype = ctypes.c_uint16
-        lib.orc_mxfp4_dequant_bf16.argtypes = [ctypes.c_int, ctypes.c_int]
-        lib.orc_mxfp4_quantize_row.restype = None
-        lib.orc_mxfp4_quantize_row.argtypes = [_vp, _i64, _vp]
-        lib.orc_mxfp4_store.restype = ctypes.c_int
-        lib.orc_mxfp4_store.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64]
-        lib.orc_mxfp4_gather_dequant.restype = ctypes.c_int
-        lib.orc_mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
-        for name in ("orc_mxfp8_rope_store", "orc_nvfp4_rope_store"):
-            fn = getattr(lib, name)
-            fn.restype = ctypes.c_int
-            fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
-        _lib = lib
-        return lib
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    lib.orc_row_bytes.restype = _i64
+    lib.orc_row_bytes.argtypes = [_i64, _i32]
+    lib.orc_ceil_pow2_exponent.restype = ctypes.c_int
+    lib.orc_ceil_pow2_exponent.argtypes = [ctypes.c_float]
+    lib.orc_e2m1_code.restype = ctypes.c_int
+    lib.orc_e2m1_code.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_encode_array.restype = None
+    lib.orc_e4m3_encode_array.argtypes = [_vp, _i64, _vp]
+    lib.orc_mxfp4_dequant_bf16.restype = ctypes.c_uint16
+    lib.orc_mxfp4_dequant_bf16.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.orc_mxfp4_quantize_row.restype = None
+    lib.orc_mxfp4_quantize_row.argtypes = [_vp, _i64, _vp]
+    lib.orc_mxfp4_store.restype = ctypes.c_int
+    lib.orc_mxfp4_store.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64]
+    lib.orc_mxfp4_gather_dequant.restype = ctypes.c_int
+    lib.orc_mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
+    for name in ("orc_mxfp8_rope_store", "orc_nvfp4_rope_store"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
+    return lib
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -90,133 +83,6 @@ def _ptr(a: np.ndarray) -> int:
 def _check(rc: int, what: str) -> None:
     if rc != 0:
         raise ValueError(f"oracle {what}: arguments outside the contract (rc={rc})")
-
-
-# ---------------------------------------------------------------- scalars
-
-def row_bytes(latent: int, group: int = 32) -> int:
-    return int(_load().orc_row_bytes(latent, group))
-
-
-def ceil_pow2_exponent(v: float) -> int:
-    return int(_load().orc_ceil_pow2_exponent(v))
-
-
-def e2m1_code(q: float) -> int:
-    return int(_load().orc_e2m1_code(q))
-
-
-def e4m3_encode(v: float) -> int:
-    return int(_load().orc_e4m3_encode(v))
-
-
-def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
-    v = np.ascontiguousarray(v, dtype=np.float32)
-    out = np.empty(v.shape, dtype=np.uint8)
-    _load().orc_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
-    return out
-
-
-def e4m3_value(b: int) -> float:
-    return float(_load().orc_e4m3_value(b))
-
-
-def dequant_bf16(code: int, scale_byte: int) -> int:
-    return int(_load().orc_mxfp4_dequant_bf16(code, scale_byte))
-
-
-# ---------------------------------------------------------------- arrays
-
-def quantize_row(x_bf16_bits: np.ndarray) -> np.ndarray:
-    """One latent row (uint16 bf16 bits) -> packed row bytes (uint8)."""
-    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
-    out = np.zeros(row_bytes(x.size), dtype=np.uint8)
-    _load().orc_mxfp4_quantize_row(_ptr(x), x.size, _ptr(out))
-    return out
-
-
-def mxfp4_store(src: np.ndarray, slot_mapping: np.ndarray, cache: np.ndarray,
-                num_blocks: int, block_size: int, block_stride_rows: int,
-                threads: int = 1) -> None:
-    """Store rows of ``src`` (uint16 [T, latent] bf16 bits) into ``cache``.
-
-    ``src`` may be a row-strided view (unit inner stride).  ``cache`` is the
-    flat uint8 buffer holding the paged layer view; it is modified in place.
-    ``threads > 1`` splits the tokens into contiguous ranges run concurrently
-    (distinct slots never share bytes).
-    """
-    assert src.dtype == np.uint16 and src.ndim == 2 and src.strides[1] == 2
-    assert slot_mapping.dtype == np.int64 and cache.dtype == np.uint8
-    assert cache.flags.c_contiguous and slot_mapping.flags.c_contiguous
-    num_tokens = slot_mapping.size
-    latent = src.shape[1]
-    src_row_stride = src.strides[0] // 2
-    need = ((num_blocks - 1) * block_stride_rows + block_size) * row_bytes(latent)
-    assert cache.size >= need, "cache buffer smaller than the paged view"
-    assert src.shape[0] >= num_tokens
-    lib = _load()
-    base = src.__array_interface__["data"][0]
-
-    def run(lo: int, hi: int) -> None:
-        rc = lib.orc_mxfp4_store(
-            base + lo * src_row_stride * 2, hi - lo, latent, src_row_stride,
-            slot_mapping.ctypes.data + lo * 8, _ptr(cache),
-            num_blocks, block_size, block_stride_rows)
-        _check(rc, "mxfp4_store")
-
-    _run_chunks(run, num_tokens, threads)
-
-
-def mxfp4_gather_dequant(cache: np.ndarray, num_blocks: int, block_size: int,
-                         block_stride_rows: int, latent: int, slots: np.ndarray,
-                         out: np.ndarray | None = None) -> np.ndarray:
-    """Dequantize the rows of ``slots`` to bf16 bits, uint16 [n, latent]."""
-    assert slots.dtype == np.int64 and slots.flags.c_contiguous
-    n = slots.size
-    if out is None:
-        out = np.zeros((n, latent), dtype=np.uint16)
-    assert out.dtype == np.uint16 and out.flags.c_contiguous and out.shape[0] >= n
-    rc = _load().orc_mxfp4_gather_dequant(
-        _ptr(cache), num_blocks, block_size, block_stride_rows, latent,
-        _ptr(slots), n, _ptr(out), out.shape[1])
-    _check(rc, "mxfp4_gather_dequant")
-    return out
-
-
-def _rope_store(fn_name: str, latent: np.ndarray, positions: np.ndarray,
-                cos_sin: np.ndarray, cache: np.ndarray, block: int,
-                num_blocks: int, cache_block_stride: int,
-                slot_mapping: np.ndarray, compress_ratio: int,
-                sanitize: bool) -> None:
-    assert latent.dtype == np.uint16 and latent.flags.c_contiguous
-    assert latent.shape[1] == 512
-    assert positions.dtype == np.int64 and slot_mapping.dtype == np.int64
-    assert cos_sin.dtype == np.float32 and cos_sin.strides[1] == 4
-    assert cache.dtype == np.uint8 and cache.flags.c_contiguous
-    n = slot_mapping.size
-    assert n <= min(latent.shape[0], positions.size)
-    rc = getattr(_load(), fn_name)(
-        _ptr(latent), _ptr(positions), cos_sin.ctypes.data,
-        cos_sin.strides[0] // 4, cos_sin.shape[0], _ptr(cache),
-        cache_block_stride, block, num_blocks, _ptr(slot_mapping), n,
-        compress_ratio, int(bool(sanitize)))
-    _check(rc, fn_name)
-
-
-def mxfp8_rope_store(latent, positions, cos_sin, cache, block, num_blocks,
-                     slot_mapping, compress_ratio, sanitize=True,
-                     cache_block_stride=None) -> None:
-    stride = block * 528 if cache_block_stride is None else cache_block_stride
-    _rope_store("orc_mxfp8_rope_store", latent, positions, cos_sin, cache, block,
-                num_blocks, stride, slot_mapping, compress_ratio, sanitize)
-
-
-def nvfp4_rope_store(latent, positions, cos_sin, cache, block, num_blocks,
-                     slot_mapping, compress_ratio, sanitize=True,
-                     cache_block_stride=None) -> None:
-    stride = block * 288 if cache_block_stride is None else cache_block_stride
-    _rope_store("orc_nvfp4_rope_store", latent, positions, cos_sin, cache, block,
-                num_blocks, stride, slot_mapping, compress_ratio, sanitize)
 
 
 def _run_chunks(run, n: int, threads: int) -> None:
@@ -230,3 +96,156 @@ def _run_chunks(run, n: int, threads: int) -> None:
         w.start()
     for w in workers:
         w.join()
+
+
+class Oracle:
+    """The oracle's functions over one build of the C source (numpy in/out)."""
+
+    def __init__(self, lib_path: str):
+        self.lib = _bind(ctypes.CDLL(lib_path))
+
+    # ------------------------------------------------------------ scalars
+
+    def row_bytes(self, latent: int, group: int = 32) -> int:
+        return int(self.lib.orc_row_bytes(latent, group))
+
+    def ceil_pow2_exponent(self, v: float) -> int:
+        return int(self.lib.orc_ceil_pow2_exponent(v))
+
+    def e2m1_code(self, q: float) -> int:
+        return int(self.lib.orc_e2m1_code(q))
+
+    def e4m3_encode(self, v: float) -> int:
+        return int(self.lib.orc_e4m3_encode(v))
+
+    def e4m3_encode_array(self, v: np.ndarray) -> np.ndarray:
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        out = np.empty(v.shape, dtype=np.uint8)
+        self.lib.orc_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+        return out
+
+    def e4m3_value(self, b: int) -> float:
+        return float(self.lib.orc_e4m3_value(b))
+
+    def dequant_bf16(self, code: int, scale_byte: int) -> int:
+        return int(self.lib.orc_mxfp4_dequant_bf16(code, scale_byte))
+
+    # ------------------------------------------------------------ arrays
+
+    def quantize_row(self, x_bf16_bits: np.ndarray) -> np.ndarray:
+        """One latent row (uint16 bf16 bits) -> packed row bytes (uint8)."""
+        x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+        out = np.zeros(self.row_bytes(x.size), dtype=np.uint8)
+        self.lib.orc_mxfp4_quantize_row(_ptr(x), x.size, _ptr(out))
+        return out
+
+    def mxfp4_store(self, src: np.ndarray, slot_mapping: np.ndarray, cache: np.ndarray,
+                    num_blocks: int, block_size: int, block_stride_rows: int,
+                    threads: int = 1) -> None:
+        """Store rows of ``src`` (uint16 [T, latent] bf16 bits) into ``cache``.
+
+        ``src`` may be a row-strided view (unit inner stride).  ``cache`` is
+        the flat uint8 buffer holding the paged layer view; it is modified in
+        place.  ``threads > 1`` splits the tokens into contiguous ranges run
+        concurrently (distinct slots never share bytes).
+        """
+        assert src.dtype == np.uint16 and src.ndim == 2 and src.strides[1] == 2
+        assert slot_mapping.dtype == np.int64 and cache.dtype == np.uint8
+        assert cache.flags.c_contiguous and slot_mapping.flags.c_contiguous
+        num_tokens = slot_mapping.size
+        latent = src.shape[1]
+        src_row_stride = src.strides[0] // 2
+        need = ((num_blocks - 1) * block_stride_rows + block_size) * self.row_bytes(latent)
+        assert cache.size >= need, "cache buffer smaller than the paged view"
+        assert src.shape[0] >= num_tokens
+        lib = self.lib
+        base = src.__array_interface__["data"][0]
+
+        def run(lo: int, hi: int) -> None:
+            rc = lib.orc_mxfp4_store(
+                base + lo * src_row_stride * 2, hi - lo, latent, src_row_stride,
+                slot_mapping.ctypes.data + lo * 8, _ptr(cache),
+                num_blocks, block_size, block_stride_rows)
+            _check(rc, "mxfp4_store")
+
+        _run_chunks(run, num_tokens, threads)
+
+    def mxfp4_gather_dequant(self, cache: np.ndarray, num_blocks: int, block_size: int,
+                             block_stride_rows: int, latent: int, slots: np.ndarray,
+                             out: np.ndarray | None = None) -> np.ndarray:
+        """Dequantize the rows of ``slots`` to bf16 bits, uint16 [n, latent]."""
+        assert slots.dtype == np.int64 and slots.flags.c_contiguous
+        n = slots.size
+        if out is None:
+            out = np.zeros((n, latent), dtype=np.uint16)
+        assert out.dtype == np.uint16 and out.flags.c_contiguous and out.shape[0] >= n
+        rc = self.lib.orc_mxfp4_gather_dequant(
+            _ptr(cache), num_blocks, block_size, block_stride_rows, latent,
+            _ptr(slots), n, _ptr(out), out.shape[1])
+        _check(rc, "mxfp4_gather_dequant")
+        return out
+
+    def _rope_store(self, fn_name, latent, positions, cos_sin, cache, block, num_blocks,
+                    cache_block_stride, slot_mapping, compress_ratio, sanitize) -> None:
+        assert latent.dtype == np.uint16 and latent.flags.c_contiguous
+        assert latent.shape[1] == 512
+        assert positions.dtype == np.int64 and slot_mapping.dtype == np.int64
+        assert cos_sin.dtype == np.float32 and cos_sin.strides[1] == 4
+        assert cache.dtype == np.uint8 and cache.flags.c_contiguous
+        n = slot_mapping.size
+        assert n <= min(latent.shape[0], positions.size)
+        rc = getattr(self.lib, fn_name)(
+            _ptr(latent), _ptr(positions), cos_sin.ctypes.data,
+            cos_sin.strides[0] // 4, cos_sin.shape[0], _ptr(cache),
+            cache_block_stride, block, num_blocks, _ptr(slot_mapping), n,
+            compress_ratio, int(bool(sanitize)))
+        _check(rc, fn_name)
+
+    def mxfp8_rope_store(self, latent, positions, cos_sin, cache, block, num_blocks,
+                         slot_mapping, compress_ratio, sanitize=True,
+                         cache_block_stride=None) -> None:
+        stride = block * 528 if cache_block_stride is None else cache_block_stride
+        self._rope_store("orc_mxfp8_rope_store", latent, positions, cos_sin, cache, block,
+                         num_blocks, stride, slot_mapping, compress_ratio, sanitize)
+
+    def nvfp4_rope_store(self, latent, positions, cos_sin, cache, block, num_blocks,
+                         slot_mapping, compress_ratio, sanitize=True,
+                         cache_block_stride=None) -> None:
+        stride = block * 288 if cache_block_stride is None else cache_block_stride
+        self._rope_store("orc_nvfp4_rope_store", latent, positions, cos_sin, cache, block,
+                         num_blocks, stride, slot_mapping, compress_ratio, sanitize)
+
+
+def default() -> Oracle:
+    """The oracle built from oracle/mxoracle.c (built on first use)."""
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(SRC)
+            ):
+                build()
+            _default = Oracle(_LIB_PATH)
+        return _default
+
+
+def _forward(name):
+    def fn(*args, **kwargs):
+        return getattr(default(), name)(*args, **kwargs)
+    fn.__name__ = name
+    fn.__doc__ = getattr(Oracle, name).__doc__
+    return fn
+
+
+row_bytes = _forward("row_bytes")
+ceil_pow2_exponent = _forward("ceil_pow2_exponent")
+e2m1_code = _forward("e2m1_code")
+e4m3_encode = _forward("e4m3_encode")
+e4m3_encode_array = _forward("e4m3_encode_array")
+e4m3_value = _forward("e4m3_value")
+dequant_bf16 = _forward("dequant_bf16")
+quantize_row = _forward("quantize_row")
+mxfp4_store = _forward("mxfp4_store")
+mxfp4_gather_dequant = _forward("mxfp4_gather_dequant")
+mxfp8_rope_store = _forward("mxfp8_rope_store")
+nvfp4_rope_store = _forward("nvfp4_rope_store")

@@ -144,11 +144,12 @@ def test_inverse_bytes_and_advice(mxlib):
     assert mxlib.mxfp4_inverse_bytes(1 << 30, 64) == _abi.MX_E_RANGE
     adv = mxlib.mxfp4_slot_order_advised
     assert adv(4_500_000, 512, 1, 4_500_000) == 1
-    assert adv(100_000, 1024, 1000, 150) == 1 and adv(100_000, 2048, 1000, 150) == 1
+    assert adv(200_000, 1024, 1000, 300) == 1 and adv(200_000, 2048, 1000, 300) == 1
+    assert adv(1 << 17, 512, 1, 1 << 18) == 1
     assert adv(16_384, 512, 8192, 64) == 0      # sparse prefill: scatter
-    assert adv(65_535, 512, 1, 65_535) == 0     # small batch: scatter
-    assert adv(100_000, 256, 1, 100_000) == 0   # latent below 512
-    assert adv(100_000, 512, 1, 200_001) == 0   # under half of the slots
+    assert adv((1 << 17) - 1, 512, 1, 1 << 17) == 0  # small batch: scatter
+    assert adv(200_000, 256, 1, 200_000) == 0   # latent below 512
+    assert adv(200_000, 512, 1, 400_001) == 0   # under half of the slots
 
 
 def build_inverse(mxlib, **kw):

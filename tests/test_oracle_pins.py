@@ -53,10 +53,10 @@ def expected_scale_exponent(amax: Fraction) -> int:
     return max(ceil_log2(amax / 6), -126)
 
 
-def flat_store(src: np.ndarray) -> np.ndarray:
+def flat_store(src: np.ndarray, orc=oracle) -> np.ndarray:
     n = src.shape[0]
     cache = np.full(n * 272, 0xA5, dtype=np.uint8)
-    oracle.mxfp4_store(src, np.arange(n, dtype=np.int64), cache, 1, n, n)
+    orc.mxfp4_store(src, np.arange(n, dtype=np.int64), cache, 1, n, n)
     return cache.reshape(n, 272)
 
 
@@ -67,32 +67,36 @@ def nibble(rows: np.ndarray, token: int, elem: int) -> int:
 
 # ---------------------------------------------------------------- constants
 
-def test_format_constants():
-    assert oracle.row_bytes(512) == G["row_bytes_512"] == 512 // 2 + 512 // 32
+def test_format_constants(orc=oracle):
+    assert orc.row_bytes(512) == G["row_bytes_512"] == 512 // 2 + 512 // 32
     assert round(G["bf16_row_bytes_512"] / G["row_bytes_512"], 2) == float(G["capacity_ratio"])
-    assert oracle.row_bytes(128) == 68 and oracle.row_bytes(1024) == 544
-    assert oracle.row_bytes(100) < 0  # not a multiple of the group
+    assert orc.row_bytes(128) == 68 and orc.row_bytes(1024) == 544
+    assert orc.row_bytes(100) < 0  # not a multiple of the group
     # E2M1 grid: midpoints are exactly halfway between consecutive magnitudes.
     assert [float((GRID[i] + GRID[i + 1]) / 2) for i in range(7)] == MIDS
     assert float(GRID[-1]) == G["e2m1_max"]
     # E4M3 extremes used by the variants.
-    assert oracle.e4m3_value(0x7E) == G["e4m3_max"]
-    assert oracle.e4m3_value(0x01) == G["nvfp4_scale_min"]  # 2^-9: least subnormal
-    assert oracle.e4m3_value(0x08) == 2.0 ** -6              # least normal
+    assert orc.e4m3_value(0x7E) == G["e4m3_max"]
+    assert orc.e4m3_value(0x01) == G["nvfp4_scale_min"]  # 2^-9: least subnormal
+    assert orc.e4m3_value(0x08) == 2.0 ** -6              # least normal
 
 
 # ---------------------------------------------------------------- exponent + codes
 
-@pytest.fixture(scope="module")
-def solo_sweep():
+def make_solo_sweep(orc=oracle):
     """All 65,536 bf16 patterns, each alone in its group (rest +0)."""
     pats = np.arange(65536, dtype=np.uint32).reshape(4096, 16)
     src = np.zeros((4096, 512), dtype=np.uint16)
     src[:, ::32] = pats.astype(np.uint16)
-    return pats, flat_store(src)
+    return pats, flat_store(src, orc)
 
 
-def test_scale_exponent_exhaustive(solo_sweep):
+@pytest.fixture(scope="module")
+def solo_sweep():
+    return make_solo_sweep()
+
+
+def test_scale_exponent_exhaustive(solo_sweep, orc=oracle):
     pats, rows = solo_sweep
     for t in range(4096):
         for g in range(16):
@@ -107,7 +111,7 @@ def test_scale_exponent_exhaustive(solo_sweep):
                 assert got == expected_scale_exponent(abs(x)) + G["e8m0_bias"], hex(p)
 
 
-def test_bit_pattern_rule_agrees_with_definition():
+def test_bit_pattern_rule_agrees_with_definition(orc=oracle):
     """The store page computes the exponent on the fp32 bit pattern of
     amax/6; for every positive finite bf16 amax it equals the exact
     definition (floored at -126), so the reading of how amax/6 is formed
@@ -118,10 +122,10 @@ def test_bit_pattern_rule_agrees_with_definition():
         exp_field, mant = (bits >> 23) & 0xFF, bits & 0x7FFFFF
         rule = exp_field - 127 + (1 if mant else 0)
         assert rule == expected_scale_exponent(Fraction(float(a))), hex(p)
-        assert oracle.ceil_pow2_exponent(float(np.float32(a) / np.float32(6.0))) == rule
+        assert orc.ceil_pow2_exponent(float(np.float32(a) / np.float32(6.0))) == rule
 
 
-def test_solo_codes_exhaustive(solo_sweep):
+def test_solo_codes_exhaustive(solo_sweep, orc=oracle):
     pats, rows = solo_sweep
     for t in range(4096):
         for g in range(16):
@@ -141,7 +145,7 @@ def test_solo_codes_exhaustive(solo_sweep):
 
 
 @pytest.mark.parametrize("k", [0, 125, -126, 17, -100])
-def test_anchored_sweep(k):
+def test_anchored_sweep(k, orc=oracle):
     """Groups [6*2^k, x, ...] fix e = k; every finite bf16 x with
     |x| <= 6*2^k is swept (k = 125 reaches the fp32 underflow region of the
     quotient, k = -126 the subnormal inputs)."""
@@ -157,7 +161,7 @@ def test_anchored_sweep(k):
     flat[:ngroups, 0] = abits
     for i, p in enumerate(cands):
         flat[i // per, 1 + i % per] = p
-    rows = flat_store(src)
+    rows = flat_store(src, orc)
     for gi in range(ngroups):
         t, g = divmod(gi, 16)
         assert int(rows[t, 256 + g]) == k + 127
@@ -170,7 +174,7 @@ def test_anchored_sweep(k):
 
 
 @pytest.mark.parametrize("j", [-124, -60, -3, 0, 1, 7, 64, 126])
-def test_powers_of_two(j):
+def test_powers_of_two(j, orc=oracle):
     """A power-of-two amax costs no exponent step: amax = 2^j encodes as
     4.0 (code 6) with byte j-2+127; amax = 3*2^j as 6.0 (code 7) with byte
     j-1+127 (a log2-based ceiling would give byte +1 and code 5)."""
@@ -178,14 +182,14 @@ def test_powers_of_two(j):
     src[0, 0] = bf16_bits_of_fraction(TWO ** j)
     src[0, 32] = bf16_bits_of_fraction(-TWO ** j)
     src[0, 64] = bf16_bits_of_fraction(3 * TWO ** j)
-    rows = flat_store(src)
+    rows = flat_store(src, orc)
     assert rows[0, 256] == j - 2 + 127 and nibble(rows, 0, 0) == 6
     assert rows[0, 257] == j - 2 + 127 and nibble(rows, 0, 32) == 6 | 8
     assert rows[0, 258] == j - 1 + 127 and nibble(rows, 0, 64) == 7
 
 
 @pytest.mark.parametrize("k", [-120, -5, 0, 3, 100])
-def test_ties_to_even(k):
+def test_ties_to_even(k, orc=oracle):
     """Exact midpoints m*2^k (anchor 6*2^k) go to the even index of their
     two neighbours: indices 0, 2, 2, 4, 4, 6, 6 for the seven midpoints."""
     src = np.zeros((1, 512), dtype=np.uint16)
@@ -193,14 +197,14 @@ def test_ties_to_even(k):
     for i, m in enumerate(MIDS):
         src[0, 1 + i] = bf16_bits_of_fraction(Fraction(m) * TWO ** k)
         src[0, 9 + i] = bf16_bits_of_fraction(-Fraction(m) * TWO ** k)
-    rows = flat_store(src)
+    rows = flat_store(src, orc)
     expect = [0, 2, 2, 4, 4, 6, 6]
     for i in range(7):
         assert nibble(rows, 0, 1 + i) == expect[i]
         assert nibble(rows, 0, 9 + i) == expect[i] | 8
 
 
-def test_negative_zero_small_negatives_and_nibble_order():
+def test_negative_zero_small_negatives_and_nibble_order(orc=oracle):
     """bf16 -0.0 gives code 0; a small negative gives code 8 [P1
     `_quantize_e2m1`]; element 2i sits in the low nibble of byte i [P3
     Details]."""
@@ -209,26 +213,26 @@ def test_negative_zero_small_negatives_and_nibble_order():
     src[0, 1] = bf16_bits_of_fraction(Fraction(1, 2))  # code 1
     src[0, 2] = 0x8000                                 # -0.0 -> 0
     src[0, 3] = 0xBC24                                 # about -0.01 -> 8
-    rows = flat_store(src)
+    rows = flat_store(src, orc)
     assert rows[0, 0] == 0x17
     assert rows[0, 1] == 0x80
     assert rows[0, 256] == 127
 
 
-def test_all_zero_groups_and_nonfinite():
+def test_all_zero_groups_and_nonfinite(orc=oracle):
     src = np.zeros((1, 512), dtype=np.uint16)
     src[0, 32:64] = 0x8000           # all -0.0
     src[0, 64] = 0x7F80              # +Inf with finite neighbours
     src[0, 65] = 0x4000
     src[0, 96] = 0x7FC1              # NaN
-    rows = flat_store(src)
+    rows = flat_store(src, orc)
     assert rows[0, 256] == 127 and rows[0, 257] == 127
     assert (rows[0, 16:32] == 0).all()
     assert rows[0, 258] == 0xFF and (rows[0, 32:48] == 0).all()
     assert rows[0, 259] == 0xFF and (rows[0, 48:64] == 0).all()
 
 
-def test_invariants_on_random_rows():
+def test_invariants_on_random_rows(orc=oracle):
     """On varied random rows: decoded magnitude never exceeds 6, the scale is
     minimal (the amax element decodes to >= 3 times the scale unless the
     -126 floor applies), scale bytes lie in [1, 253], and the error is at most
@@ -240,7 +244,7 @@ def test_invariants_on_random_rows():
     bits = ((xf.view(np.uint32).astype(np.uint64) + 0x7FFF + ((xf.view(np.uint32) >> 16) & 1)) >> 16)
     src = bits.astype(np.uint16)
     src[(src & 0x7F80) == 0x7F80] = 0x3F80  # keep the rows finite
-    rows = flat_store(src)
+    rows = flat_store(src, orc)
     for t in range(64):
         for g in range(16):
             byte = int(rows[t, 256 + g])
@@ -265,7 +269,7 @@ def test_invariants_on_random_rows():
 
 # ---------------------------------------------------------------- layout
 
-def test_paged_addressing_pads_and_canaries():
+def test_paged_addressing_pads_and_canaries(orc=oracle):
     """Row of slot s at ((s // B) * stride_rows + s % B) * 272 [P1
     `store_mxfp4_mla`]; pads (-1) and slots past the last one write nothing;
     every byte outside written rows keeps its canary."""
@@ -274,37 +278,37 @@ def test_paged_addressing_pads_and_canaries():
     src = (rng.integers(0, 0x7F00, size=(12, 512)) | (rng.integers(0, 2, size=(12, 512)) << 15)).astype(np.uint16)
     slots = np.array([0, 7, 8, 15, 39, -1, 17, 40, 1000, 33, -5, 3], dtype=np.int64)
     cache = np.full(((nb - 1) * stride + bs) * 272, 0xA5, dtype=np.uint8)
-    oracle.mxfp4_store(src, slots, cache, nb, bs, stride)
+    orc.mxfp4_store(src, slots, cache, nb, bs, stride)
     touched = np.zeros(cache.size, dtype=bool)
     for t, s in enumerate(slots):
         if s < 0 or s >= nb * bs:
             continue
         off = ((s // bs) * stride + s % bs) * 272
-        assert (cache[off:off + 272] == oracle.quantize_row(src[t])).all()
+        assert (cache[off:off + 272] == orc.quantize_row(src[t])).all()
         touched[off:off + 272] = True
     assert (cache[~touched] == 0xA5).all()
 
 
-def test_strided_source_rows():
+def test_strided_source_rows(orc=oracle):
     """The latent may be a row-strided view (e.g. the first 512 columns of a
     [T, 576] tensor); only rows are strided."""
     rng = np.random.default_rng(4)
     wide = rng.integers(0, 0x7F00, size=(6, 576)).astype(np.uint16)
     view = wide[:, :512]
     cache = np.zeros(6 * 272, dtype=np.uint8)
-    oracle.mxfp4_store(view, np.arange(6, dtype=np.int64), cache, 1, 6, 6)
+    orc.mxfp4_store(view, np.arange(6, dtype=np.int64), cache, 1, 6, 6)
     for t in range(6):
-        assert (cache[t * 272:(t + 1) * 272] == oracle.quantize_row(np.ascontiguousarray(view[t]))).all()
+        assert (cache[t * 272:(t + 1) * 272] == orc.quantize_row(np.ascontiguousarray(view[t]))).all()
 
 
 # ---------------------------------------------------------------- dequant
 
-def test_dequant_table_exhaustive():
+def test_dequant_table_exhaustive(orc=oracle):
     """All 16 codes x 256 scale bytes against the exact product
     E2M1(code) * 2^(byte - 127) (+-Inf from 2^128, NaN for byte 0xFF)."""
     for b in range(256):
         for c in range(16):
-            got = oracle.dequant_bf16(c, b)
+            got = orc.dequant_bf16(c, b)
             if b == 0xFF:
                 assert got == 0x7FC0
                 continue
@@ -315,13 +319,13 @@ def test_dequant_table_exhaustive():
                 assert got == bf16_bits_of_fraction(v), (c, b)
 
 
-def test_round_trip_within_half_gap():
+def test_round_trip_within_half_gap(orc=oracle):
     rng = np.random.default_rng(5)
     src = (rng.standard_normal((16, 512)) * np.exp2(rng.uniform(-30, 30, (16, 1)))).astype(np.float32)
     bits = (src.view(np.uint32) >> 16).astype(np.uint16)  # truncation is fine for test data
-    rows = flat_store(bits)
+    rows = flat_store(bits, orc)
     cache = rows.reshape(-1).copy()
-    out = oracle.mxfp4_gather_dequant(cache, 1, 16, 16, 512, np.arange(16, dtype=np.int64))
+    out = orc.mxfp4_gather_dequant(cache, 1, 16, 16, 512, np.arange(16, dtype=np.int64))
     for t in range(16):
         for g in range(16):
             e = int(rows[t, 256 + g]) - 127
@@ -333,10 +337,10 @@ def test_round_trip_within_half_gap():
                 assert abs(x - d) <= gap / 2 * TWO ** e
 
 
-def test_dequant_skips_bad_slots():
+def test_dequant_skips_bad_slots(orc=oracle):
     cache = np.zeros(4 * 272, dtype=np.uint8)
     out = np.full((3, 512), 0x1234, dtype=np.uint16)
-    oracle.mxfp4_gather_dequant(cache, 1, 4, 4, 512, np.array([-1, 4, 2], dtype=np.int64), out)
+    orc.mxfp4_gather_dequant(cache, 1, 4, 4, 512, np.array([-1, 4, 2], dtype=np.int64), out)
     assert (out[0] == 0x1234).all() and (out[1] == 0x1234).all() and (out[2] == 0).all()
 
 
@@ -347,7 +351,7 @@ def _torch_e4m3(v: np.ndarray) -> np.ndarray:
         .view(torch.uint8).numpy()
 
 
-def test_e4m3_encode_matches_torch():
+def test_e4m3_encode_matches_torch(orc=oracle):
     """fp32 -> E4M3FN with round-to-nearest-even, subnormals and the sign of
     zero, against torch's float8_e4m3fn over every bf16 value in [-448, 448],
     every grid midpoint +-1 ulp, and random fp32 values."""
@@ -355,7 +359,7 @@ def test_e4m3_encode_matches_torch():
     h = np.arange(65536, dtype=np.uint32)
     f = (h << 16).view(np.float32)
     vals.append(f[np.isfinite(f) & (np.abs(f) <= 448)])
-    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+    grid = np.array([orc.e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
     mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
     vals += [mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000))]
     rng = np.random.default_rng(6)
@@ -363,8 +367,8 @@ def test_e4m3_encode_matches_torch():
     v = np.concatenate(vals).astype(np.float32)
     v = np.concatenate([v, -v])
     v = v[np.abs(v) <= 448]
-    assert (oracle.e4m3_encode_array(v) == _torch_e4m3(v)).all()
-    assert oracle.e4m3_encode(-0.0) == 0x80 and oracle.e4m3_encode(0.0) == 0x00
+    assert (orc.e4m3_encode_array(v) == _torch_e4m3(v)).all()
+    assert orc.e4m3_encode(-0.0) == 0x80 and orc.e4m3_encode(0.0) == 0x00
 
 
 # ---------------------------------------------------------------- RoPE variants
@@ -382,7 +386,7 @@ def _run_rope(fn, latent, positions, table, slots, block=4, nb=None, cr=4, width
     return cache, nb
 
 
-def test_mxfp8_exponent_exhaustive_and_values():
+def test_mxfp8_exponent_exhaustive_and_values(orc=oracle):
     """Every positive finite bf16 value as a group's only nonzero element,
     through an identity rotation: scale byte = min(max(E + 127, 0), 254) with
     E the exact ceiling of log2 of fp32(max(amax, fl(1e-4)) * fl(1/448))
@@ -398,7 +402,7 @@ def test_mxfp8_exponent_exhaustive_and_values():
     block = 16
     nb = -(-n // block)
     cache = np.full(nb * block * 528, 0xA5, dtype=np.uint8)
-    oracle.mxfp8_rope_store(latent, positions, _identity_table(), cache, block, nb, slots, 4)
+    orc.mxfp8_rope_store(latent, positions, _identity_table(), cache, block, nb, slots, 4)
     pages = cache.reshape(nb, block * 528)
     inv448 = np.float32(1.0 / 448.0)
     floor = np.float32(1e-4)
@@ -415,19 +419,20 @@ def test_mxfp8_exponent_exhaustive_and_values():
         assert pages[page, r * 512 + 32 * g] == want_val[i], hex(p)
 
 
-def test_mxfp8_zero_group_byte_105():
+def test_mxfp8_zero_group_byte_105(orc=oracle):
     latent = np.zeros((1, 512), dtype=np.uint16)
-    cache, _ = _run_rope(oracle.mxfp8_rope_store, latent, np.array([3], dtype=np.int64),
+    cache, _ = _run_rope(orc.mxfp8_rope_store, latent, np.array([3], dtype=np.int64),
                          _identity_table(), np.array([0], dtype=np.int64))
     assert (cache[4 * 512: 4 * 512 + 16] == 105).all()
     assert (cache[:512] == 0).all()
 
 
-def test_rope_exact_angles_pin_pairing_and_row():
+def test_rope_exact_angles_pin_pairing_and_row(orc=oracle):
     """Rotations by exactly 90 and 180 degrees are permutations/negations of
     the RoPE pairs: (e, o) -> (-o, e) and (-e, -o) on dims 448..511 only.
-    The table row is (position // CR) * CR: rows after it hold NaN and must not
-    be read."""
+    The table row is (position // CR) * CR: rows 41..43 and 61..63 hold NaN and
+    must not be read, while the comparison tokens sit on identity rows 80..83,
+    so only the right row makes the pairs agree."""
     rng = np.random.default_rng(8)
     a = rng.standard_normal((1, 512)).astype(np.float32)
     a[a == 0] = 1.0
@@ -436,7 +441,7 @@ def test_rope_exact_angles_pin_pairing_and_row():
     table = np.full((96, 64), np.nan, dtype=np.float32)
     table[40, :32], table[40, 32:] = 0.0, 1.0    # 90 degrees at row 40
     table[60, :32], table[60, 32:] = -1.0, 0.0   # 180 degrees at row 60
-    table[80, :32], table[80, 32:] = 1.0, 0.0    # identity at row 80
+    table[80:84, :32], table[80:84, 32:] = 1.0, 0.0  # identity at rows 80..83
     b90 = af.copy()
     b90[0, 448::2], b90[0, 449::2] = -af[0, 449::2], af[0, 448::2]
     b180 = af.copy()
@@ -445,7 +450,7 @@ def test_rope_exact_angles_pin_pairing_and_row():
     latent = np.concatenate([ab, to_bits(b90), ab, to_bits(b180)])
     positions = np.array([43, 83, 63, 83], dtype=np.int64)  # bases 40, 80, 60, 80
     slots = np.arange(4, dtype=np.int64)
-    for fn, width in ((oracle.mxfp8_rope_store, 528), (oracle.nvfp4_rope_store, 288)):
+    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288)):
         cache = np.full(4 * width, 0xA5, dtype=np.uint8)
         fn(latent, positions, table, cache, 4, 1, slots, 4)
         vb = 512 if width == 528 else 256
@@ -456,7 +461,7 @@ def test_rope_exact_angles_pin_pairing_and_row():
         assert (vals[2] == vals[3]).all() and (scales[2] == scales[3]).all()
 
 
-def test_rope_gate_and_canaries():
+def test_rope_gate_and_canaries(orc=oracle):
     """Only tokens with a valid slot and (position + 1) % CR == 0 are written;
     everything else keeps its canary."""
     rng = np.random.default_rng(9)
@@ -464,7 +469,7 @@ def test_rope_gate_and_canaries():
     positions = np.array([3, 4, 7, 8, 11, 15, 1, 2], dtype=np.int64)
     slots = np.array([0, 1, 2, 3, -1, 5, 6, 7], dtype=np.int64)
     table = _identity_table(16)
-    for fn, width in ((oracle.mxfp8_rope_store, 528), (oracle.nvfp4_rope_store, 288)):
+    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288)):
         cache = np.full(2 * 4 * width, 0xA5, dtype=np.uint8)
         fn(latent, positions, table, cache, 4, 2, slots, 4)
         vb = 512 if width == 528 else 256
@@ -481,7 +486,7 @@ def test_rope_gate_and_canaries():
                 assert (v == 0xA5).all() and (sc == 0xA5).all(), s
 
 
-def test_nvfp4_scales_and_codes():
+def test_nvfp4_scales_and_codes(orc=oracle):
     """NVFP4 tile scale = torch E4M3 of clamp(fp32(amax * fl(1/6)), 2^-9, 448);
     codes = the pages' midpoint count on the numpy fp32 quotient r / scale,
     saturating at index 7, sign bit below zero."""
@@ -496,7 +501,7 @@ def test_nvfp4_scales_and_codes():
     positions = np.full(n, 3, dtype=np.int64)
     slots = np.arange(n, dtype=np.int64)
     cache = np.full(n * 288, 0xA5, dtype=np.uint8)
-    oracle.nvfp4_rope_store(bits, positions, _identity_table(), cache, n, 1, slots, 4)
+    orc.nvfp4_rope_store(bits, positions, _identity_table(), cache, n, 1, slots, 4)
     vals = cache[: n * 256].reshape(n, 256)
     scales = cache[n * 256:].reshape(n, 32)
     tiles = xf.reshape(n, 32, 16)
@@ -516,7 +521,7 @@ def test_nvfp4_scales_and_codes():
                 assert got == code, (t, k, j, float(y))
 
 
-def test_e2m1_saturates_for_huge_quotients():
+def test_e2m1_saturates_for_huge_quotients(orc=oracle):
     """The pages' midpoint count gives index 7 to every magnitude above 5, so
     huge quotients (an NVFP4 tile whose scale clamped at 448) saturate to
     +-6, whatever their size; NaN codes 0 (reading R16)."""
@@ -525,11 +530,11 @@ def test_e2m1_saturates_for_huge_quotients():
             q = np.float32(s * v)
             want = midpoint_index(abs(Fraction(float(q))) if np.isfinite(q) else Fraction(10 ** 40),
                                   MIDS, STRICT) | (8 if q < 0 else 0)
-            assert oracle.e2m1_code(float(q)) == want == (7 | (8 if s < 0 else 0)), v
-    assert oracle.e2m1_code(float("nan")) == 0
+            assert orc.e2m1_code(float(q)) == want == (7 | (8 if s < 0 else 0)), v
+    assert orc.e2m1_code(float("nan")) == 0
 
 
-def test_nvfp4_huge_tiles_saturate():
+def test_nvfp4_huge_tiles_saturate(orc=oracle):
     """Tiles with amax far above 6 * 448: scale byte 0x7E (448) and every
     element above 5 * 448 in magnitude codes +-6."""
     latent = np.zeros((1, 512), dtype=np.uint16)
@@ -537,8 +542,59 @@ def test_nvfp4_huge_tiles_saturate():
     latent[0, 1] = 0xFF00        # -2^127
     latent[0, 2] = 0x4500        # 2048 -> 2048 / 448 = 4.57 -> code 6
     cache = np.full(288, 0xA5, dtype=np.uint8)
-    oracle.nvfp4_rope_store(latent, np.array([3], dtype=np.int64), _identity_table(), cache, 1, 1,
+    orc.nvfp4_rope_store(latent, np.array([3], dtype=np.int64), _identity_table(), cache, 1, 1,
                             np.array([0], dtype=np.int64), 4)
     assert cache[256] == 0x7E
     assert cache[0] == 0x7 | (0xF << 4)
     assert cache[1] == 0x6 | (0x7 << 4)
+
+
+def test_rope_nan_sanitised(orc=oracle):
+    """With sanitising, NaN becomes +0 before the scales are picked.  NoPE
+    pairs go through the same rotation arithmetic with (cos, sin) = (1, 0), so
+    a NaN also turns its pair partner into NaN (odd*1 + NaN*0) and both become
+    0.  Latent [NaN, 0, 1.0, 0, ...] through an identity rotation:
+    MXFP8 group 0: amax 1 -> v = fl(1/448) in (2^-9, 2^-8] -> E = -8, scale
+    byte 119; 1.0 * 2^8 = 256 -> E4M3 0x78 at element 2; elements 0, 1 -> 0x00.
+    NVFP4 tile 0: sf = fl(1/6) = 0.16667 lies above the E4M3 midpoint 0.1640625
+    of 0.15625 and 0.171875 -> scale 0x23; 1 / 0.171875 = 5.82 -> code 7 at
+    element 2, so byte 0 = 0x00 and byte 1 = 0x07."""
+    latent = np.zeros((1, 512), dtype=np.uint16)
+    latent[0, 0] = 0x7FC0  # NaN
+    latent[0, 1] = 0x0000  # its pair partner
+    latent[0, 2] = 0x3F80  # 1.0, next pair
+    pos, slot = np.array([3], dtype=np.int64), np.array([0], dtype=np.int64)
+    c8 = np.full(528, 0xA5, dtype=np.uint8)
+    orc.mxfp8_rope_store(latent, pos, _identity_table(), c8, 1, 1, slot, 4)
+    assert c8[0] == 0x00 and c8[1] == 0x00 and c8[2] == 0x78 and c8[512] == 119
+    c4 = np.full(288, 0xA5, dtype=np.uint8)
+    orc.nvfp4_rope_store(latent, pos, _identity_table(), c4, 1, 1, slot, 4)
+    assert c4[0] == 0x00 and c4[1] == 0x07 and c4[256] == 0x23
+
+
+def test_mxfp8_exponent_just_above_powers_of_two(orc=oracle):
+    """R11: the exponent is the exact ceiling of log2(v).  RoPE output is full
+    fp32, so with a table entry c and input 1.0 the group amax is exactly c;
+    c is chosen so that v = fl(c * fl(1/448)) is the fp32 just above 2^k.
+    There an fp32 log2 rounds down to k (|k| >= 4), while the exact ceiling,
+    computed here in rationals, is k + 1."""
+    inv448 = np.float32(1.0 / 448.0)
+    for k in (-20, -9, -5, 4, 10, 60):
+        target = np.nextafter(np.float32(2.0 ** k), np.float32(np.inf))
+        c = np.float32(float(target) * 448.0)
+        for _ in range(64):  # walk c until the fp32 product is the target
+            v = np.float32(c * inv448)
+            if v == target:
+                break
+            c = np.nextafter(c, np.float32(np.inf) if v < target else np.float32(0))
+        assert np.float32(c * inv448) == target
+        table = np.zeros((4, 64), dtype=np.float32)
+        table[:, :32] = c
+        latent = np.zeros((1, 512), dtype=np.uint16)
+        latent[0, 448] = 0x3F80  # 1.0 -> rotated to exactly c
+        cache = np.full(528, 0xA5, dtype=np.uint8)
+        orc.mxfp8_rope_store(latent, np.array([3], dtype=np.int64), table, cache, 1, 1,
+                             np.array([0], dtype=np.int64), 4)
+        E = ceil_log2(Fraction(float(target)))
+        assert E == k + 1
+        assert cache[512 + 14] == min(max(E + 127, 0), 254), k

@@ -134,3 +134,32 @@ def test_rope_without_sanitising(device, variant):
     got, want = run_both(device, variant, latent, positions, table, slots, 64, n // 64, 4,
                          sanitize=False)
     assert (got == want).all(), first_mismatch(got, want)
+
+
+def test_mxfp8_exponent_just_above_powers_of_two(device):
+    """fp32 group maxima whose fp32(amax * fl(1/448)) is the float just above
+    2^k: the kernel's exponent must be the exact ceiling (k + 1)."""
+    inv448 = np.float32(1.0 / 448.0)
+    tables, ks = [], (-20, -9, -5, 4, 10, 60)
+    for k in ks:
+        target = np.nextafter(np.float32(2.0 ** k), np.float32(np.inf))
+        c = np.float32(float(target) * 448.0)
+        for _ in range(64):
+            v = np.float32(c * inv448)
+            if v == target:
+                break
+            c = np.nextafter(c, np.float32(np.inf) if v < target else np.float32(0))
+        assert np.float32(c * inv448) == target
+        tables.append(c)
+    n = len(ks)
+    table = np.zeros((4 * n, 64), dtype=np.float32)
+    for i, c in enumerate(tables):
+        table[4 * i:4 * i + 4, :32] = c
+    latent = np.zeros((n, 512), dtype=np.uint16)
+    latent[:, 448] = 0x3F80
+    positions = np.arange(n, dtype=np.int64) * 4 + 3
+    slots = np.arange(n, dtype=np.int64)
+    got, want = run_both(device, "mxfp8", latent, positions, table, slots, n, 1, 4)
+    assert (got == want).all(), first_mismatch(got, want)
+    scales = want[n * 512:].reshape(n, 16)[:, 14]
+    assert [int(b) - 127 for b in scales] == [k + 1 for k in ks]

@@ -222,10 +222,10 @@ def test_large_int64_addressing(device):
 
 
 @pytest.mark.parametrize("latent,nb,bs,stride,ntok", [
-    (512, 1000, 150, 200, 100_000),    # non-power-of-two block, interleaved blocks
+    (512, 1000, 150, 200, 140_000),    # non-power-of-two block, interleaved blocks
     (512, 4096, 64, 64, 200_000),      # contiguous power-of-two blocks
     (512, 2048, 64, 96, 131_072),      # power-of-two block, interleaved
-    (1024, 800, 128, 128, 70_000),
+    (1024, 1100, 128, 128, 140_000),
 ])
 def test_slot_order_form(device, latent, nb, bs, stride, ntok):
     """build_inverse + store_by_slot over dense scattered batches (with pads
@@ -257,7 +257,7 @@ def test_page_api_with_inverse(device):
     """store_mxfp4_mla with an inverse buffer: slot order for a dense batch,
     the scatter form for a sparse one; both match the oracle."""
     rng = np.random.default_rng(22)
-    for ntok, nslots in ((1 << 17, 1 << 17), (70_000, 1 << 20)):
+    for ntok, nslots in ((1 << 17, 1 << 17), (140_000, 1 << 20)):
         src = (rng.standard_normal((ntok, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
         slots = rng.choice(nslots, ntok, replace=False).astype(np.int64)
         inv = torch.empty(nslots, dtype=torch.int32, device=device)
@@ -287,3 +287,17 @@ def test_inverse_map_contents(device):
     got = inv.cpu().numpy()
     assert (got[: nb * bs] == want).all()
     assert (got[nb * bs:] == 12345).all()  # nothing past the map
+
+
+def test_large_batch_ragged_generic_paging(device):
+    """A batch past the 2^18-token switch (4 tokens per wave) with a ragged
+    tail, a non-power-of-two block, interleaved blocks and scattered slots."""
+    rng = np.random.default_rng(24)
+    n, nb, bs, stride = 300_001, 3100, 100, 150
+    x = rng.standard_normal((n, 512)) * np.exp2(rng.uniform(-30, 30, size=(n, 1)))
+    src = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    slots = rng.choice(nb * bs, n, replace=False).astype(np.int64)
+    slots[rng.random(n) < 0.02] = -1
+    log(f"store {n} tokens, B={bs}, stride={stride}")
+    got, want = run_both(device, src, slots, nb, bs, stride, ((nb - 1) * stride + bs) * 272)
+    assert (got == want).all(), first_mismatch(got, want, 272)
