@@ -136,6 +136,21 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
         "frac_hbm_peak": round(n_tokens * 1304 / per / 1e9 / HBM_PEAK_GBS, 4),
     }
     del dq, slots
+    # ring-state save: 262,144 fp32 [kv, score] rows (1024 wide) to scattered
+    # slots of an 8192-block x 32-row ring
+    n_rows = 262_144
+    rows = torch.empty((n_rows, 1024), dtype=torch.float32, device="cuda").uniform_(-1, 1)
+    ring = torch.zeros((8192, 32, 1024), dtype=torch.float32, device="cuda")
+    ring_slots = torch.randperm(8192 * 32, device="cuda")[:n_rows].contiguous()
+    _, ev = time_launches(lambda: ops.save_ring_rows(rows, ring_slots, ring), steps, warmup, torch)
+    per = ev / steps
+    out["save_ring_rows"] = {
+        "workload": f"{n_rows} fp32 rows x 1024 -> scattered slots of an 8192 x 32 ring",
+        "us_per_launch": round(per * 1e6, 2),
+        "GBps": round(n_rows * (4096 + 4096 + 8) / per / 1e9, 1),
+        "frac_hbm_peak": round(n_rows * (4096 + 4096 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    del rows, ring, ring_slots
     # RoPE inserts on the 16384-token, compress-ratio-4 workload
     case = workloads.rope_case()
     lat = torch.from_numpy(case.latent.view("int16")).cuda().view(torch.bfloat16)

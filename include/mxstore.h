@@ -103,7 +103,7 @@ int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
 int64_t mxfp4_inverse_bytes(int64_t num_blocks, int64_t block_size);
 
 /* 1 when the slot-order form is expected to beat mxfp4_store for this shape:
- * latent in {512, 1024, 2048}, 2^16 <= num_tokens < 2^31 and num_tokens >=
+ * latent in {512, 1024, 2048}, 2^17 <= num_tokens < 2^31 and num_tokens >=
  * half the slots; else 0.  Host-only heuristic (measured on MI355X), no
  * device work. */
 int mxfp4_slot_order_advised(int64_t num_tokens, int64_t latent,
@@ -201,6 +201,28 @@ int nvfp4_rope_store(const uint16_t* latent_bf16, const int64_t* positions,
                      const int64_t* slot_mapping, int64_t num_tokens,
                      int32_t compress_ratio, int32_t sanitize_nans,
                      void* stream);
+
+/*
+ * Ring-state save [P2 `save_ring_rows`; ring rule from the
+ * `fused_save_compress_norm` docstring]: for each i < num_rows with
+ * s = slot_mapping[i] in [0, num_blocks * capacity), copy the fp32 row
+ * rows[i, 0:width] bit for bit to
+ *   state + (s / capacity) * state_stride + (s % capacity) * state_row_stride
+ * (all strides in elements).  Slot -1 -- and any other negative slot or one
+ * past the last ring row -- is skipped.  The pages' rows are the [kv, score]
+ * states, width 1024.
+ *
+ * rows            fp32 [num_rows, width], row stride row_stride >= width.
+ * state           fp32 ring [num_blocks, capacity, width]-shaped view with
+ *                 state_row_stride >= width, state_stride >= capacity *
+ *                 state_row_stride.
+ * width           multiple of 4 in [4, 2^20]; rows and state 16-byte aligned
+ *                 and every stride a multiple of 4 elements.
+ */
+int save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64_t row_stride,
+                   const int64_t* slot_mapping, float* state, int64_t num_blocks,
+                   int64_t capacity, int64_t state_stride, int64_t state_row_stride,
+                   void* stream);
 
 /* Message for the last nonzero status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */

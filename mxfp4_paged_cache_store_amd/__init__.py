@@ -22,6 +22,7 @@ from .ops import (
     resolve_paged_view,
     rope_quant_insert,
     row_bytes,
+    save_ring_rows,
     store_mxfp4_mla,
 )
 from ._abi import MxError
@@ -42,5 +43,6 @@ __all__ = [
     "resolve_paged_view",
     "rope_quant_insert",
     "row_bytes",
+    "save_ring_rows",
     "store_mxfp4_mla",
 ]

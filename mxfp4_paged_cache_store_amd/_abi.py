@@ -32,6 +32,7 @@ EXPORTED = (
     "mxfp4_gather_dequant",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
+    "save_ring_rows",
     "mx_last_error",
 )
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp]
+        L.save_ring_rows.restype = ctypes.c_int
+        L.save_ring_rows.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
         L.mx_last_error.restype = ctypes.c_char_p
         L.mx_last_error.argtypes = []
         _lib = L

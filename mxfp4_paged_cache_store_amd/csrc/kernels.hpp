@@ -44,7 +44,21 @@ struct RopeArgs {
   int32_t sanitize;
 };
 
+struct RingArgs {
+  const float* rows;  // [num_rows, width], row stride row_stride (elements)
+  int64_t num_rows;
+  int64_t width;      // multiple of 4
+  int64_t row_stride;
+  const int64_t* slots;
+  float* state;       // ring: block stride state_stride, row stride state_row_stride
+  uint32_t num_slots; // num_blocks * capacity
+  uint32_t capacity;
+  int64_t state_stride;
+  int64_t state_row_stride;
+};
+
 // Each returns the hipError_t of the launch.
+hipError_t launch_ring_rows(const RingArgs& a, hipStream_t stream);
 hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream);
 // Slot-order form: inverse[s] = token of slot s or -1 (num_slots int32,
 // 16-byte aligned), then the gather-store over all slots.

@@ -44,7 +44,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTokensPerWave = 4;
 constexpr int kWavesPerBlock = 4;
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -106,7 +105,8 @@ __device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw)
 // LATENT: values per token (power of two, 128..2048).  A token occupies
 // min(LATENT/8, 64) lanes per pass; LATENT > 512 takes LATENT/512 passes.
 // kPow2: slot -> row by shift/mask (else a 32-bit division).
-template <int LATENT, bool kPow2>
+// kTokensPerWave: passes per wave (2 for small batches, 4 for large: measured).
+template <int LATENT, bool kPow2, int kTokensPerWave>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(const StoreArgs a) {
   constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
   constexpr int kToksPerPass = kWave / kLanesPerTok;
@@ -306,20 +306,26 @@ hipError_t launch_by_slot(const StoreArgs& a, const int32_t* inv, hipStream_t st
   return hipGetLastError();
 }
 
-template <int LATENT>
-hipError_t launch_latent(const StoreArgs& a, hipStream_t stream) {
+template <int LATENT, int TPW>
+hipError_t launch_tpw(const StoreArgs& a, hipStream_t stream) {
   constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
-  constexpr int64_t kToksPerBlock =
-      (int64_t)kWavesPerBlock * kTokensPerWave * (kWave / kLanesPerTok);
+  constexpr int64_t kToksPerBlock = (int64_t)kWavesPerBlock * TPW * (kWave / kLanesPerTok);
   const int64_t blocks = (a.num_tokens + kToksPerBlock - 1) / kToksPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (a.map.pow2)
-    hipLaunchKernelGGL((mxfp4_store_kernel<LATENT, true>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((mxfp4_store_kernel<LATENT, true, TPW>), dim3((unsigned)blocks),
                        dim3(kWave * kWavesPerBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((mxfp4_store_kernel<LATENT, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((mxfp4_store_kernel<LATENT, false, TPW>), dim3((unsigned)blocks),
                        dim3(kWave * kWavesPerBlock), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int LATENT>
+hipError_t launch_latent(const StoreArgs& a, hipStream_t stream) {
+  // Small batches are latency-bound: more, shorter waves finish sooner.
+  if (a.num_tokens < (int64_t(1) << 18)) return launch_tpw<LATENT, 2>(a, stream);
+  return launch_tpw<LATENT, 4>(a, stream);
 }
 
 }  // namespace

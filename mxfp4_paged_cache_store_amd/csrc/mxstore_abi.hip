@@ -173,7 +173,7 @@ int mxfp4_slot_order_advised(int64_t num_tokens, int64_t latent, int64_t num_blo
   // The slot order pays for its inverse once a batch is large enough to
   // stream from HBM and covers at least half of the slots.
   const int64_t num_slots = num_blocks * block_size;
-  return num_tokens >= (int64_t(1) << 16) && num_tokens <= 0x7FFFFFFF && 2 * num_tokens >= num_slots;
+  return num_tokens >= (int64_t(1) << 17) && num_tokens <= 0x7FFFFFFF && 2 * num_tokens >= num_slots;
 }
 
 int mxfp4_build_inverse(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
@@ -262,6 +262,36 @@ int nvfp4_rope_store(const uint16_t* latent_bf16, const int64_t* positions, cons
   if (num_tokens == 0) return ok();
   a.sanitize = sanitize_nans ? 1 : 0;
   return launched(mxs::launch_nvfp4_rope(a, (hipStream_t)stream), "nvfp4_rope_store");
+}
+
+int save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64_t row_stride,
+                   const int64_t* slot_mapping, float* state, int64_t num_blocks, int64_t capacity,
+                   int64_t state_stride, int64_t state_row_stride, void* stream) {
+  if (num_rows < 0) return fail(MX_E_RANGE, "num_rows must be >= 0");
+  if (width < 4 || width % 4 || width > (int64_t(1) << 20))
+    return fail(MX_E_SHAPE, "width must be a multiple of 4 in [4, 2^20], got %lld", (long long)width);
+  if (num_blocks < 1 || capacity < 1 || num_blocks > (int64_t(0xFFFFFFFF) / capacity))
+    return fail(MX_E_RANGE, "num_blocks and capacity must be >= 1 with fewer than 2^32 ring rows");
+  if (row_stride < width || state_row_stride < width || state_stride < capacity * state_row_stride)
+    return fail(MX_E_STRIDE, "row strides must cover a row and the block stride a whole ring");
+  if (row_stride % 4 || state_row_stride % 4 || state_stride % 4)
+    return fail(MX_E_ALIGN, "strides must be multiples of 4 elements (16 bytes)");
+  if (num_rows == 0) return ok();
+  if (!rows || !slot_mapping || !state) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(rows, 16) || !aligned(state, 16))
+    return fail(MX_E_ALIGN, "rows and state must be 16-byte aligned");
+  mxs::RingArgs a{};
+  a.rows = rows;
+  a.num_rows = num_rows;
+  a.width = width;
+  a.row_stride = row_stride;
+  a.slots = slot_mapping;
+  a.state = state;
+  a.num_slots = (uint32_t)(num_blocks * capacity);
+  a.capacity = (uint32_t)capacity;
+  a.state_stride = state_stride;
+  a.state_row_stride = state_row_stride;
+  return launched(mxs::launch_ring_rows(a, (hipStream_t)stream), "save_ring_rows");
 }
 
 const char* mx_last_error(void) { return g_err; }

@@ -168,6 +168,26 @@ def nvfp4_rope_store(latent, positions, cos_sin, kv_cache, slot_mapping, compres
                                            _stream(stream)))
 
 
+def save_ring_rows(rows: torch.Tensor, slot_mapping: torch.Tensor, state_cache: torch.Tensor,
+                   stream=None) -> None:
+    """Store fp32 [kv, score] rows to their ring slots, skipping slot -1
+    [P2 `save_ring_rows`]: same arguments and checks as the page's wrapper;
+    ``state_cache`` is the fp32 ring [blocks, capacity, width]."""
+    _need_cuda(rows, slot_mapping, state_cache)
+    if rows.dtype != torch.float32 or rows.dim() != 2 or rows.stride(1) != 1:
+        raise ValueError("rows must be fp32 [n, width] with unit inner stride")
+    if state_cache.dtype != torch.float32 or state_cache.dim() != 3 or state_cache.stride(2) != 1 \
+            or state_cache.shape[2] != rows.shape[1]:
+        raise ValueError("state_cache must be fp32 [blocks, capacity, width] with unit inner stride")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() \
+            or slot_mapping.numel() != rows.shape[0]:
+        raise ValueError("slot_mapping must be contiguous int64 with one entry per row")
+    _abi.check(_abi.lib().save_ring_rows(
+        rows.data_ptr(), rows.shape[0], rows.shape[1], rows.stride(0), slot_mapping.data_ptr(),
+        state_cache.data_ptr(), state_cache.shape[0], state_cache.shape[1], state_cache.stride(0),
+        state_cache.stride(1), _stream(stream)))
+
+
 # ------------------------------------------------------------------ page-level API
 
 def resolve_paged_view(cache: torch.Tensor, latent: int, group: int = GROUP_SIZE):

@@ -73,6 +73,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
+    lib.orc_save_ring_rows.restype = ctypes.c_int
+    lib.orc_save_ring_rows.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64]
     return lib
 
 
@@ -216,6 +218,21 @@ class Oracle:
                          num_blocks, stride, slot_mapping, compress_ratio, sanitize)
 
 
+    def save_ring_rows(self, rows: np.ndarray, slot_mapping: np.ndarray,
+                       state: np.ndarray) -> None:
+        """Copy fp32 ``rows`` [n, width] (row-strided allowed) into the ring
+        ``state`` [blocks, capacity, width] (strided views allowed) in place."""
+        assert rows.dtype == np.float32 and rows.ndim == 2 and rows.strides[1] == 4
+        assert state.dtype == np.float32 and state.ndim == 3 and state.strides[2] == 4
+        assert slot_mapping.dtype == np.int64 and slot_mapping.flags.c_contiguous
+        assert slot_mapping.size == rows.shape[0] and state.shape[2] == rows.shape[1]
+        rc = self.lib.orc_save_ring_rows(
+            rows.ctypes.data, rows.shape[0], rows.shape[1], rows.strides[0] // 4,
+            _ptr(slot_mapping), state.ctypes.data, state.shape[0], state.shape[1],
+            state.strides[0] // 4, state.strides[1] // 4)
+        _check(rc, "save_ring_rows")
+
+
 def default() -> Oracle:
     """The oracle built from oracle/mxoracle.c (built on first use)."""
     global _default
@@ -249,3 +266,4 @@ mxfp4_store = _forward("mxfp4_store")
 mxfp4_gather_dequant = _forward("mxfp4_gather_dequant")
 mxfp8_rope_store = _forward("mxfp8_rope_store")
 nvfp4_rope_store = _forward("nvfp4_rope_store")
+save_ring_rows = _forward("save_ring_rows")

@@ -478,3 +478,31 @@ int orc_nvfp4_rope_store(const uint16_t* latent, const int64_t* positions,
   }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Ring-state save [P2 `save_ring_rows`]                               */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Copy fp32 rows of `width` values (the [kv, score] state, 1024 wide on the
+ * page) to their ring slots.  A slot s encodes block * capacity + row, row =
+ * the position modulo the ring capacity [P2 `fused_save_compress_norm`
+ * docstring], so the destination is state + (s / capacity) * state_stride +
+ * (s % capacity) * state_row_stride (strides in elements).  Slot -1 (and, by
+ * our reading, any negative slot or one past the last ring row) is skipped.
+ * The copy is bit-for-bit (NaN payloads included).
+ */
+int orc_save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64_t row_stride,
+                       const int64_t* slot_mapping, float* state, int64_t num_blocks,
+                       int64_t capacity, int64_t state_stride, int64_t state_row_stride) {
+  if (num_rows < 0 || width < 1 || row_stride < width || num_blocks < 1 || capacity < 1)
+    return ORC_EINVAL;
+  if (state_row_stride < width || state_stride < capacity * state_row_stride) return ORC_EINVAL;
+  for (int64_t i = 0; i < num_rows; ++i) {
+    int64_t s = slot_mapping[i];
+    if (s < 0 || s >= num_blocks * capacity) continue;
+    float* dst = state + (s / capacity) * state_stride + (s % capacity) * state_row_stride;
+    memcpy(dst, rows + i * row_stride, (size_t)width * sizeof(float));
+  }
+  return ORC_OK;
+}

@@ -192,3 +192,30 @@ def test_store_by_slot_rejects(mxlib, kw, status):
 
 def test_store_by_slot_empty_is_a_noop(mxlib):
     assert store_by_slot(mxlib, n=0, src=0, inv=0, cache=0) == _abi.MX_OK
+
+
+def ring(mxlib, **kw):
+    a = dict(rows=FAKE, n=3, width=1024, rstride=1024, slots=FAKE, state=FAKE, nb=4, cap=8,
+             sstride=8 * 1024, srstride=1024)
+    a.update(kw)
+    return mxlib.save_ring_rows(a["rows"], a["n"], a["width"], a["rstride"], a["slots"], a["state"],
+                                a["nb"], a["cap"], a["sstride"], a["srstride"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(width=1022, rstride=1024), _abi.MX_E_SHAPE),
+    (dict(width=0), _abi.MX_E_SHAPE),
+    (dict(n=-1), _abi.MX_E_RANGE),
+    (dict(cap=0), _abi.MX_E_RANGE),
+    (dict(rstride=1000), _abi.MX_E_STRIDE),
+    (dict(sstride=7 * 1024), _abi.MX_E_STRIDE),
+    (dict(rstride=1026), _abi.MX_E_ALIGN),
+    (dict(rows=FAKE + 4), _abi.MX_E_ALIGN),
+    (dict(state=0), _abi.MX_E_NULL),
+])
+def test_ring_rows_rejects(mxlib, kw, status):
+    assert ring(mxlib, **kw) == status
+
+
+def test_ring_rows_empty_is_a_noop(mxlib):
+    assert ring(mxlib, n=0, rows=0, slots=0, state=0) == _abi.MX_OK

@@ -1,0 +1,71 @@
+"""The entry points can be captured in a HIP graph: every replay, with eager
+work and synchronisations in between, writes the same bytes as eager calls.
+(No entry point records a memset: the inverse map is cleared by a kernel.)"""
+
+import numpy as np
+import pytest
+import torch
+
+from mxfp4_paged_cache_store_amd import ops, workloads
+from tests.gpu_util import bf16_dev, i64_dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager(device):
+    n = 1 << 17  # large and dense enough for the slot-order form
+    g_src = torch.empty((n, 512), dtype=torch.bfloat16, device=device)
+    g_slots = torch.randperm(n, device=device)
+    inv = torch.empty(n, dtype=torch.int32, device=device)
+    g_cache = torch.empty(n * 272, dtype=torch.uint8, device=device)
+    p_src = torch.empty((4096, 512), dtype=torch.bfloat16, device=device)
+    p_slots = torch.randperm(1 << 16, device=device)[:4096]
+    p_cache = torch.empty((1 << 16) * 272, dtype=torch.uint8, device=device)
+    dq_out = torch.empty((4096, 512), dtype=torch.bfloat16, device=device)
+    rc = workloads.rope_case(tokens=1024)
+    r_lat = bf16_dev(rc.latent, device)
+    r_pos, r_cs, r_slots = i64_dev(rc.positions, device), torch.from_numpy(rc.cos_sin).to(device), i64_dev(rc.slots, device)
+    r_kv = torch.empty((16, 64, 528), dtype=torch.uint8, device=device)
+    assert ops.mxfp4_slot_order_advised(n, 512, 1, n)
+
+    def work():
+        ops.store_mxfp4_mla(g_src, g_slots, g_cache, inverse=inv)
+        ops.mxfp4_store(p_src, p_slots, p_cache, 1, 1 << 16, 1 << 16)
+        ops.mxfp4_gather_dequant(p_cache, 1, 1 << 16, 1 << 16, 512, p_slots, dq_out)
+        ops.mxfp8_rope_store(r_lat, r_pos, r_cs, r_kv, r_slots, rc.compress_ratio)
+
+    def reset(seed):
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+        g_src.uniform_(-4, 4, generator=gen)
+        p_src.uniform_(-100, 100, generator=gen)
+        g_cache.fill_(0xA5)
+        p_cache.fill_(0xA5)
+        dq_out.fill_(0)
+        r_kv.fill_(0xA5)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset(0)
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+
+    for rep in range(4):
+        log(f"graph replay {rep}")
+        reset(100 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [g_cache.clone(), p_cache.clone(), dq_out.clone(), r_kv.clone()]
+        reset(100 + rep)
+        work()  # eager
+        torch.cuda.synchronize()
+        want = [g_cache, p_cache, dq_out, r_kv]
+        for name, a, b in zip(("slot-order store", "scatter store", "dequant", "mxfp8 insert"), got, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rep, name)

@@ -598,3 +598,31 @@ def test_mxfp8_exponent_just_above_powers_of_two(orc=oracle):
         E = ceil_log2(Fraction(float(target)))
         assert E == k + 1
         assert cache[512 + 14] == min(max(E + 127, 0), 254), k
+
+
+def test_save_ring_rows_placement(orc=oracle):
+    """[P2 `save_ring_rows`] with the ring rule of `fused_save_compress_norm`:
+    slot s lands in block s // capacity, ring row s % capacity.  Hand-placed
+    case (capacity 3, 3 blocks, padded strides): slots 0, 4, -1, 5, 8, 9, -7
+    -> (0,0), (1,1), skip, (1,2), (2,2), skip (past the last row), skip.
+    Rows are bit patterns, NaN payloads and -0.0 included."""
+    rng = np.random.default_rng(30)
+    bits = rng.integers(0, 2**32, size=(7, 6), dtype=np.uint64).astype(np.uint32)
+    bits[0, 0] = 0x7FC01234  # NaN with payload
+    bits[1, 1] = 0x80000000  # -0.0
+    rows_wide = np.zeros((7, 8), dtype=np.float32)
+    rows_wide[:, :6] = bits.view(np.float32)
+    rows = rows_wide[:, :6]
+    backing = np.full((3, 4, 7), np.float32(1.5), dtype=np.float32)  # canary value
+    state = backing[:, :3, :6]
+    slots = np.array([0, 4, -1, 5, 8, 9, -7], dtype=np.int64)
+    orc.save_ring_rows(rows, slots, state)
+    placed = {(0, 0): 0, (1, 1): 1, (1, 2): 3, (2, 2): 4}
+    for b in range(3):
+        for r in range(4):
+            for c in range(7):
+                got = np.array(backing[b, r, c]).view(np.uint32)
+                if r < 3 and c < 6 and (b, r) in placed:
+                    assert got == bits[placed[(b, r)], c], (b, r, c)
+                else:
+                    assert got == np.array(np.float32(1.5)).view(np.uint32), (b, r, c)
