@@ -73,6 +73,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
+    lib.orc_rmsnorm_cr1.restype = ctypes.c_int
+    lib.orc_rmsnorm_cr1.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _i64]
     lib.orc_save_ring_rows.restype = ctypes.c_int
     lib.orc_save_ring_rows.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64]
     return lib
@@ -233,6 +235,26 @@ class Oracle:
         _check(rc, "save_ring_rows")
 
 
+    def rmsnorm_cr1(self, kv: np.ndarray, slot_mapping: np.ndarray, weight_bf16: np.ndarray,
+                    eps: float, out: np.ndarray | None = None) -> np.ndarray:
+        """RMSNorm of the valid fp32 rows of ``kv`` [n, width] (row-strided
+        allowed) with a bf16-bits weight, in double; rows of invalid tokens of
+        ``out`` (float64 [n, width]) are left as they are (NaN if allocated
+        here)."""
+        assert kv.dtype == np.float32 and kv.ndim == 2 and kv.strides[1] == 4
+        assert slot_mapping.dtype == np.int64 and slot_mapping.flags.c_contiguous
+        w = np.ascontiguousarray(weight_bf16, dtype=np.uint16)
+        n, width = slot_mapping.size, kv.shape[1]
+        assert w.size == width and kv.shape[0] >= n
+        if out is None:
+            out = np.full((n, width), np.nan, dtype=np.float64)
+        assert out.dtype == np.float64 and out.flags.c_contiguous
+        rc = self.lib.orc_rmsnorm_cr1(kv.ctypes.data, n, width, kv.strides[0] // 4,
+                                      _ptr(slot_mapping), _ptr(w), eps, _ptr(out), out.shape[1])
+        _check(rc, "rmsnorm_cr1")
+        return out
+
+
 def default() -> Oracle:
     """The oracle built from oracle/mxoracle.c (built on first use)."""
     global _default
@@ -267,3 +289,4 @@ mxfp4_gather_dequant = _forward("mxfp4_gather_dequant")
 mxfp8_rope_store = _forward("mxfp8_rope_store")
 nvfp4_rope_store = _forward("nvfp4_rope_store")
 save_ring_rows = _forward("save_ring_rows")
+rmsnorm_cr1 = _forward("rmsnorm_cr1")

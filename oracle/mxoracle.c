@@ -506,3 +506,36 @@ int orc_save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64
   }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Compress-ratio-1 normalisation [P2 `fused_save_compress_norm`]      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * With compress ratio 1 each token is a group of its own: there is no ring
+ * state and nothing to pool, and the slot mapping serves only to say which
+ * tokens are valid (a negative slot: not written) [P2
+ * `fused_save_compress_norm`, its description and parameter list].  The
+ * step is then an RMSNorm of the token's fp32 row (`width` values, 512 on
+ * the page) with a bf16 weight:
+ *   y[d] = x[d] / sqrt(mean(x^2) + eps) * w[d].
+ * Computed here in double (the pages do not fix the reduction order), so the
+ * result is the exact value up to double rounding; out[t] is written only
+ * for slot_mapping[t] >= 0.  Parity against the GPU is a tolerance derived
+ * from fp32 arithmetic and the final bf16 rounding.
+ */
+int orc_rmsnorm_cr1(const float* kv, int64_t num_tokens, int64_t width, int64_t row_stride,
+                    const int64_t* slot_mapping, const uint16_t* weight_bf16, float eps,
+                    double* out, int64_t out_row_stride) {
+  if (num_tokens < 0 || width < 1 || row_stride < width || out_row_stride < width) return ORC_EINVAL;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (slot_mapping[t] < 0) continue;
+    const float* x = kv + t * row_stride;
+    double ss = 0.0;
+    for (int64_t d = 0; d < width; ++d) ss += (double)x[d] * (double)x[d];
+    const double r = 1.0 / sqrt(ss / (double)width + (double)eps);
+    double* y = out + t * out_row_stride;
+    for (int64_t d = 0; d < width; ++d) y[d] = (double)x[d] * r * (double)bf16_to_f32(weight_bf16[d]);
+  }
+  return ORC_OK;
+}

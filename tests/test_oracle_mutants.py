@@ -24,6 +24,8 @@ CHECKS = [
     (pins.test_mxfp8_zero_group_byte_105, {}),
     (pins.test_mxfp8_exponent_just_above_powers_of_two, {}),
     (pins.test_rope_nan_sanitised, {}),
+    (pins.test_save_ring_rows_placement, {}),
+    (pins.test_rmsnorm_cr1_closed_forms, {}),
     (pins.test_rope_gate_and_canaries, {}),
     (pins.test_rope_exact_angles_pin_pairing_and_row, {}),
     (pins.test_nvfp4_huge_tiles_saturate, {}),
@@ -68,6 +70,13 @@ MUTANTS = {
     "RoPE rotation sign": ("r[2 * p] = ec - os;", "r[2 * p] = ec + os;"),
     "no NaN sanitising": ("if (isnan(r[d])) r[d] = 0.0f;", "(void)r;"),
     "NVFP4 scale not rounded to E4M3": ("float S = (float)e4m3_value(s8);", "float S = sf;"),
+    "ring row from block stride": (
+        "(s / capacity) * state_stride + (s % capacity) * state_row_stride;",
+        "(s / capacity) * state_stride + (s % capacity) * width;"),
+    "ring keeps slots past the end": ("if (s < 0 || s >= num_blocks * capacity) continue;", "if (s < 0) continue;"),
+    "RMSNorm without eps": ("sqrt(ss / (double)width + (double)eps)", "sqrt(ss / (double)width)"),
+    "RMSNorm mean over width-1": ("sqrt(ss / (double)width + (double)eps)", "sqrt(ss / (double)(width - 1) + (double)eps)"),
+    "RMSNorm writes invalid tokens": ("    if (slot_mapping[t] < 0) continue;\n    const float* x = kv", "    const float* x = kv"),
     "NVFP4 sign of -0.0 kept": ("return idx | ((q < 0.0f) ? 8 : 0);", "return idx | ((q < 0.0f || signbit(q)) ? 8 : 0);"),
 }
 

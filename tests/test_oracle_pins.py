@@ -613,12 +613,13 @@ def test_save_ring_rows_placement(orc=oracle):
     rows_wide = np.zeros((7, 8), dtype=np.float32)
     rows_wide[:, :6] = bits.view(np.float32)
     rows = rows_wide[:, :6]
-    backing = np.full((3, 4, 7), np.float32(1.5), dtype=np.float32)  # canary value
-    state = backing[:, :3, :6]
+    # a fourth block of canaries sits where slot 9 would land if kept
+    backing = np.full((4, 4, 7), np.float32(1.5), dtype=np.float32)
+    state = backing[:3, :3, :6]
     slots = np.array([0, 4, -1, 5, 8, 9, -7], dtype=np.int64)
     orc.save_ring_rows(rows, slots, state)
     placed = {(0, 0): 0, (1, 1): 1, (1, 2): 3, (2, 2): 4}
-    for b in range(3):
+    for b in range(4):
         for r in range(4):
             for c in range(7):
                 got = np.array(backing[b, r, c]).view(np.uint32)
@@ -626,3 +627,30 @@ def test_save_ring_rows_placement(orc=oracle):
                     assert got == bits[placed[(b, r)], c], (b, r, c)
                 else:
                     assert got == np.array(np.float32(1.5)).view(np.uint32), (b, r, c)
+
+
+def test_rmsnorm_cr1_closed_forms(orc=oracle):
+    """Compress ratio 1 [P2 `fused_save_compress_norm`]: y = x / rms(x) * w.
+    Closed forms: a constant row c with eps = 0 gives sign(c) * w exactly;
+    x = (3, 4, 0, ...) over 512 dims has rms 5 / sqrt(512); scaling x by 2^k
+    leaves y unchanged when eps = 0; eps enters under the root; tokens with a
+    negative slot are not written."""
+    w = np.full(512, 0x3F80, dtype=np.uint16)          # 1.0
+    w[7] = 0xC000                                       # -2.0
+    kv = np.zeros((5, 512), dtype=np.float32)
+    kv[0] = 0.75
+    kv[1] = -3.0
+    kv[2, 0], kv[2, 1] = 3.0, 4.0
+    kv[3] = kv[2] * np.float32(2.0 ** 40)
+    kv[4] = 1.0
+    slots = np.array([0, 1, 2, 3, -1], dtype=np.int64)
+    y = orc.rmsnorm_cr1(kv, slots, w, 0.0)
+    assert (y[0] == np.where(np.arange(512) == 7, -2.0, 1.0)).all()
+    assert (y[1] == np.where(np.arange(512) == 7, 2.0, -1.0)).all()
+    s = np.sqrt(512.0) / 5.0
+    assert abs(y[2, 0] - 3 * s) < 1e-12 and abs(y[2, 1] - 4 * s) < 1e-12 and (y[2, 2:] == 0).all()
+    assert np.allclose(y[3], y[2], rtol=1e-15, atol=0)
+    assert np.isnan(y[4]).all()                         # not written
+    eps = 0.25
+    y_eps = orc.rmsnorm_cr1(kv[:1], slots[:1], w, eps)
+    assert abs(y_eps[0, 0] - 0.75 / np.sqrt(0.75 ** 2 + eps)) < 1e-15
