@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-companions", action="store_true")
     p.add_argument("--sweep", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=1_000_000)
+    p.add_argument("--cpu-sample", type=int, default=4_500_000)
     p.add_argument("--scatter", action="store_true", help="time the scatter form as the step")
     p.add_argument("--counters", action="store_true",
                    help="for rocprofv3 --pmc: a 1 GiB copy (calibration) then 3 steps, no JSON")
@@ -116,7 +116,8 @@ def cpu_baseline(sample: int):
         "kind": "oracle",
         "sample": f"{sample} tokens x 512 bf16 uniform in [-4, 4], random-permutation slots "
                   f"into a flat cache (same distribution as the timed batch), "
-                  f"{threads} threads over contiguous token ranges, {dt:.2f} s",
+                  f"{threads} threads over contiguous token ranges, {dt:.2f} s wall "
+                  f"({threads * dt:.0f} thread-seconds)",
     }
 
 
@@ -151,6 +152,23 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
         "frac_hbm_peak": round(n_rows * (4096 + 4096 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
     }
     del rows, ring, ring_slots
+    # compress-ratio-1 RMSNorm: 2,097,152 fp32 [512] rows -> bf16, all valid
+    n_norm = 1 << 21
+    kv = torch.empty((n_norm, 512), dtype=torch.float32, device="cuda").normal_()
+    norm_slots = torch.arange(n_norm, dtype=torch.int64, device="cuda")
+    w = torch.empty(512, dtype=torch.float32, device="cuda").normal_(0.8, 0.5).to(torch.bfloat16)
+    latent_out = torch.empty((n_norm, 512), dtype=torch.bfloat16, device="cuda")
+    _, ev = time_launches(lambda: ops.fused_save_compress_norm_cr1(kv, norm_slots, w, 1e-6, latent_out),
+                          steps, warmup, torch)
+    per = ev / steps
+    out["fused_save_compress_norm_cr1"] = {
+        "workload": f"{n_norm} fp32 rows x 512 -> bf16 RMSNorm, all tokens valid",
+        "us_per_launch": round(per * 1e6, 2),
+        "tokens_per_s": round(n_norm / per, 1),
+        "GBps": round(n_norm * (2048 + 1024 + 8) / per / 1e9, 1),
+        "frac_hbm_peak": round(n_norm * (2048 + 1024 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    del kv, norm_slots, w, latent_out
     # RoPE inserts on the 16384-token, compress-ratio-4 workload
     case = workloads.rope_case()
     lat = torch.from_numpy(case.latent.view("int16")).cuda().view(torch.bfloat16)

@@ -224,6 +224,32 @@ int save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64_t r
                    int64_t capacity, int64_t state_stride, int64_t state_row_stride,
                    void* stream);
 
+/*
+ * Compress-ratio-1 case of the save/compress/norm step [P2
+ * `fused_save_compress_norm`: ratio 1 keeps no ring and the slot mapping
+ * only marks valid tokens; weight bf16 [512], output bf16 [tokens, 512]
+ * written only where valid].  For each t < num_tokens with
+ * slot_mapping[t] >= 0:
+ *   r = 1 / sqrt(sum_d kv[t, d]^2 / 512 + rms_norm_eps)
+ *   latent_out[t, d] = bf16_rn((kv[t, d] * r) * w[d])
+ * in fp32 with correctly rounded sqrt and division; the order of the sum is
+ * the kernel's own (the pages do not fix it).  Rows of other tokens are not
+ * written.
+ *
+ * kv_score         fp32 [num_tokens, 512], row stride kv_row_stride >= 512,
+ *                  a multiple of 4; 16-byte aligned.
+ * width            must be 512.
+ * rms_norm_weight  bf16 [512], 8-byte aligned.
+ * rms_norm_eps     finite, >= 0.
+ * latent_out       bf16 [num_tokens, 512], row stride out_row_stride >= 512,
+ *                  a multiple of 4; 8-byte aligned.
+ * num_tokens       [0, 2^33]; 0 is a no-op.
+ */
+int fused_save_compress_norm_cr1(const float* kv_score, int64_t num_tokens, int64_t width,
+                                 int64_t kv_row_stride, const int64_t* slot_mapping,
+                                 const uint16_t* rms_norm_weight, float rms_norm_eps,
+                                 uint16_t* latent_out, int64_t out_row_stride, void* stream);
+
 /* Message for the last nonzero status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
 const char* mx_last_error(void);

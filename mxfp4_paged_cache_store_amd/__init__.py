@@ -4,11 +4,13 @@ libmxstore.so (hand-written HIP for gfx950, C ABI in include/mxstore.h)
 quantizes a bf16 MLA latent to MXFP4 (E2M1 codes + one E8M0 scale per 32
 values, 272 bytes per 512-wide token) and scatters it into a paged cache; a
 gather-dequant companion unpacks slots back to bf16; two RoPE+quant inserts
-write the MXFP8 (528 B) and NVFP4 (288 B) compressed-cache records.
+write the MXFP8 (528 B) and NVFP4 (288 B) compressed-cache records; the
+ring-state save and the compress-ratio-1 RMSNorm precede those inserts.
 """
 
 from .ops import (
     GROUP_SIZE,
+    fused_save_compress_norm_cr1,
     MXFP8_RECORD_BYTES,
     NVFP4_RECORD_BYTES,
     mxfp4_gather_dequant,
@@ -32,6 +34,7 @@ __all__ = [
     "MXFP8_RECORD_BYTES",
     "NVFP4_RECORD_BYTES",
     "MxError",
+    "fused_save_compress_norm_cr1",
     "mxfp4_gather_dequant",
     "mxfp4_store",
     "mxfp4_build_inverse",

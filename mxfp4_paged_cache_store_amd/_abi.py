@@ -33,6 +33,7 @@ EXPORTED = (
     "mxfp8_rope_store",
     "nvfp4_rope_store",
     "save_ring_rows",
+    "fused_save_compress_norm_cr1",
     "mx_last_error",
 )
 
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp]
         L.save_ring_rows.restype = ctypes.c_int
         L.save_ring_rows.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
+        L.fused_save_compress_norm_cr1.restype = ctypes.c_int
+        L.fused_save_compress_norm_cr1.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_float,
+                                                   _vp, _i64, _vp]
         L.mx_last_error.restype = ctypes.c_char_p
         L.mx_last_error.argtypes = []
         _lib = L

@@ -57,8 +57,20 @@ struct RingArgs {
   int64_t state_row_stride;
 };
 
+struct NormArgs {
+  const float* kv;        // [num_tokens, 512] fp32, row stride kv_row_stride (elements)
+  int64_t num_tokens;
+  int64_t kv_row_stride;
+  const int64_t* slots;   // < 0: token not written
+  const uint16_t* weight; // [512] bf16
+  float eps;
+  uint16_t* out;          // [num_tokens, 512] bf16, row stride out_row_stride (elements)
+  int64_t out_row_stride;
+};
+
 // Each returns the hipError_t of the launch.
 hipError_t launch_ring_rows(const RingArgs& a, hipStream_t stream);
+hipError_t launch_compress_norm_cr1(const NormArgs& a, hipStream_t stream);
 hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream);
 // Slot-order form: inverse[s] = token of slot s or -1 (num_slots int32,
 // 16-byte aligned), then the gather-store over all slots.

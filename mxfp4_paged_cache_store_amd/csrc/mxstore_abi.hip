@@ -294,6 +294,34 @@ int save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64_t r
   return launched(mxs::launch_ring_rows(a, (hipStream_t)stream), "save_ring_rows");
 }
 
+int fused_save_compress_norm_cr1(const float* kv_score, int64_t num_tokens, int64_t width,
+                                 int64_t kv_row_stride, const int64_t* slot_mapping,
+                                 const uint16_t* rms_norm_weight, float rms_norm_eps, uint16_t* latent_out,
+                                 int64_t out_row_stride, void* stream) {
+  if (num_tokens < 0 || num_tokens > (int64_t(1) << 33)) return fail(MX_E_RANGE, "num_tokens must be in [0, 2^33]");
+  if (width != 512) return fail(MX_E_SHAPE, "width must be 512 at compress ratio 1, got %lld", (long long)width);
+  if (!(rms_norm_eps >= 0.0f) || rms_norm_eps > 3.0e38f)
+    return fail(MX_E_ARG, "rms_norm_eps must be finite and >= 0");
+  if (kv_row_stride < width || out_row_stride < width)
+    return fail(MX_E_STRIDE, "row strides must cover a row of 512 values");
+  if (kv_row_stride % 4 || out_row_stride % 4)
+    return fail(MX_E_ALIGN, "row strides must be multiples of 4 elements");
+  if (num_tokens == 0) return ok();
+  if (!kv_score || !slot_mapping || !rms_norm_weight || !latent_out) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(kv_score, 16) || !aligned(rms_norm_weight, 8) || !aligned(latent_out, 8))
+    return fail(MX_E_ALIGN, "kv_score must be 16-byte and weight / latent_out 8-byte aligned");
+  mxs::NormArgs a{};
+  a.kv = kv_score;
+  a.num_tokens = num_tokens;
+  a.kv_row_stride = kv_row_stride;
+  a.slots = slot_mapping;
+  a.weight = rms_norm_weight;
+  a.eps = rms_norm_eps;
+  a.out = latent_out;
+  a.out_row_stride = out_row_stride;
+  return launched(mxs::launch_compress_norm_cr1(a, (hipStream_t)stream), "fused_save_compress_norm_cr1");
+}
+
 const char* mx_last_error(void) { return g_err; }
 
 }  // extern "C"

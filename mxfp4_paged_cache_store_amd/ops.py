@@ -188,6 +188,32 @@ def save_ring_rows(rows: torch.Tensor, slot_mapping: torch.Tensor, state_cache: 
         state_cache.stride(1), _stream(stream)))
 
 
+def fused_save_compress_norm_cr1(kv_score: torch.Tensor, slot_mapping: torch.Tensor,
+                                 rms_norm_weight: torch.Tensor, rms_norm_eps: float,
+                                 latent_out: torch.Tensor, stream=None) -> None:
+    """Compress ratio 1 of [P2 `fused_save_compress_norm`]: RMSNorm of each
+    valid token's fp32 [512] row with the bf16 weight, into bf16
+    ``latent_out`` (rows of tokens with slot < 0 are not written)."""
+    _need_cuda(kv_score, slot_mapping, rms_norm_weight, latent_out)
+    if kv_score.dtype != torch.float32 or kv_score.dim() != 2 or kv_score.stride(1) != 1 \
+            or kv_score.shape[1] != 512:
+        raise ValueError("kv_score must be fp32 [tokens, 512] with unit inner stride")
+    if rms_norm_weight.dtype != torch.bfloat16 or rms_norm_weight.numel() != 512 \
+            or not rms_norm_weight.is_contiguous():
+        raise ValueError("rms_norm_weight must be contiguous bf16 [512]")
+    if latent_out.dtype != torch.bfloat16 or latent_out.dim() != 2 or latent_out.stride(1) != 1 \
+            or latent_out.shape[1] != 512:
+        raise ValueError("latent_out must be bf16 [tokens, 512] with unit inner stride")
+    n = slot_mapping.numel()
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() \
+            or n > kv_score.shape[0] or n > latent_out.shape[0]:
+        raise ValueError("slot_mapping must be contiguous int64 with at most one entry per row")
+    _abi.check(_abi.lib().fused_save_compress_norm_cr1(
+        kv_score.data_ptr(), n, 512, kv_score.stride(0), slot_mapping.data_ptr(),
+        rms_norm_weight.data_ptr(), float(rms_norm_eps), latent_out.data_ptr(), latent_out.stride(0),
+        _stream(stream)))
+
+
 # ------------------------------------------------------------------ page-level API
 
 def resolve_paged_view(cache: torch.Tensor, latent: int, group: int = GROUP_SIZE):

@@ -168,13 +168,13 @@ def large_case_device(tokens: int = LARGE_TOKENS, seed: int = 3, device: str = "
 
 
 def large_sample_host(tokens: int, seed: int = 3) -> tuple[np.ndarray, np.ndarray]:
-    """A host-side batch with the large workload's distribution (uniform in
-    [-4, 4], random-permutation slots over `tokens` flat slots), used to time
-    the CPU oracle on a bounded sample."""
-    rng = np.random.default_rng(seed)
-    src = f32_to_bf16_bits(rng.uniform(-4, 4, size=(tokens, LATENT)).astype(np.float32))
-    slots = rng.permutation(tokens).astype(np.int64)
-    return src, slots
+    """The large workload's recipe drawn on the host (torch's CPU generator;
+    same distribution as the device batch, other values), as numpy arrays
+    (bf16 bits uint16 [T, 512], int64 slots), used to time the CPU oracle."""
+    import torch
+
+    src, slots = large_case_device(tokens, seed, device="cpu")
+    return src.view(torch.int16).numpy().view(np.uint16), slots.numpy()
 
 
 # ------------------------------------------------------------------ config 4

@@ -86,3 +86,43 @@ def f32(x) -> np.float32:
 
 def f32_bits(x: np.float32) -> int:
     return int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_bf16_rounding(got_bits: np.ndarray, exact: np.ndarray, band: float = 2.0 ** -10) -> int:
+    """Check bf16 results against exact (float64) values computed in higher
+    precision.  A result must be the round-to-nearest-even of the exact value,
+    except where the exact value lies within ``band`` bf16 ulps of a midpoint
+    between two bf16 neighbours: there either neighbour is accepted (an fp32
+    computation with relative error e can land on either side when the
+    exact value is within 256 * e ulps of the midpoint).  Zeros must carry
+    the exact value's sign; NaN positions must match.  Returns how many
+    elements fell in the band."""
+    got_bits = np.asarray(got_bits, dtype=np.uint16)
+    exact = np.asarray(exact, dtype=np.float64)
+    assert got_bits.shape == exact.shape
+    got = bf16_bits_to_f64(got_bits)
+    nan = np.isnan(exact)
+    assert (np.isnan(got) == nan).all(), np.argwhere(np.isnan(got) != nan)[:5]
+    e, g, gb = exact[~nan], got[~nan], got_bits[~nan]
+    zero = e == 0
+    want_zero_bits = np.where(np.signbit(e[zero]), 0x8000, 0x0000)
+    assert (gb[zero] == want_zero_bits).all(), "sign of zero"
+    e, g = e[~zero], g[~zero]
+    assert (np.signbit(g) == np.signbit(e)).all(), "sign"
+    a = np.abs(e)
+    _, ex = np.frexp(a)                               # a = m * 2^ex, m in [0.5, 1)
+    qe = np.maximum(ex - 8, -133)                     # bf16 quantum: 8 significant bits, subnormals 2^-133
+    q = np.ldexp(a, -qe)
+    lo = np.floor(q)
+    frac = q - lo
+    rne = np.where((frac > 0.5) | ((frac == 0.5) & (lo % 2 == 1)), lo + 1, lo)
+    gq = np.ldexp(np.abs(g), -qe)
+    near = np.abs(frac - 0.5) <= band
+    ok = (gq == rne) | (near & ((gq == lo) | (gq == lo + 1)))
+    assert ok.all(), [(float(e[i]), float(g[i])) for i in np.flatnonzero(~ok)[:5]]
+    return int(near.sum())

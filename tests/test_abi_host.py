@@ -219,3 +219,32 @@ def test_ring_rows_rejects(mxlib, kw, status):
 
 def test_ring_rows_empty_is_a_noop(mxlib):
     assert ring(mxlib, n=0, rows=0, slots=0, state=0) == _abi.MX_OK
+
+
+def norm(mxlib, **kw):
+    a = dict(kv=FAKE, n=3, width=512, kstride=512, slots=FAKE, w=FAKE, eps=1e-6, out=FAKE,
+             ostride=512)
+    a.update(kw)
+    return mxlib.fused_save_compress_norm_cr1(a["kv"], a["n"], a["width"], a["kstride"], a["slots"],
+                                              a["w"], a["eps"], a["out"], a["ostride"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(width=1024, kstride=1024), _abi.MX_E_SHAPE),
+    (dict(n=-1), _abi.MX_E_RANGE),
+    (dict(eps=-1e-6), _abi.MX_E_ARG),
+    (dict(eps=float("nan")), _abi.MX_E_ARG),
+    (dict(eps=float("inf")), _abi.MX_E_ARG),
+    (dict(kstride=500), _abi.MX_E_STRIDE),
+    (dict(ostride=511), _abi.MX_E_STRIDE),
+    (dict(kstride=514), _abi.MX_E_ALIGN),
+    (dict(kv=FAKE + 8), _abi.MX_E_ALIGN),
+    (dict(out=FAKE + 2), _abi.MX_E_ALIGN),
+    (dict(w=0), _abi.MX_E_NULL),
+])
+def test_compress_norm_rejects(mxlib, kw, status):
+    assert norm(mxlib, **kw) == status
+
+
+def test_compress_norm_empty_is_a_noop(mxlib):
+    assert norm(mxlib, n=0, kv=0, slots=0, w=0, out=0) == _abi.MX_OK

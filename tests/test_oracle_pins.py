@@ -654,3 +654,22 @@ def test_rmsnorm_cr1_closed_forms(orc=oracle):
     eps = 0.25
     y_eps = orc.rmsnorm_cr1(kv[:1], slots[:1], w, eps)
     assert abs(y_eps[0, 0] - 0.75 / np.sqrt(0.75 ** 2 + eps)) < 1e-15
+
+
+def test_bf16_rounding_checker_matches_torch():
+    """The parity checker used for bf16 outputs reproduces torch's fp32 ->
+    bf16 round-to-nearest-even on values exact in fp32 (normal, subnormal,
+    midpoints, signed zeros), and rejects a value one ulp off."""
+    from tests.exact_ref import check_bf16_rounding
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(20000) * np.exp2(rng.uniform(-140, 120, 20000))).astype(np.float32)
+    mids = (rng.integers(0, 2**16, 2000).astype(np.uint32) << 16) | 0x8000   # exact midpoints
+    v = np.concatenate([v, mids.view(np.float32), np.float32([0.0, -0.0, 1e-45, -3e-39])])
+    v = v[np.isfinite(v)]
+    bits = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    check_bf16_rounding(bits, v.astype(np.float64), band=0.0)
+    bad = bits.copy()
+    i = int(np.flatnonzero(np.abs(v) > 1e-30)[0])
+    bad[i] ^= 1
+    with pytest.raises(AssertionError):
+        check_bf16_rounding(bad, v.astype(np.float64), band=0.0)
