@@ -69,10 +69,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_mxfp4_store.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64]
     lib.orc_mxfp4_gather_dequant.restype = ctypes.c_int
     lib.orc_mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
-    for name in ("orc_mxfp8_rope_store", "orc_nvfp4_rope_store"):
+    for name in ("orc_mxfp8_rope_store", "orc_nvfp4_rope_store", "orc_v4_rope_store"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
+    lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+    lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
     lib.orc_rmsnorm_cr1.restype = ctypes.c_int
     lib.orc_rmsnorm_cr1.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _i64]
     lib.orc_save_ring_rows.restype = ctypes.c_int
@@ -219,6 +221,15 @@ class Oracle:
         self._rope_store("orc_nvfp4_rope_store", latent, positions, cos_sin, cache, block,
                          num_blocks, stride, slot_mapping, compress_ratio, sanitize)
 
+    def v4_rope_store(self, latent, positions, cos_sin, cache, block, num_blocks,
+                      slot_mapping, compress_ratio, sanitize=True,
+                      cache_block_stride=None) -> None:
+        stride = block * 584 if cache_block_stride is None else cache_block_stride
+        self._rope_store("orc_v4_rope_store", latent, positions, cos_sin, cache, block,
+                         num_blocks, stride, slot_mapping, compress_ratio, sanitize)
+
+    def f32_to_bf16(self, x: float) -> int:
+        return int(self.lib.orc_f32_to_bf16(float(x)))
 
     def save_ring_rows(self, rows: np.ndarray, slot_mapping: np.ndarray,
                        state: np.ndarray) -> None:
@@ -290,3 +301,5 @@ mxfp8_rope_store = _forward("mxfp8_rope_store")
 nvfp4_rope_store = _forward("nvfp4_rope_store")
 save_ring_rows = _forward("save_ring_rows")
 rmsnorm_cr1 = _forward("rmsnorm_cr1")
+v4_rope_store = _forward("v4_rope_store")
+f32_to_bf16 = _forward("f32_to_bf16")

@@ -507,6 +507,89 @@ int orc_save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64
   return ORC_OK;
 }
 
+/*
+ * fp32 -> bf16, round to nearest, ties to even, by comparing the distances to
+ * the two bf16 neighbours of |x| in double (exact).  NaN -> 0x7FC0 (the
+ * canonical quiet NaN); +-0 and +-Inf keep their sign.  A magnitude at or
+ * above the midpoint between the largest finite bf16 and 2^128 becomes Inf.
+ */
+uint16_t orc_f32_to_bf16(float x) {
+  const uint32_t u = bits_from_f32(x);
+  if (isnan(x)) return 0x7FC0;
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isinf(x) || x == 0.0f) return (uint16_t)(u >> 16);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  const uint16_t lo = (uint16_t)(mag >> 16); /* toward zero */
+  const uint16_t hi = (uint16_t)(lo + 1);    /* next magnitude up (0x7F80 = Inf) */
+  const double a = fabs((double)x);
+  const double vlo = (double)bf16_to_f32(lo);
+  const double vhi = hi == 0x7F80 ? ldexp(1.0, 128) : (double)bf16_to_f32(hi);
+  const double dlo = a - vlo, dhi = vhi - a;
+  uint16_t pick;
+  if (dlo < dhi) pick = lo;
+  else if (dhi < dlo) pick = hi;
+  else pick = (lo & 1u) ? hi : lo;
+  return (uint16_t)(sign | pick);
+}
+
+/*
+ * V4 record insert: the 584-byte paged record of DeepSeek-V4 [P2
+ * `rope_quant_insert`, its description of the record widths: 576 value bytes
+ * followed by eight UE8M0 scale bytes, the last of them zero padding; the V4
+ * kernel's body is not printed].  Readings (parity against the pages
+ * unpinned beyond the layout): the 576 value bytes are the 448 NoPE dims as
+ * E4M3 followed by the 64 rotated RoPE dims as bf16 (448 + 128 = 576); the
+ * seven real scales cover the NoPE dims in groups of 64 (448 / 7) and follow
+ * the MXFP8 kernel's rule on the same page (amax floored at 1e-4, exact
+ * ceil-log2 exponent of fp32(amax / 448), clamp to +-448, byte clamped to
+ * [0, 254 or 255]); the gate, RoPE and sanitising are those of the other two
+ * inserts; the records are segregated as in the other two:
+ *   page = [B x 576 value bytes | B x 8 scale bytes].
+ */
+int orc_v4_rope_store(const uint16_t* latent, const int64_t* positions,
+                      const float* cos_sin, int64_t cos_stride, int64_t cos_rows,
+                      uint8_t* cache, int64_t cache_block_stride, int64_t block,
+                      int64_t num_blocks, const int64_t* slot_mapping,
+                      int64_t num_tokens, int32_t cr, int32_t sanitize) {
+  if (num_tokens < 0 || cr < 1 || block < 1 || num_blocks < 1) return ORC_EINVAL;
+  if (cache_block_stride < block * 584) return ORC_EINVAL;
+  const float floor_amax = 1e-4f;
+  const float inv448 = (float)(1.0 / 448.0);
+  float r[ROPE_LATENT];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (!rope_token(latent + t * ROPE_LATENT, positions[t], cos_sin, cos_stride,
+                    cos_rows, slot, num_blocks, block, cr, sanitize, r))
+      continue;
+    uint8_t* page = cache + (slot / block) * cache_block_stride;
+    uint8_t* values = page + (slot % block) * 576;
+    uint8_t* scales = page + block * 576 + (slot % block) * 8;
+    for (int g = 0; g < 7; ++g) {
+      float amax = 0.0f;
+      for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(r[64 * g + j]));
+      amax = fmaxf(amax, floor_amax);
+      int E = orc_ceil_pow2_exponent(amax * inv448);
+      float mult = ldexpf(1.0f, -E);
+      for (int j = 0; j < 64; ++j) {
+        float y = fminf(fmaxf(r[64 * g + j] * mult, -448.0f), 448.0f);
+        values[64 * g + j] = orc_e4m3_encode(y);
+      }
+      int enc = E + 127;
+      int max_enc = sanitize ? 254 : 255;
+      if (enc < 0) enc = 0;
+      if (enc > max_enc) enc = max_enc;
+      scales[g] = (uint8_t)enc;
+    }
+    scales[7] = 0;
+    for (int d = 448; d < ROPE_LATENT; ++d) {
+      uint16_t h = orc_f32_to_bf16(r[d]);
+      values[448 + 2 * (d - 448)] = (uint8_t)(h & 0xFF);
+      values[448 + 2 * (d - 448) + 1] = (uint8_t)(h >> 8);
+    }
+  }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* Compress-ratio-1 normalisation [P2 `fused_save_compress_norm`]      */
 /* ------------------------------------------------------------------ */

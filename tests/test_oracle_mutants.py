@@ -26,6 +26,8 @@ CHECKS = [
     (pins.test_rope_nan_sanitised, {}),
     (pins.test_save_ring_rows_placement, {}),
     (pins.test_rmsnorm_cr1_closed_forms, {}),
+    (pins.test_f32_to_bf16_matches_torch, {}),
+    (pins.test_v4_record_values_scales_and_pad, {}),
     (pins.test_rope_gate_and_canaries, {}),
     (pins.test_rope_exact_angles_pin_pairing_and_row, {}),
     (pins.test_nvfp4_huge_tiles_saturate, {}),
@@ -77,6 +79,12 @@ MUTANTS = {
     "RMSNorm without eps": ("sqrt(ss / (double)width + (double)eps)", "sqrt(ss / (double)width)"),
     "RMSNorm mean over width-1": ("sqrt(ss / (double)width + (double)eps)", "sqrt(ss / (double)(width - 1) + (double)eps)"),
     "RMSNorm writes invalid tokens": ("    if (slot_mapping[t] < 0) continue;\n    const float* x = kv", "    const float* x = kv"),
+    "bf16 ties away from zero": ("else pick = (lo & 1u) ? hi : lo;", "else pick = hi;"),
+    "V4 groups of 32": ("for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(r[64 * g + j]));",
+                        "for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(r[64 * g + j]));"),
+    "V4 pad scale not zero": ("    scales[7] = 0;\n", "    scales[7] = scales[6];\n"),
+    "V4 RoPE bf16 big-endian": ("values[448 + 2 * (d - 448)] = (uint8_t)(h & 0xFF);",
+                                "values[448 + 2 * (d - 448)] = (uint8_t)(h >> 8); continue;"),
     "NVFP4 sign of -0.0 kept": ("return idx | ((q < 0.0f) ? 8 : 0);", "return idx | ((q < 0.0f || signbit(q)) ? 8 : 0);"),
 }
 

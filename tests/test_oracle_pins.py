@@ -450,11 +450,12 @@ def test_rope_exact_angles_pin_pairing_and_row(orc=oracle):
     latent = np.concatenate([ab, to_bits(b90), ab, to_bits(b180)])
     positions = np.array([43, 83, 63, 83], dtype=np.int64)  # bases 40, 80, 60, 80
     slots = np.arange(4, dtype=np.int64)
-    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288)):
+    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288),
+                      (orc.v4_rope_store, 584)):
         cache = np.full(4 * width, 0xA5, dtype=np.uint8)
         fn(latent, positions, table, cache, 4, 1, slots, 4)
-        vb = 512 if width == 528 else 256
-        sb = 16 if width == 528 else 32
+        vb = {528: 512, 288: 256, 584: 576}[width]
+        sb = width - vb
         vals = cache[: 4 * vb].reshape(4, vb)
         scales = cache[4 * vb:].reshape(4, sb)
         assert (vals[0] == vals[1]).all() and (scales[0] == scales[1]).all()
@@ -469,10 +470,11 @@ def test_rope_gate_and_canaries(orc=oracle):
     positions = np.array([3, 4, 7, 8, 11, 15, 1, 2], dtype=np.int64)
     slots = np.array([0, 1, 2, 3, -1, 5, 6, 7], dtype=np.int64)
     table = _identity_table(16)
-    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288)):
+    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288),
+                      (orc.v4_rope_store, 584)):
         cache = np.full(2 * 4 * width, 0xA5, dtype=np.uint8)
         fn(latent, positions, table, cache, 4, 2, slots, 4)
-        vb = 512 if width == 528 else 256
+        vb = {528: 512, 288: 256, 584: 576}[width]
         sb = width - vb
         written = {0, 2, 5}  # positions 3, 7, 15 with valid slots
         for s in range(8):
@@ -673,3 +675,54 @@ def test_bf16_rounding_checker_matches_torch():
     bad[i] ^= 1
     with pytest.raises(AssertionError):
         check_bf16_rounding(bad, v.astype(np.float64), band=0.0)
+
+
+def test_f32_to_bf16_matches_torch(orc=oracle):
+    """The oracle's fp32 -> bf16 rounding equals torch's (nearest, ties to
+    even) on random values over the whole exponent range, exact midpoints,
+    subnormals, the overflow boundary, signed zeros and infinities; NaN gives
+    0x7FC0."""
+    rng = np.random.default_rng(12)
+    bits = rng.integers(0, 2**32, 3000, dtype=np.uint64).astype(np.uint32)
+    mids = (rng.integers(0, 2**16, 1000).astype(np.uint32) << 16) | 0x8000
+    edge = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7FC000, 0x7F7F8001, 0x00008000, 0x00018000,
+                     0x80000000, 0x00000000, 0x7F800000, 0xFF800000, 0x00000001], dtype=np.uint32)
+    v = np.concatenate([bits, mids, edge]).view(np.float32)
+    v = v[~np.isnan(v)]
+    want = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.f32_to_bf16(x) for x in v], dtype=np.uint16)
+    assert (got == want).all(), [(hex(int(v.view(np.uint32)[i])), hex(got[i]), hex(want[i]))
+                                 for i in np.flatnonzero(got != want)[:5]]
+    assert orc.f32_to_bf16(float("nan")) == 0x7FC0
+
+
+def test_v4_record_values_scales_and_pad(orc=oracle):
+    """V4 record (584 B): group g (64 NoPE dims) anchored at 448 * 2^k_g has
+    scale byte k_g + 127 and values torch-E4M3 of x / 2^k_g; the eighth scale
+    byte is 0; through an identity rotation the RoPE dims come back as the
+    input's bf16 bits (little-endian, after the 448 E4M3 bytes).  A zero
+    latent gives the 1e-4 floor's byte 105 and zero values."""
+    rng = np.random.default_rng(13)
+    ks = [0, -7, 5, -20, 60, -13, 100]   # 448 * 2^k above the 1e-4 floor
+    lat = np.zeros((2, 512), dtype=np.float32)
+    for g, k in enumerate(ks):
+        x = rng.uniform(-0.5, 0.5, 64) * 448.0 * 2.0 ** k
+        x[32 + 4 * g] = 448.0 * 2.0 ** k   # the anchor sits in the group's second half
+        lat[0, 64 * g: 64 * g + 64] = x
+    lat[0, 448:] = rng.standard_normal(64)
+    lb = (lat.view(np.uint32) >> 16).astype(np.uint16)   # truncate: bf16 values
+    lb[1] = 0
+    lf = (lb.astype(np.uint32) << 16).view(np.float32)
+    cache, _ = _run_rope(orc.v4_rope_store, lb, np.array([3, 7], dtype=np.int64),
+                         _identity_table(), np.array([0, 1], dtype=np.int64), width=584)
+    vals = cache[:4 * 576].reshape(4, 576)
+    scales = cache[4 * 576: 4 * 584].reshape(4, 8)
+    assert list(scales[0]) == [k + 127 for k in ks] + [0]
+    for g, k in enumerate(ks):
+        q = torch.from_numpy((lf[0, 64 * g: 64 * g + 64].astype(np.float64) * 2.0 ** -k).astype(np.float32))
+        want = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert (vals[0, 64 * g: 64 * g + 64] == want).all(), g
+    assert (vals[0, 448:].view(np.uint16) == lb[0, 448:]).all()
+    assert list(scales[1]) == [105] * 7 + [0]
+    assert (vals[1] == 0).all()
+    assert (cache[2 * 576: 4 * 576] == 0xA5).all() and (scales[2:] == 0xA5).all()
