@@ -177,7 +177,8 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
     sl = torch.from_numpy(case.slots).cuda()
     written = int(((case.positions + 1) % case.compress_ratio == 0).sum())
     for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
-                            ("nvfp4_rope_store", ops.nvfp4_rope_store, 288)):
+                            ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
+                            ("v4_rope_store", ops.v4_rope_store, 584)):
         kv = torch.zeros((case.num_blocks, case.block, width), dtype=torch.uint8, device="cuda")
         _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, case.compress_ratio), steps, warmup, torch)
         per = ev / steps

@@ -203,6 +203,26 @@ int nvfp4_rope_store(const uint16_t* latent_bf16, const int64_t* positions,
                      void* stream);
 
 /*
+ * V4 RoPE+quant insert, 584-byte record [P2 `rope_quant_insert`: the V4
+ * record is 576 value bytes and eight UE8M0 scale bytes, one of them zero
+ * padding; the kernel body is not printed].  Same gate, rotation and
+ * sanitising as mxfp8_rope_store.  Reading of the record: the 448 NoPE
+ * values as E4M3 in 7 groups of 64 under the MXFP8 scale rule, then the 64
+ * rotated RoPE values as bf16 (nearest-even, little-endian; NaN, possible
+ * only without sanitising, as 0x7FC0).  Page layout:
+ *   [cache_block x 576 value bytes | cache_block x 8 scale bytes],
+ * scale bytes 0..6 for the groups, byte 7 = 0.  cache_block_stride (bytes) is
+ * a multiple of 16 and >= cache_block * 584.
+ */
+int v4_rope_store(const uint16_t* latent_bf16, const int64_t* positions,
+                  const float* cos_sin, int64_t cos_stride, int64_t cos_rows,
+                  uint8_t* cache, int64_t cache_block_stride,
+                  int64_t cache_block, int64_t num_blocks,
+                  const int64_t* slot_mapping, int64_t num_tokens,
+                  int32_t compress_ratio, int32_t sanitize_nans,
+                  void* stream);
+
+/*
  * Ring-state save [P2 `save_ring_rows`; ring rule from the
  * `fused_save_compress_norm` docstring]: for each i < num_rows with
  * s = slot_mapping[i] in [0, num_blocks * capacity), copy the fp32 row

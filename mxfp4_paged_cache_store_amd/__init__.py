@@ -4,7 +4,7 @@ libmxstore.so (hand-written HIP for gfx950, C ABI in include/mxstore.h)
 quantizes a bf16 MLA latent to MXFP4 (E2M1 codes + one E8M0 scale per 32
 values, 272 bytes per 512-wide token) and scatters it into a paged cache; a
 gather-dequant companion unpacks slots back to bf16; two RoPE+quant inserts
-write the MXFP8 (528 B) and NVFP4 (288 B) compressed-cache records; the
+write the MXFP8 (528 B), NVFP4 (288 B) and V4 (584 B) compressed-cache records; the
 ring-state save and the compress-ratio-1 RMSNorm precede those inserts.
 """
 
@@ -13,6 +13,7 @@ from .ops import (
     fused_save_compress_norm_cr1,
     MXFP8_RECORD_BYTES,
     NVFP4_RECORD_BYTES,
+    V4_RECORD_BYTES,
     mxfp4_gather_dequant,
     mxfp4_store,
     mxfp4_build_inverse,
@@ -21,6 +22,7 @@ from .ops import (
     mxfp4_store_by_slot,
     mxfp8_rope_store,
     nvfp4_rope_store,
+    v4_rope_store,
     resolve_paged_view,
     rope_quant_insert,
     row_bytes,
@@ -33,6 +35,7 @@ __all__ = [
     "GROUP_SIZE",
     "MXFP8_RECORD_BYTES",
     "NVFP4_RECORD_BYTES",
+    "V4_RECORD_BYTES",
     "MxError",
     "fused_save_compress_norm_cr1",
     "mxfp4_gather_dequant",
@@ -43,6 +46,7 @@ __all__ = [
     "mxfp4_store_by_slot",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
+    "v4_rope_store",
     "resolve_paged_view",
     "rope_quant_insert",
     "row_bytes",

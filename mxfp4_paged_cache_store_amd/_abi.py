@@ -32,6 +32,7 @@ EXPORTED = (
     "mxfp4_gather_dequant",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
+    "v4_rope_store",
     "save_ring_rows",
     "fused_save_compress_norm_cr1",
     "mx_last_error",
@@ -77,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_store_by_slot.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
         L.mxfp4_gather_dequant.restype = ctypes.c_int
         L.mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp]
-        for name in ("mxfp8_rope_store", "nvfp4_rope_store"):
+        for name in ("mxfp8_rope_store", "nvfp4_rope_store", "v4_rope_store"):
             fn = getattr(L, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp]

@@ -81,5 +81,6 @@ hipError_t launch_mxfp4_store_by_slot(const StoreArgs& a, int latent, const int3
 hipError_t launch_mxfp4_dequant(const DequantArgs& a, int latent, hipStream_t stream);
 hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_v4_rope(const RopeArgs& a, hipStream_t stream);
 
 }  // namespace mxs

@@ -264,6 +264,21 @@ int nvfp4_rope_store(const uint16_t* latent_bf16, const int64_t* positions, cons
   return launched(mxs::launch_nvfp4_rope(a, (hipStream_t)stream), "nvfp4_rope_store");
 }
 
+int v4_rope_store(const uint16_t* latent_bf16, const int64_t* positions, const float* cos_sin,
+                  int64_t cos_stride, int64_t cos_rows, uint8_t* cache,
+                  int64_t cache_block_stride, int64_t cache_block, int64_t num_blocks,
+                  const int64_t* slot_mapping, int64_t num_tokens, int32_t compress_ratio,
+                  int32_t sanitize_nans, void* stream) {
+  mxs::RopeArgs a{};
+  int rc = check_rope(latent_bf16, positions, cos_sin, cos_stride, cos_rows, cache,
+                      cache_block_stride, cache_block, num_blocks, slot_mapping, num_tokens,
+                      compress_ratio, 584, &a);
+  if (rc) return rc;
+  if (num_tokens == 0) return ok();
+  a.sanitize = sanitize_nans ? 1 : 0;
+  return launched(mxs::launch_v4_rope(a, (hipStream_t)stream), "v4_rope_store");
+}
+
 int save_ring_rows(const float* rows, int64_t num_rows, int64_t width, int64_t row_stride,
                    const int64_t* slot_mapping, float* state, int64_t num_blocks, int64_t capacity,
                    int64_t state_stride, int64_t state_row_stride, void* stream) {

@@ -1,6 +1,6 @@
-// rope_insert.hip -- GPT-J RoPE followed by MXFP8 (528-byte) or NVFP4
-// (288-byte) quantization of a 512-wide bf16 latent into a paged compressed
-// KV cache, for gfx950.
+// rope_insert.hip -- GPT-J RoPE followed by MXFP8 (528-byte), NVFP4
+// (288-byte) or V4 (584-byte) quantization of a 512-wide bf16 latent into a
+// paged compressed KV cache, for gfx950.
 //
 // What is computed follows the DeepSeek-V4.1 insert page ("vllm.models.
 // deepseek_v41.common.ops.fused_compress_quant_cache":
@@ -20,12 +20,17 @@
 //   NVFP4  per 16 values: S8 = e4m3(clamp(amax * fl(1/6), 2^-9, 448)),
 //          y = r / S8 correctly rounded, nearest-even E2M1 codes saturating
 //          at 6, sign bit only below zero, NaN (possible only without
-//          sanitising) coded 0.
+//          sanitising) coded 0;
+//   V4     (the page gives the record's widths, not its kernel) the 448 NoPE
+//          values as E4M3 in 7 groups of 64 under the MXFP8 rule, then the 64
+//          rotated RoPE values as bf16 (nearest-even, NaN -> 0x7FC0), then
+//          7 UE8M0 bytes and one zero padding byte in the page's scale area.
 //
 // Layout on CDNA4: one wave per token; lane l holds values 8l..8l+7 (pairs
 // 4l..4l+3), so the RoPE pairs live in lanes 56..63, an MXFP8 group is a DPP
-// quad and an NVFP4 tile a lane pair.  E4M3 and E2M1 conversions use gfx950's
-// v_cvt_scalef32_pk_fp8_f32 / v_cvt_scalef32_pk_fp4_f32 with scale 1.0.
+// quad, a V4 group a half-row of 8 lanes and an NVFP4 tile a lane pair.
+// E4M3 and E2M1 conversions use gfx950's v_cvt_scalef32_pk_fp8_f32 /
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0.
 #include "kernels.hpp"
 
 namespace mxs {
@@ -203,6 +208,68 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void nvfp4_rope_kernel(cons
   }
 }
 
+constexpr int kRowHalfMirror = 0x141;  // lane i reads lane 7-i of its half-row
+
+// fp32 -> bf16, nearest-even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rn(float f) {
+  const uint32_t u = as_u32(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void v4_rope_kernel(const RopeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kTokensPerWave;
+  const float inv448 = (float)(1.0 / 448.0);
+
+  for (int p = 0; p < kTokensPerWave; ++p) {
+    const int64_t t = first + p;
+    if (t >= a.num_tokens) break;
+    float r[8];
+    int64_t page_off;
+    uint32_t in_page;
+    if (!rope_token(a, t, lane, r, page_off, in_page)) continue;
+
+    // Group of 64 = lanes 8g..8g+7 (lanes 56..63, the RoPE dims, form their
+    // own half-row and their scale is not used).
+    float amax = max_abs8(r);
+    amax = fmaxf(amax, as_f32(dpp<kQuadSwap1>(as_u32(amax))));
+    amax = fmaxf(amax, as_f32(dpp<kQuadSwap2>(as_u32(amax))));
+    amax = fmaxf(amax, as_f32(dpp<kRowHalfMirror>(as_u32(amax))));
+    amax = fmaxf(amax, 1e-4f);
+    const uint32_t vb = as_u32(amax * inv448);
+    const int E = (int)((vb >> 23) & 0xFFu) - 127 + ((vb & 0x7FFFFFu) != 0u ? 1 : 0);
+    const float mul = E <= 126 ? as_f32((uint32_t)(127 - E) << 23)
+                               : as_f32(0x00400000u >> (E - 127));
+    int enc = E + 127;
+    enc = max(enc, 0);
+    enc = min(enc, a.sanitize ? 254 : 255);
+
+    uint8_t* page = a.cache + page_off;
+    uint8_t* values = page + (int64_t)in_page * 576;
+    uint8_t* scales = page + (int64_t)a.block * 576 + (int64_t)in_page * 8;
+    if (lane < 56) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(r[i] * mul, -448.0f), 448.0f);
+      const uint32_t lo = e4m3x2(y[0], y[1]) | (e4m3x2(y[2], y[3]) << 16);
+      const uint32_t hi = e4m3x2(y[4], y[5]) | (e4m3x2(y[6], y[7]) << 16);
+      *reinterpret_cast<u32x2*>(values + lane * 8) = u32x2{lo, hi};
+    } else {
+      const u32x4 h = {bf16_rn(r[0]) | (bf16_rn(r[1]) << 16), bf16_rn(r[2]) | (bf16_rn(r[3]) << 16),
+                       bf16_rn(r[4]) | (bf16_rn(r[5]) << 16), bf16_rn(r[6]) | (bf16_rn(r[7]) << 16)};
+      *reinterpret_cast<u32x4*>(values + 448 + (lane - 56) * 16) = h;
+    }
+    uint32_t s[7];
+#pragma unroll
+    for (int g = 0; g < 7; ++g) s[g] = (uint32_t)__builtin_amdgcn_readlane(enc, 8 * g);
+    if (lane == 0)
+      *reinterpret_cast<u32x2*>(scales) =
+          u32x2{s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24), s[4] | (s[5] << 8) | (s[6] << 16)};
+  }
+}
+
 hipError_t launch_rope(void (*kernel)(const RopeArgs), const RopeArgs& a, hipStream_t stream) {
   constexpr int64_t kToksPerBlock = (int64_t)kWavesPerBlock * kTokensPerWave;
   const int64_t blocks = (a.num_tokens + kToksPerBlock - 1) / kToksPerBlock;
@@ -219,6 +286,10 @@ hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream) {
 
 hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream) {
   return launch_rope(nvfp4_rope_kernel, a, stream);
+}
+
+hipError_t launch_v4_rope(const RopeArgs& a, hipStream_t stream) {
+  return launch_rope(v4_rope_kernel, a, stream);
 }
 
 }  // namespace mxs

@@ -20,6 +20,7 @@ from . import _abi
 GROUP_SIZE = 32  # values per E8M0 scale (OCP MX block size)
 MXFP8_RECORD_BYTES = 528  # 512 E4M3 values + 16 UE8M0 scales [P2 `rope_quant_insert`]
 NVFP4_RECORD_BYTES = 288  # 256 bytes of E2M1 pairs + 32 E4M3 scales [P2 `rope_quant_insert`]
+V4_RECORD_BYTES = 584     # 576 value bytes + 8 UE8M0 scales, one of them padding [P2 `rope_quant_insert`]
 
 
 def _stream(stream) -> int:
@@ -168,6 +169,14 @@ def nvfp4_rope_store(latent, positions, cos_sin, kv_cache, slot_mapping, compres
                                            _stream(stream)))
 
 
+def v4_rope_store(latent, positions, cos_sin, kv_cache, slot_mapping, compress_ratio,
+                  sanitize_nans: bool = True, stream=None) -> None:
+    """``v4_rope_store`` of the C ABI; ``kv_cache`` is uint8 [blocks, B, 584]."""
+    args = _rope_args(latent, positions, cos_sin, kv_cache, slot_mapping, V4_RECORD_BYTES)
+    _abi.check(_abi.lib().v4_rope_store(*args, int(compress_ratio), int(bool(sanitize_nans)),
+                                        _stream(stream)))
+
+
 def save_ring_rows(rows: torch.Tensor, slot_mapping: torch.Tensor, state_cache: torch.Tensor,
                    stream=None) -> None:
     """Store fp32 [kv, score] rows to their ring slots, skipping slot -1
@@ -266,11 +275,13 @@ def rope_quant_insert(latent, positions, cos_sin_cache, kv_cache, slot_mapping,
                       compress_ratio: int, sanitize_nans: bool = True, stream=None) -> None:
     """GPT-J RoPE + quantized insert into a paged compressed cache whose
     record width selects the format [P2 `rope_quant_insert`]: 528 -> MXFP8,
-    288 -> NVFP4.  Other widths (the 584-byte V4 record, bf16/fp8 plain rows)
-    are not provided by this library."""
+    288 -> NVFP4, 584 -> V4.  The plain bf16/fp8 rows of the page are not
+    provided by this library."""
     width = kv_cache.shape[-1] if kv_cache.dim() == 3 else None
-    if kv_cache.dtype != torch.uint8 or width not in (MXFP8_RECORD_BYTES, NVFP4_RECORD_BYTES):
+    fns = {MXFP8_RECORD_BYTES: mxfp8_rope_store, NVFP4_RECORD_BYTES: nvfp4_rope_store,
+           V4_RECORD_BYTES: v4_rope_store}
+    if kv_cache.dtype != torch.uint8 or width not in fns:
         raise ValueError(f"unsupported paged KV record: dtype {kv_cache.dtype}, width {width}")
-    fn = mxfp8_rope_store if width == MXFP8_RECORD_BYTES else nvfp4_rope_store
+    fn = fns[width]
     fn(latent, positions, cos_sin_cache, kv_cache, slot_mapping, compress_ratio,
        sanitize_nans, stream)

@@ -110,7 +110,8 @@ def rope(mxlib, fn, **kw):
                               a["san"], None)
 
 
-@pytest.mark.parametrize("fn,width", [("mxfp8_rope_store", 528), ("nvfp4_rope_store", 288)])
+@pytest.mark.parametrize("fn,width", [("mxfp8_rope_store", 528), ("nvfp4_rope_store", 288),
+                                      ("v4_rope_store", 584)])
 @pytest.mark.parametrize("kw,status", [
     (dict(cr=0), _abi.MX_E_ARG),
     (dict(pstride=100), _abi.MX_E_STRIDE),
@@ -126,14 +127,15 @@ def test_rope_rejects(mxlib, fn, width, kw, status):
     assert rope(mxlib, fn, **kw) == status
 
 
-@pytest.mark.parametrize("fn", ["mxfp8_rope_store", "nvfp4_rope_store"])
+@pytest.mark.parametrize("fn", ["mxfp8_rope_store", "nvfp4_rope_store", "v4_rope_store"])
 def test_rope_empty_is_a_noop(mxlib, fn):
-    assert rope(mxlib, fn, n=0, latent=0, pos=0, cs=0, cache=0, slots=0) == _abi.MX_OK
+    assert rope(mxlib, fn, n=0, latent=0, pos=0, cs=0, cache=0, slots=0, pstride=64 * 592) == _abi.MX_OK
 
 
 def test_nvfp4_record_width_checked(mxlib):
     # a 288-byte page stride is too small for the 528-byte record
     assert rope(mxlib, "mxfp8_rope_store", pstride=64 * 288) == _abi.MX_E_STRIDE
+    assert rope(mxlib, "v4_rope_store", pstride=64 * 528) == _abi.MX_E_STRIDE
 
 
 def test_inverse_bytes_and_advice(mxlib):

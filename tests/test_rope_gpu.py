@@ -1,4 +1,4 @@
-"""GPU parity of the MXFP8 / NVFP4 RoPE+quant inserts against the oracle:
+"""GPU parity of the MXFP8 / NVFP4 / V4 RoPE+quant inserts against the oracle:
 every byte of the paged compressed cache, canaries included."""
 
 import numpy as np
@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 VARIANTS = {
     "mxfp8": (ops.mxfp8_rope_store, oracle.mxfp8_rope_store, 528),
     "nvfp4": (ops.nvfp4_rope_store, oracle.nvfp4_rope_store, 288),
+    "v4": (ops.v4_rope_store, oracle.v4_rope_store, 584),
 }
 
 
@@ -32,7 +33,7 @@ def run_both(device, variant, latent, positions, table, slots, block, num_blocks
     return got, host
 
 
-@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
 def test_rope_insert_workload(device, variant):
     """16384 tokens, positions in [0, 65536), compress ratio 4, cache block
     64: only tokens with (pos + 1) % 4 == 0 are written."""
@@ -43,7 +44,7 @@ def test_rope_insert_workload(device, variant):
     assert (got == want).all(), first_mismatch(got, want)
 
 
-@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
 @pytest.mark.parametrize("cr", [1, 2, 3])
 def test_rope_ratios_extremes(device, variant, cr):
     """Compress ratios 1..3, a non-power-of-two block, wide value ranges
@@ -76,13 +77,13 @@ def test_rope_ratios_extremes(device, variant, cr):
     assert (got == want).all(), first_mismatch(got, want)
 
 
-@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
 def test_rope_exponent_sweep(device, variant):
     """Every positive finite bf16 value as the only nonzero in its group or
     tile, positive and negative, through the real table."""
     pats = np.arange(1, 0x7F80, dtype=np.uint16)
     pats = np.concatenate([pats, pats | 0x8000])
-    per = 16 if variant == "mxfp8" else 32
+    per = {"mxfp8": 16, "nvfp4": 32, "v4": 8}[variant]
     step = 512 // per
     n = -(-pats.size // per)
     latent = np.zeros((n, 512), dtype=np.uint16)
@@ -100,7 +101,7 @@ def test_rope_exponent_sweep(device, variant):
 
 def test_rope_quant_insert_dispatch(device):
     case = workloads.rope_case(tokens=1024)
-    for width, variant in ((528, "mxfp8"), (288, "nvfp4")):
+    for width, variant in ((528, "mxfp8"), (288, "nvfp4"), (584, "v4")):
         kv = torch.full((16, 64, width), 0xA5, dtype=torch.uint8, device=device)
         ops.rope_quant_insert(bf16_dev(case.latent, device), i64_dev(case.positions, device),
                               torch.from_numpy(case.cos_sin).to(device), kv,
@@ -112,11 +113,11 @@ def test_rope_quant_insert_dispatch(device):
     with pytest.raises(ValueError):
         ops.rope_quant_insert(bf16_dev(case.latent, device), i64_dev(case.positions, device),
                               torch.from_numpy(case.cos_sin).to(device),
-                              torch.zeros((4, 64, 584), dtype=torch.uint8, device=device),
+                              torch.zeros((4, 64, 600), dtype=torch.uint8, device=device),
                               i64_dev(case.slots, device), 4)
 
 
-@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
 def test_rope_without_sanitising(device, variant):
     """sanitize_nans = 0: NaN reaches the quantizer (MXFP8 scale bytes may
     reach 255); both sides follow the same IEEE max/clamp rules."""
