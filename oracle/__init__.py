@@ -73,6 +73,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
+    lib.orc_sparse_mla_attention.restype = ctypes.c_int
+    lib.orc_sparse_mla_attention.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
+                                             ctypes.c_double, _vp, _vp]
     lib.orc_f32_to_bf16.restype = ctypes.c_uint16
     lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
     lib.orc_rmsnorm_cr1.restype = ctypes.c_int
@@ -228,6 +231,27 @@ class Oracle:
         self._rope_store("orc_v4_rope_store", latent, positions, cos_sin, cache, block,
                          num_blocks, stride, slot_mapping, compress_ratio, sanitize)
 
+    def sparse_mla_attention(self, q_bits: np.ndarray, cache: np.ndarray, num_blocks: int,
+                             block_size: int, block_stride_rows: int, indices: np.ndarray,
+                             scale: float, sink: np.ndarray | None = None) -> np.ndarray:
+        """Attention of bf16 queries ``q_bits`` [T, H, latent] (uint16 bit
+        patterns) over the listed slots ``indices`` (int32 [T, topk]) of an
+        MXFP4 cache; returns float64 [T, H, latent]."""
+        q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        assert q.ndim == 3
+        idx = np.ascontiguousarray(indices, dtype=np.int32)
+        assert idx.ndim == 2 and idx.shape[0] == q.shape[0]
+        t, h, latent = q.shape
+        out = np.zeros((t, h, latent), dtype=np.float64)
+        s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        assert s is None or s.size == h
+        rc = self.lib.orc_sparse_mla_attention(
+            _ptr(q), t, h, latent, _ptr(np.ascontiguousarray(cache)), num_blocks, block_size,
+            block_stride_rows, _ptr(idx), idx.shape[1], float(scale),
+            None if s is None else _ptr(s), _ptr(out))
+        _check(rc, "sparse_mla_attention")
+        return out
+
     def f32_to_bf16(self, x: float) -> int:
         return int(self.lib.orc_f32_to_bf16(float(x)))
 
@@ -303,3 +327,4 @@ save_ring_rows = _forward("save_ring_rows")
 rmsnorm_cr1 = _forward("rmsnorm_cr1")
 v4_rope_store = _forward("v4_rope_store")
 f32_to_bf16 = _forward("f32_to_bf16")
+sparse_mla_attention = _forward("sparse_mla_attention")

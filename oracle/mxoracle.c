@@ -37,6 +37,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
@@ -326,6 +327,83 @@ int orc_mxfp4_gather_dequant(const uint8_t* cache, int64_t num_blocks,
       o[d] = orc_mxfp4_dequant_bf16(code, row[latent / 2 + d / 32]);
     }
   }
+  return ORC_OK;
+}
+
+/*
+ * Sparse MLA attention over the MXFP4 cache, the read side of the format [P3:
+ * Claims -- attention over the packed cache equals attention over the same
+ * values dequantized to bf16; Details, read path -- the ragged sparse kernel
+ * unpacks each gathered tile once and feeds both products].  Rope-free MLA
+ * in its absorbed form: keys and values are both the cached latent row.  For
+ * query token t and head h, over the listed slots j = indices[t, 0..topk)
+ * that are valid (>= 0 and inside the cache; others are skipped, as pads are
+ * by the store):
+ *   s_j = scale * sum_d q[t, h, d] * v_j[d]         (v_j: the row as bf16)
+ *   m   = max(max_j s_j, sink[h] when given)
+ *   out[t, h, :] = sum_j e^(s_j - m) v_j / (sum_j e^(s_j - m) + e^(sink[h] - m))
+ * (the sink term only when sinks are given); no valid slot gives zeros.  A
+ * slot listed twice counts twice.  Computed in double from the bf16 query
+ * and the bf16 dequantized rows (finite inputs assumed).
+ */
+int orc_sparse_mla_attention(const uint16_t* q, int64_t num_tokens, int64_t num_heads,
+                             int64_t latent, const uint8_t* cache, int64_t num_blocks,
+                             int64_t block_size, int64_t block_stride_rows,
+                             const int32_t* indices, int64_t topk, double scale,
+                             const float* sink, double* out) {
+  const int64_t pitch = orc_row_bytes(latent, 32);
+  if (pitch <= 0 || num_tokens < 0 || num_heads < 1 || topk < 0) return ORC_EINVAL;
+  if (num_blocks < 1 || block_size < 1 || block_stride_rows < block_size) return ORC_EINVAL;
+  double* v = (double*)malloc((size_t)(topk > 0 ? topk : 1) * (size_t)latent * sizeof(double));
+  double* sc = (double*)malloc((size_t)(topk > 0 ? topk : 1) * sizeof(double));
+  int* ok = (int*)malloc((size_t)(topk > 0 ? topk : 1) * sizeof(int));
+  if (!v || !sc || !ok) {
+    free(v);
+    free(sc);
+    free(ok);
+    return ORC_EINVAL;
+  }
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    for (int64_t j = 0; j < topk; ++j) {
+      int64_t r = slot_row((int64_t)indices[t * topk + j], num_blocks, block_size, block_stride_rows);
+      ok[j] = r >= 0;
+      if (!ok[j]) continue;
+      const uint8_t* row = cache + r * pitch;
+      for (int64_t d = 0; d < latent; ++d) {
+        int byte = row[d / 2];
+        int code = (d % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        v[j * latent + d] = (double)bf16_to_f32(orc_mxfp4_dequant_bf16(code, row[latent / 2 + d / 32]));
+      }
+    }
+    for (int64_t h = 0; h < num_heads; ++h) {
+      const uint16_t* qh = q + (t * num_heads + h) * latent;
+      double* o = out + (t * num_heads + h) * latent;
+      double m = -INFINITY;
+      int any = 0;
+      for (int64_t j = 0; j < topk; ++j) {
+        if (!ok[j]) continue;
+        double dot = 0.0;
+        for (int64_t d = 0; d < latent; ++d) dot += (double)bf16_to_f32(qh[d]) * v[j * latent + d];
+        sc[j] = scale * dot;
+        if (sc[j] > m) m = sc[j];
+        any = 1;
+      }
+      for (int64_t d = 0; d < latent; ++d) o[d] = 0.0;
+      if (!any) continue;
+      if (sink && (double)sink[h] > m) m = (double)sink[h];
+      double den = sink ? exp((double)sink[h] - m) : 0.0;
+      for (int64_t j = 0; j < topk; ++j) {
+        if (!ok[j]) continue;
+        double w = exp(sc[j] - m);
+        den += w;
+        for (int64_t d = 0; d < latent; ++d) o[d] += w * v[j * latent + d];
+      }
+      for (int64_t d = 0; d < latent; ++d) o[d] /= den;
+    }
+  }
+  free(v);
+  free(sc);
+  free(ok);
   return ORC_OK;
 }
 

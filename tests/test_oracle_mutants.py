@@ -28,6 +28,10 @@ CHECKS = [
     (pins.test_rmsnorm_cr1_closed_forms, {}),
     (pins.test_f32_to_bf16_matches_torch, {}),
     (pins.test_v4_record_values_scales_and_pad, {}),
+    (pins.test_attention_single_key_pads_and_sink, {}),
+    (pins.test_attention_uniform_when_query_is_zero, {}),
+    (pins.test_attention_temperature, {}),
+    (pins.test_attention_hard_limit_and_order, {}),
     (pins.test_rope_gate_and_canaries, {}),
     (pins.test_rope_exact_angles_pin_pairing_and_row, {}),
     (pins.test_nvfp4_huge_tiles_saturate, {}),
@@ -85,6 +89,14 @@ MUTANTS = {
     "V4 pad scale not zero": ("    scales[7] = 0;\n", "    scales[7] = scales[6];\n"),
     "V4 RoPE bf16 big-endian": ("values[448 + 2 * (d - 448)] = (uint8_t)(h & 0xFF);",
                                 "values[448 + 2 * (d - 448)] = (uint8_t)(h >> 8); continue;"),
+    "attention without scale": ("sc[j] = scale * dot;", "sc[j] = dot; (void)scale;"),
+    "attention sink ignored": ("double den = sink ? exp((double)sink[h] - m) : 0.0;", "double den = 0.0;"),
+    "attention without max shift": ("double w = exp(sc[j] - m);", "double w = exp(sc[j]);"),
+    "attention normalised by count": ("for (int64_t d = 0; d < latent; ++d) o[d] /= den;",
+                                      "for (int64_t d = 0; d < latent; ++d) o[d] /= (double)topk;"),
+    "attention scores negated": ("sc[j] = scale * dot;", "sc[j] = -scale * dot;"),
+    "attention query of head 0": ("const uint16_t* qh = q + (t * num_heads + h) * latent;",
+                                  "const uint16_t* qh = q + (t * num_heads) * latent;"),
     "NVFP4 sign of -0.0 kept": ("return idx | ((q < 0.0f) ? 8 : 0);", "return idx | ((q < 0.0f || signbit(q)) ? 8 : 0);"),
 }
 

@@ -726,3 +726,92 @@ def test_v4_record_values_scales_and_pad(orc=oracle):
     assert list(scales[1]) == [105] * 7 + [0]
     assert (vals[1] == 0).all()
     assert (cache[2 * 576: 4 * 576] == 0xA5).all() and (scales[2:] == 0xA5).all()
+
+
+# ---------------------------------------------------------------- attention (read side)
+
+def _attn_cache(rows_f32: np.ndarray, orc=oracle):
+    """Store fp32 rows (rounded to bf16) as an MXFP4 flat cache; return the
+    cache and the rows' dequantized values (the pinned store and dequant)."""
+    n = rows_f32.shape[0]
+    bits = (np.ascontiguousarray(rows_f32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    cache = np.zeros(n * 272, dtype=np.uint8)
+    orc.mxfp4_store(bits, np.arange(n, dtype=np.int64), cache, 1, n, n)
+    deq = orc.mxfp4_gather_dequant(cache, 1, n, n, 512, np.arange(n, dtype=np.int64))
+    return cache, (deq.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_attention_single_key_pads_and_sink(orc=oracle):
+    """[P3 read path] One valid key among pads (-1, a negative, a slot past
+    the cache) returns that row exactly for any query; no valid key returns
+    zeros; with q = 0 the score is 0, so a sink of 0 halves the row, a sink
+    of -inf changes nothing and a huge sink drives the output to 0."""
+    rng = np.random.default_rng(40)
+    cache, v = _attn_cache(rng.standard_normal((8, 512)).astype(np.float32), orc)
+    q = _bf16_bits(rng.standard_normal((4, 2, 512)))
+    q[2:] = 0
+    idx = np.array([[5, -1, 99999, -7], [-1, -1, 8, -3], [5, -1, -1, -1], [5, -1, -1, -1]],
+                   dtype=np.int32)
+    out = orc.sparse_mla_attention(q, cache, 1, 8, 8, idx, 0.04)
+    assert (out[0] == v[5]).all() and (out[1] == 0).all() and (out[2] == v[5]).all()
+    out = orc.sparse_mla_attention(q, cache, 1, 8, 8, idx, 0.04,
+                                   sink=np.array([0.0, -np.inf], dtype=np.float32))
+    assert (out[2, 0] == v[5] / 2).all() and (out[2, 1] == v[5]).all()
+    out = orc.sparse_mla_attention(q, cache, 1, 8, 8, idx, 0.04,
+                                   sink=np.array([1e4, 1e4], dtype=np.float32))
+    assert np.abs(out[2:]).max() < 1e-300 and (out[0] == v[5] * 0).all()
+
+
+def test_attention_uniform_when_query_is_zero(orc=oracle):
+    """q = 0 gives equal weights: the mean of the listed valid rows, a row
+    listed twice counting twice."""
+    rng = np.random.default_rng(41)
+    cache, v = _attn_cache(rng.standard_normal((6, 512)).astype(np.float32), orc)
+    q = np.zeros((2, 3, 512), dtype=np.uint16)
+    idx = np.array([[0, 1, 2, 3, -1], [4, 4, 1, -1, -1]], dtype=np.int32)
+    out = orc.sparse_mla_attention(q, cache, 1, 6, 6, idx, 1.0)
+    assert np.allclose(out[0], v[:4].mean(axis=0), rtol=1e-14, atol=1e-300)
+    assert np.allclose(out[1], (2 * v[4] + v[1]) / 3, rtol=1e-14, atol=1e-300)
+
+
+def test_attention_temperature(orc=oracle):
+    """Rows 0 (zeros) and 1 (one-hot 1.0) with a one-hot query give scores 0
+    and `scale`; scale = ln 3 weighs them 1 : 3, so output dim 0 is 3/4."""
+    rows = np.zeros((2, 512), dtype=np.float32)
+    rows[1, 0] = 1.0
+    cache, v = _attn_cache(rows, orc)
+    assert v[1, 0] == 1.0 and (v[1, 1:] == 0).all() and (v[0] == 0).all()
+    q = np.zeros((1, 1, 512), dtype=np.float32)
+    q[0, 0, 0] = 1.0
+    out = orc.sparse_mla_attention(_bf16_bits(q), cache, 1, 2, 2,
+                                   np.array([[0, 1]], dtype=np.int32), np.log(3.0))
+    assert abs(out[0, 0, 0] - 0.75) < 1e-15 and (out[0, 0, 1:] == 0).all()
+
+
+def test_attention_hard_limit_and_order(orc=oracle):
+    """A very large scale turns softmax into argmax: the output is the row
+    with the largest exact dot product (found by brute force); listing the
+    slots in another order gives the same output."""
+    rng = np.random.default_rng(42)
+    cache, v = _attn_cache(rng.standard_normal((32, 512)).astype(np.float32), orc)
+    qf = rng.standard_normal((3, 2, 512)).astype(np.float32)
+    q = _bf16_bits(qf)
+    qd = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    idx = np.stack([rng.permutation(32)[:20] for _ in range(3)]).astype(np.int32)
+    for t in range(3):
+        for h in range(2):
+            dots = sorted(((float(qd[t, h] @ v[j]), j) for j in idx[t]), reverse=True)
+            assert dots[0][0] - dots[1][0] > 1e-3
+    out = orc.sparse_mla_attention(q, cache, 1, 32, 32, idx, 1e6)
+    for t in range(3):
+        for h in range(2):
+            best = max(idx[t], key=lambda j: float(qd[t, h] @ v[j]))
+            assert np.allclose(out[t, h], v[best], rtol=0, atol=1e-12)
+    out1 = orc.sparse_mla_attention(q, cache, 1, 32, 32, idx, 0.05)
+    out2 = orc.sparse_mla_attention(q, cache, 1, 32, 32, idx[:, ::-1].copy(), 0.05)
+    assert np.allclose(out1, out2, rtol=0, atol=1e-12)   # values are O(1)
+    assert not np.allclose(out1[0, 0], out1[0, 1])   # heads see their own queries
