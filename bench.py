@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 BYTES_PER_TOKEN = 1024 + 272 + 8  # latent read + row written + slot read
 BYTES_PER_PAD = 8
 # The slot-order store reads one int32 inverse entry per slot instead of the
@@ -169,6 +170,23 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
         "frac_hbm_peak": round(n_norm * (2048 + 1024 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
     }
     del kv, norm_slots, w, latent_out
+    # sparse MLA attention over the packed cache: the last 4,096 queries of a
+    # 16,384-token prefill, 32 heads, top-2048 causal slots
+    q, acache, aidx, ascale = workloads.attention_workload_device()
+    aout = torch.empty_like(q)
+    _, ev = time_launches(lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout),
+                          max(3, steps // 3), warmup, torch)
+    per = ev / max(3, steps // 3)
+    valid = int((aidx >= 0).sum())
+    flops = 4.0 * q.shape[1] * 512 * valid
+    out["sparse_mla_attention"] = {
+        "workload": f"{q.shape[0]} queries x {q.shape[1]} heads, top-{aidx.shape[1]} of a "
+                    f"{acache.shape[0]}-token MXFP4 cache ({valid} valid slot reads)",
+        "us_per_launch": round(per * 1e6, 2),
+        "TFLOPs": round(flops / per / 1e12, 1),
+        "frac_bf16_mfma_peak": round(flops / per / 1e12 / BF16_PEAK_TFLOPS, 4),
+    }
+    del q, acache, aidx, aout
     # RoPE inserts on the 16384-token, compress-ratio-4 workload
     case = workloads.rope_case()
     lat = torch.from_numpy(case.latent.view("int16")).cuda().view(torch.bfloat16)

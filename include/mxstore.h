@@ -270,6 +270,42 @@ int fused_save_compress_norm_cr1(const float* kv_score, int64_t num_tokens, int6
                                  const uint16_t* rms_norm_weight, float rms_norm_eps,
                                  uint16_t* latent_out, int64_t out_row_stride, void* stream);
 
+/*
+ * Sparse MLA attention over the MXFP4 cache -- the read side of the format
+ * [P3: Claims -- attention over the packed cache equals attention over the
+ * same values dequantized to bf16; Details, read path -- the ragged sparse
+ * kernel unpacks each gathered tile once and feeds both products].  Rope-free
+ * MLA in absorbed form: keys and values are both the cached 512-wide latent.
+ * For each query token t and head h, over the listed slots
+ * s = indices[t * indices_stride + j], j < topk, that are valid (0 <= s <
+ * num_blocks * block_size; others are skipped):
+ *   score_j = scale * dot(q[t, h, :], v_s)            (v_s: the row as bf16)
+ *   out[t, h, :] = sum_j e^(score_j - m) v_s / (sum_j e^(score_j - m)
+ *                                                + e^(sink[h] - m))
+ * with m the running maximum and the sink term only when `sink` is given
+ * (natural-log logits, one per head).  A token with no valid slot gets zeros.
+ * Scores accumulate in fp32 on bf16 MFMAs; the softmax runs in base 2 in
+ * fp32; the weights are rounded to bf16 for the weighted sum (fp32
+ * accumulate); the result is rounded to bf16.
+ *
+ * q_bf16        bf16 [num_tokens, num_heads, 512]; strides in elements,
+ *               multiples of 8; 16-byte aligned.
+ * cache         the paged MXFP4 cache as for mxfp4_store (latent 512, 272-byte
+ *               rows, fewer than 2^31 slots); 16-byte aligned.
+ * indices       int32 [num_tokens, indices_stride >= topk]; may be null when
+ *               topk is 0 (every output is then zero).
+ * num_heads     a multiple of 16 in [16, 1024].
+ * scale         finite softmax scale (e.g. 1/sqrt(qk head dim)).
+ * out_bf16      bf16 [num_tokens, num_heads, 512]; strides in elements.
+ */
+int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads,
+                         int64_t latent, int64_t q_token_stride, int64_t q_head_stride,
+                         const uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                         int64_t block_stride_rows, const int32_t* indices, int64_t topk,
+                         int64_t indices_stride, float scale, const float* sink,
+                         uint16_t* out_bf16, int64_t out_token_stride, int64_t out_head_stride,
+                         void* stream);
+
 /* Message for the last nonzero status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
 const char* mx_last_error(void);

@@ -5,7 +5,8 @@ quantizes a bf16 MLA latent to MXFP4 (E2M1 codes + one E8M0 scale per 32
 values, 272 bytes per 512-wide token) and scatters it into a paged cache; a
 gather-dequant companion unpacks slots back to bf16; two RoPE+quant inserts
 write the MXFP8 (528 B), NVFP4 (288 B) and V4 (584 B) compressed-cache records; the
-ring-state save and the compress-ratio-1 RMSNorm precede those inserts.
+ring-state save and the compress-ratio-1 RMSNorm precede those inserts; a
+sparse MLA attention reads the packed cache directly (MFMA).
 """
 
 from .ops import (
@@ -27,6 +28,7 @@ from .ops import (
     rope_quant_insert,
     row_bytes,
     save_ring_rows,
+    sparse_mla_attention,
     store_mxfp4_mla,
 )
 from ._abi import MxError
@@ -51,5 +53,6 @@ __all__ = [
     "rope_quant_insert",
     "row_bytes",
     "save_ring_rows",
+    "sparse_mla_attention",
     "store_mxfp4_mla",
 ]

@@ -35,6 +35,7 @@ EXPORTED = (
     "v4_rope_store",
     "save_ring_rows",
     "fused_save_compress_norm_cr1",
+    "sparse_mla_attention",
     "mx_last_error",
 )
 
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.fused_save_compress_norm_cr1.restype = ctypes.c_int
         L.fused_save_compress_norm_cr1.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_float,
                                                    _vp, _i64, _vp]
+        L.sparse_mla_attention.restype = ctypes.c_int
+        L.sparse_mla_attention.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                           _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _i64, _i64, _vp]
         L.mx_last_error.restype = ctypes.c_char_p
         L.mx_last_error.argtypes = []
         _lib = L

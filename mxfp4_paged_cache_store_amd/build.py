@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(BUILD_DIR, "libmxstore.so")
 INCLUDE_DIR = os.path.join(ROOT_DIR, "include")
 
 SOURCES = ["mxstore_abi.hip", "mxfp4_store.hip", "mxfp4_dequant.hip", "rope_insert.hip",
-           "ring_rows.hip", "compress_norm.hip"]
+           "ring_rows.hip", "compress_norm.hip", "sparse_attn.hip"]
 
 # -ffp-contract=off: every multiply and add rounds once (the RoPE arithmetic
 #   and the x*2^-e + 0.0 sign fix-up depend on it).

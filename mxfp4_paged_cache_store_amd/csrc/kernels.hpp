@@ -68,9 +68,28 @@ struct NormArgs {
   int64_t out_row_stride;
 };
 
+struct AttnArgs {
+  const uint16_t* q;          // bf16 [num_tokens, num_heads, 512] (strides in elements)
+  int64_t q_token_stride;
+  int64_t q_head_stride;
+  const uint8_t* cache;       // MXFP4 rows of 272 bytes
+  SlotMap map;
+  const int32_t* indices;     // [num_tokens, topk], row stride idx_stride
+  int64_t topk;
+  int64_t idx_stride;
+  float c;                    // softmax scale * log2(e)
+  const float* sink;          // [num_heads] natural-log logits, or null
+  uint16_t* out;              // bf16 [num_tokens, num_heads, 512]
+  int64_t out_token_stride;
+  int64_t out_head_stride;
+  int32_t num_heads;          // multiple of 16
+  int64_t num_tokens;
+};
+
 // Each returns the hipError_t of the launch.
 hipError_t launch_ring_rows(const RingArgs& a, hipStream_t stream);
 hipError_t launch_compress_norm_cr1(const NormArgs& a, hipStream_t stream);
+hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream);
 // Slot-order form: inverse[s] = token of slot s or -1 (num_slots int32,
 // 16-byte aligned), then the gather-store over all slots.

@@ -337,6 +337,49 @@ int fused_save_compress_norm_cr1(const float* kv_score, int64_t num_tokens, int6
   return launched(mxs::launch_compress_norm_cr1(a, (hipStream_t)stream), "fused_save_compress_norm_cr1");
 }
 
+int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads, int64_t latent,
+                         int64_t q_token_stride, int64_t q_head_stride, const uint8_t* cache,
+                         int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
+                         const int32_t* indices, int64_t topk, int64_t indices_stride, float scale,
+                         const float* sink, uint16_t* out_bf16, int64_t out_token_stride,
+                         int64_t out_head_stride, void* stream) {
+  mxs::AttnArgs a{};
+  if (latent != 512) return fail(MX_E_SHAPE, "latent must be 512, got %lld", (long long)latent);
+  int rc = check_paged(latent, 32, num_blocks, block_size, block_stride_rows, &a.map);
+  if (rc) return rc;
+  if (num_blocks * block_size > 0x7FFFFFFF) return fail(MX_E_RANGE, "the cache must hold fewer than 2^31 slots (int32 indices)");
+  if (num_tokens < 0 || num_tokens > 0x7FFFFFFF) return fail(MX_E_RANGE, "num_tokens must be in [0, 2^31)");
+  if (num_heads < 16 || num_heads > 1024 || num_heads % 16)
+    return fail(MX_E_SHAPE, "num_heads must be a multiple of 16 in [16, 1024], got %lld", (long long)num_heads);
+  if (topk < 0 || topk > (int64_t(1) << 24)) return fail(MX_E_RANGE, "topk must be in [0, 2^24]");
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(MX_E_ARG, "scale must be finite");
+  if (q_head_stride < latent || q_token_stride < num_heads * q_head_stride || out_head_stride < latent ||
+      out_token_stride < num_heads * out_head_stride || indices_stride < topk)
+    return fail(MX_E_STRIDE, "strides must cover a head row, a token's heads and a token's topk indices");
+  if (q_head_stride % 8 || q_token_stride % 8)
+    return fail(MX_E_ALIGN, "query strides must be multiples of 8 elements (16-byte rows)");
+  if (num_tokens == 0) return ok();
+  if (!q_bf16 || !cache || (!indices && topk > 0) || !out_bf16) return fail(MX_E_NULL, "null device pointer");
+  if (!aligned(q_bf16, 16) || !aligned(cache, 16) || !aligned(indices, 4) || !aligned(out_bf16, 2) ||
+      (sink && !aligned(sink, 4)))
+    return fail(MX_E_ALIGN, "q and cache must be 16-byte aligned, indices and sink 4-byte, out 2-byte");
+  a.q = q_bf16;
+  a.q_token_stride = q_token_stride;
+  a.q_head_stride = q_head_stride;
+  a.cache = cache;
+  a.indices = indices;
+  a.topk = topk;
+  a.idx_stride = indices_stride;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  a.sink = sink;
+  a.out = out_bf16;
+  a.out_token_stride = out_token_stride;
+  a.out_head_stride = out_head_stride;
+  a.num_heads = (int32_t)num_heads;
+  a.num_tokens = num_tokens;
+  return launched(mxs::launch_sparse_mla_attn(a, (hipStream_t)stream), "sparse_mla_attention");
+}
+
 const char* mx_last_error(void) { return g_err; }
 
 }  // extern "C"

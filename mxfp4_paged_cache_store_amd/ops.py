@@ -223,6 +223,36 @@ def fused_save_compress_norm_cr1(kv_score: torch.Tensor, slot_mapping: torch.Ten
         _stream(stream)))
 
 
+def sparse_mla_attention(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, scale: float,
+                         sink: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """Sparse MLA attention of bf16 queries [T, H, 512] over the listed slots
+    (int32 [T, topk], invalid entries skipped) of a paged MXFP4 cache (the
+    view rules of ``store_mxfp4_mla``), keys = values = the dequantized rows;
+    optional fp32 per-head sinks [P3 read path].  Returns bf16 [T, H, 512]."""
+    _need_cuda(q, cache, indices)
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 512 or q.stride(2) != 1:
+        raise ValueError("q must be bf16 [tokens, heads, 512] with unit inner stride")
+    if indices.dtype != torch.int32 or indices.dim() != 2 or indices.shape[0] != q.shape[0] \
+            or (indices.shape[1] > 1 and indices.stride(1) != 1):
+        raise ValueError("indices must be int32 [tokens, topk] with unit inner stride")
+    num_blocks, block_size, stride_rows = resolve_paged_view(cache, 512)
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != q.shape[1]
+                             or not sink.is_contiguous()):
+        raise ValueError("sink must be contiguous fp32 [heads]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or out.stride(2) != 1:
+        raise ValueError("out must be bf16 shaped like q with unit inner stride")
+    _abi.check(_abi.lib().sparse_mla_attention(
+        q.data_ptr(), q.shape[0], q.shape[1], 512, q.stride(0), q.stride(1), cache.data_ptr(),
+        num_blocks, block_size, stride_rows, indices.data_ptr(), indices.shape[1],
+        max(indices.stride(0), indices.shape[1]),
+        float(scale), None if sink is None else sink.data_ptr(), out.data_ptr(), out.stride(0),
+        out.stride(1), _stream(stream)))
+    return out
+
+
 # ------------------------------------------------------------------ page-level API
 
 def resolve_paged_view(cache: torch.Tensor, latent: int, group: int = GROUP_SIZE):

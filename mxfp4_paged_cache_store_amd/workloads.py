@@ -208,3 +208,88 @@ def rope_case(seed: int = 4, tokens: int = 16384, compress_ratio: int = 4) -> Ro
     positions = rng.integers(0, 65536, size=tokens, dtype=np.int64)
     slots = rng.permutation(tokens).astype(np.int64)
     return RopeCase(latent, positions, rope_cos_sin_table(), slots, 64, tokens // 64, compress_ratio)
+
+
+# ------------------------------------------------------------------ attention (read side)
+
+@dataclass
+class AttnCase:
+    q: np.ndarray          # uint16 bf16 bits [T, H, 512]
+    cache: np.ndarray      # uint8 [num_blocks * block_stride_rows * 272]
+    num_blocks: int
+    block_size: int
+    block_stride_rows: int
+    indices: np.ndarray    # int32 [T, topk]
+    scale: float
+    sink: np.ndarray | None  # fp32 [H] or None
+
+
+def random_mxfp4_rows(rng: np.random.Generator, rows: int, scale_lo: int = 121,
+                      scale_hi: int = 130) -> np.ndarray:
+    """Random but well-formed 272-byte MXFP4 rows: uniform code bytes and
+    E8M0 scale bytes uniform in [scale_lo, scale_hi] (values of order 2^-6
+    .. 2^3 * 6), as uint8 [rows, 272].  Caches for the read side are drawn
+    this way so that neither implementation's store produces the other's
+    input."""
+    out = rng.integers(0, 256, size=(rows, ROW_BYTES), dtype=np.uint8)
+    out[:, 256:] = rng.integers(scale_lo, scale_hi + 1, size=(rows, 16), dtype=np.uint8)
+    return out
+
+
+def attention_case(tokens: int, heads: int, topk: int, seed: int, num_blocks: int = 64,
+                   block_size: int = 64, block_stride_rows: int | None = None,
+                   invalid_frac: float = 0.1, sink: bool = False,
+                   score_std: float = 2.0) -> AttnCase:
+    """Sparse-attention inputs: q ~ N(0, 1) in bf16; a paged cache of random
+    well-formed rows (other layers' rows between blocks when the block
+    stride exceeds the block); per token `topk` random slots of the cache
+    (repeats allowed), a fraction replaced by -1 and a few by slots past the
+    end; scale chosen so scores have about `score_std` standard deviation;
+    optional per-head sinks ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    bsr = block_stride_rows or block_size
+    rows = num_blocks * bsr
+    cache = random_mxfp4_rows(rng, rows).reshape(-1)
+    q = f32_to_bf16_bits(rng.standard_normal((tokens, heads, LATENT)).astype(np.float32))
+    slots = num_blocks * block_size
+    idx = rng.integers(0, slots, size=(tokens, topk)).astype(np.int32)
+    idx[rng.random((tokens, topk)) < invalid_frac] = -1
+    if topk:
+        idx[rng.random((tokens, topk)) < 0.01] = slots + 7
+    # a dequantized value with uniform codes (mean square 68.5/8) and a scale
+    # 2^e, e uniform in [-6, 3] (mean of 4^e ~ 8.53), has rms ~ 8.55; a dot
+    # product with N(0, 1) over 512 dims then has std ~ 8.55 * sqrt(512)
+    scale = score_std / (8.55 * np.sqrt(LATENT))
+    snk = rng.standard_normal(heads).astype(np.float32) if sink else None
+    return AttnCase(q, cache, num_blocks, block_size, bsr, idx, float(scale), snk)
+
+
+def attention_workload_device(tokens: int = 4096, context: int = 16384, heads: int = 32,
+                              topk: int = 2048, seed: int = 5, device: str = "cuda"):
+    """The read-side workload: the last `tokens` queries of a `context`-token
+    prefill, each attending `topk` distinct random slots of its causal prefix
+    (fewer, padded with -1, when the prefix is shorter), heads query heads,
+    over a flat cache of `context` random well-formed rows.  Drawn on the
+    device with torch's seeded generator.  Returns (q bf16 [T, H, 512], cache
+    uint8 [context, 272], indices int32 [T, topk], scale)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    cache = torch.randint(0, 256, (context, ROW_BYTES), generator=g, device=device, dtype=torch.uint8)
+    cache[:, 256:] = torch.randint(121, 131, (context, 16), generator=g, device=device, dtype=torch.uint8)
+    q = torch.randn((tokens, heads, LATENT), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    pos = torch.arange(context - tokens, context, device=device)
+    idx = torch.empty((tokens, topk), dtype=torch.int32, device=device)
+    chunk = 512
+    for lo in range(0, tokens, chunk):
+        hi = min(tokens, lo + chunk)
+        r = torch.rand((hi - lo, context), generator=g, device=device)
+        keys = torch.arange(context, device=device)
+        r[keys[None, :] > pos[lo:hi, None]] = -1.0
+        val, sel = torch.topk(r, topk, dim=1)
+        sel = sel.to(torch.int32)
+        sel[val < 0] = -1
+        idx[lo:hi] = sel
+    scale = 2.0 / (8.55 * LATENT ** 0.5)   # scores of std ~2 (see attention_case)
+    return q, cache, idx, scale

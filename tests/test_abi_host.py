@@ -250,3 +250,38 @@ def test_compress_norm_rejects(mxlib, kw, status):
 
 def test_compress_norm_empty_is_a_noop(mxlib):
     assert norm(mxlib, n=0, kv=0, slots=0, w=0, out=0) == _abi.MX_OK
+
+
+def attn(mxlib, **kw):
+    a = dict(q=FAKE, n=3, h=16, latent=512, qts=16 * 512, qhs=512, cache=FAKE, nb=4, bs=64, bsr=64,
+             idx=FAKE, topk=128, istride=128, scale=0.05, sink=None, out=FAKE, ots=16 * 512, ohs=512)
+    a.update(kw)
+    return mxlib.sparse_mla_attention(a["q"], a["n"], a["h"], a["latent"], a["qts"], a["qhs"], a["cache"],
+                                      a["nb"], a["bs"], a["bsr"], a["idx"], a["topk"], a["istride"],
+                                      a["scale"], a["sink"], a["out"], a["ots"], a["ohs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(latent=256, qhs=256, ohs=256), _abi.MX_E_SHAPE),
+    (dict(h=24), _abi.MX_E_SHAPE),
+    (dict(h=0), _abi.MX_E_SHAPE),
+    (dict(n=-1), _abi.MX_E_RANGE),
+    (dict(topk=-1), _abi.MX_E_RANGE),
+    (dict(nb=1 << 26), _abi.MX_E_RANGE),
+    (dict(scale=float("nan")), _abi.MX_E_ARG),
+    (dict(scale=float("inf")), _abi.MX_E_ARG),
+    (dict(qhs=500), _abi.MX_E_STRIDE),
+    (dict(qts=512), _abi.MX_E_STRIDE),
+    (dict(istride=100), _abi.MX_E_STRIDE),
+    (dict(qhs=516, qts=16 * 516), _abi.MX_E_ALIGN),
+    (dict(q=FAKE + 8), _abi.MX_E_ALIGN),
+    (dict(cache=FAKE + 4), _abi.MX_E_ALIGN),
+    (dict(idx=0), _abi.MX_E_NULL),
+    (dict(bsr=32), _abi.MX_E_STRIDE),
+])
+def test_attention_rejects(mxlib, kw, status):
+    assert attn(mxlib, **kw) == status
+
+
+def test_attention_empty_is_a_noop(mxlib):
+    assert attn(mxlib, n=0, q=0, cache=0, idx=0, out=0) == _abi.MX_OK

@@ -1,0 +1,167 @@
+"""GPU parity of sparse_mla_attention against the oracle's double-precision
+attention over the bf16 dequantized cache.
+
+Tolerance, derived from the kernel's arithmetic.  Scores: bf16 x bf16
+products are exact in fp32 and the MFMAs accumulate 512 of them in fp32, so
+|dS_j| <= g * scale * sum_d |q_d v_jd| with g = 2^-18 (a generous bound on
+32 chained fp32 accumulations); a score error e moves each softmax weight by
+a relative e - e_max, so the output moves by at most 4 g * SQ * A, with
+SQ = max_j scale * sum_d |q_d v_jd| and A_d = sum_j p_j |v_jd| / Z (p the
+exact weights, Z their sum with the sink term).  The base-2 exponent
+(scale * log2 e rounded to fp32, exp2 in fp32) adds at most
+2^-19 * (1 + max|s|) relative per weight.  The weights are rounded to bf16
+for the weighted sum (relative 2^-9 each: at most 2^-9 * A) while the
+denominator uses the fp32 weights (at most 2^-9 * |out|), and the result is
+rounded to bf16 (2^-9 * |out|).  Hence, per element, with a factor of two
+to spare on both terms,
+  |gpu - exact| <= (2^-8 + 4 g SQ + 2^-19 (1 + max|s|)) * A + 2^-7 * |exact|.
+A token whose only valid slot is listed once must reproduce that row
+exactly; a token with no valid slot gives zeros."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_paged_cache_store_amd import ops, workloads
+from tests.gpu_util import bf16_dev, log, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+G = 2.0 ** -18
+
+
+def dequant_rows(cache: np.ndarray, nb: int, bs: int, bsr: int, slots: np.ndarray) -> np.ndarray:
+    """Rows of the listed slots as float64 (the oracle's pinned dequant);
+    invalid slots give zero rows (they carry no weight anyway)."""
+    flat = np.asarray(slots, dtype=np.int64).reshape(-1)
+    out = np.zeros((flat.size, 512), dtype=np.uint16)
+    good = (flat >= 0) & (flat < nb * bs)
+    if good.any():
+        out[good] = oracle.mxfp4_gather_dequant(cache, nb, bs, bsr, 512, flat[good])
+    return (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(*np.shape(slots), 512)
+
+
+def tolerance(q_bits, cache, nb, bs, bsr, idx, scale, sink, exact):
+    qd = (q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)   # [T, H, D]
+    tol = np.zeros_like(exact)
+    for t in range(idx.shape[0]):
+        good = (idx[t] >= 0) & (idx[t] < nb * bs)
+        if not good.any():
+            continue
+        v = dequant_rows(cache, nb, bs, bsr, idx[t][good])                      # [J, D]
+        s = scale * (qd[t] @ v.T)                                                # [H, J]
+        sq = scale * (np.abs(qd[t]) @ np.abs(v).T).max(axis=1)                   # [H]
+        m = s.max(axis=1)
+        if sink is not None:
+            m = np.maximum(m, sink.astype(np.float64))
+        p = np.exp(s - m[:, None])
+        z = p.sum(axis=1) + (np.exp(sink.astype(np.float64) - m) if sink is not None else 0.0)
+        a = (p @ np.abs(v)) / z[:, None]                                         # [H, D]
+        rel = 2.0 ** -8 + 4 * G * sq + 2.0 ** -19 * (1.0 + np.abs(s).max(axis=1))
+        tol[t] = rel[:, None] * a + 2.0 ** -7 * np.abs(exact[t])
+    return tol
+
+
+def run_gpu(device, case: workloads.AttnCase, out_pad: int = 0):
+    t, h, _ = case.q.shape
+    cache = u8_dev(case.cache, device)
+    if case.block_stride_rows != case.block_size or case.num_blocks > 1:
+        cache = cache.view(case.num_blocks, case.block_stride_rows, 272)[:, :case.block_size]
+    q = bf16_dev(case.q, device)
+    idx = torch.from_numpy(np.ascontiguousarray(case.indices)).to(device)
+    sink = None if case.sink is None else torch.from_numpy(case.sink).to(device)
+    backing = torch.full((t, h, 512 + out_pad), -7.0, dtype=torch.bfloat16, device=device)
+    out = backing[:, :, :512]
+    log(f"attention T={t} H={h} topk={case.indices.shape[1]} sink={case.sink is not None}")
+    ops.sparse_mla_attention(q, cache, idx, case.scale, sink=sink, out=out)
+    torch.cuda.synchronize()
+    if out_pad:
+        assert (backing[:, :, 512:] == -7.0).all(), "padding written"
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def check_case(device, case: workloads.AttnCase, out_pad: int = 0):
+    got = run_gpu(device, case, out_pad)
+    want = oracle.sparse_mla_attention(case.q, case.cache, case.num_blocks, case.block_size,
+                                       case.block_stride_rows, case.indices, case.scale, case.sink)
+    tol = tolerance(case.q, case.cache, case.num_blocks, case.block_size, case.block_stride_rows,
+                    case.indices, case.scale, case.sink, want)
+    err = np.abs(got - want)
+    worst = float((err / np.maximum(tol, 1e-300)).max()) if err.size else 0.0
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, (worst, [(tuple(i), got[tuple(i)], want[tuple(i)], tol[tuple(i)]) for i in bad[:5]])
+    return worst
+
+
+@pytest.mark.parametrize("tokens,heads,topk,sink,seed", [
+    (4, 16, 64, False, 1),       # one tile
+    (6, 16, 256, False, 2),      # four tiles
+    (5, 32, 200, True, 3),       # ragged last tile, sinks, 32-head blocks
+    (3, 48, 130, False, 4),      # three 16-head blocks
+    (2, 64, 512, True, 5),       # two 32-head blocks
+])
+def test_attention_parity(device, tokens, heads, topk, sink, seed):
+    case = workloads.attention_case(tokens, heads, topk, seed, sink=sink)
+    worst = check_case(device, case)
+    log(f"worst error / tolerance = {worst:.3f}")
+
+
+def test_attention_sharp_scores_and_paged_cache(device):
+    """Peaked softmax (score std ~12), a non-power-of-two block (48) with
+    other layers' rows interleaved (stride 80), and a padded output."""
+    case = workloads.attention_case(4, 32, 300, 6, num_blocks=40, block_size=48,
+                                    block_stride_rows=80, score_std=12.0, sink=True)
+    check_case(device, case, out_pad=8)
+
+
+def test_attention_degenerate_tokens(device):
+    """Token 0: no valid slot -> zeros (with sinks too); token 1: one valid
+    slot -> exactly that row; token 2: a slot listed 40 times among pads;
+    token 3: topk entries all past the cache."""
+    case = workloads.attention_case(4, 16, 96, 7, sink=False)
+    idx = np.full((4, 96), -1, dtype=np.int32)
+    idx[1, 50] = 17
+    idx[2, ::2][:40] = 33
+    idx[3, :] = case.num_blocks * case.block_size + 3
+    case.indices = idx
+    got = run_gpu(device, case)
+    assert (got[0] == 0).all() and (got[3] == 0).all()
+    row = dequant_rows(case.cache, case.num_blocks, case.block_size, case.block_stride_rows,
+                       np.array([17]))[0]
+    assert (got[1] == row[None, :]).all()
+    assert (got[2] == dequant_rows(case.cache, case.num_blocks, case.block_size,
+                                   case.block_stride_rows, np.array([33]))[0][None, :]).all()
+    case.sink = np.linspace(-2, 2, 16).astype(np.float32)
+    got = run_gpu(device, case)
+    assert (got[0] == 0).all() and (got[3] == 0).all()
+    check_case(device, case)
+
+
+def test_attention_topk_zero(device):
+    case = workloads.attention_case(3, 16, 0, 8)
+    got = run_gpu(device, case)
+    assert (got == 0).all()
+
+
+def test_attention_workload_sampled(device):
+    """The benchmark's workload (the last 4,096 queries of a 16,384-token
+    prefill, 32 heads, top-2048 causal slots) in the launch the benchmark
+    times; 6 sampled tokens (first, last and random) checked against the
+    oracle, all heads."""
+    q, cache, idx, scale = workloads.attention_workload_device()
+    log(f"attention workload T={q.shape[0]} H={q.shape[1]} topk={idx.shape[1]}")
+    out = ops.sparse_mla_attention(q, cache, idx, scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    pick = np.unique(np.concatenate([[0, q.shape[0] - 1], rng.choice(q.shape[0], 4, replace=False)]))
+    pick_dev = torch.from_numpy(pick).to(q.device)
+    q_s = q[pick_dev].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    idx_s = idx[pick_dev].cpu().numpy()
+    cache_h = cache.cpu().numpy().reshape(-1)
+    n = cache.shape[0]
+    got = out[pick_dev].float().cpu().numpy().astype(np.float64)
+    want = oracle.sparse_mla_attention(q_s, cache_h, 1, n, n, idx_s, scale)
+    tol = tolerance(q_s, cache_h, 1, n, n, idx_s, scale, None, want)
+    err = np.abs(got - want)
+    assert (err <= tol).all(), float((err / tol).max())
