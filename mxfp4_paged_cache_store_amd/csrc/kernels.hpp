@@ -82,6 +82,7 @@ struct AttnArgs {
   uint16_t* out;              // bf16 [num_tokens, num_heads, 512]
   int64_t out_token_stride;
   int64_t out_head_stride;
+  bool out_aligned;           // out 16-byte aligned, strides multiples of 8
   int32_t num_heads;          // multiple of 16
   int64_t num_tokens;
 };

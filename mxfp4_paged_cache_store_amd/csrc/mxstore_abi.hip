@@ -375,6 +375,7 @@ int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num
   a.out = out_bf16;
   a.out_token_stride = out_token_stride;
   a.out_head_stride = out_head_stride;
+  a.out_aligned = aligned(out_bf16, 16) && out_token_stride % 8 == 0 && out_head_stride % 8 == 0;
   a.num_heads = (int32_t)num_heads;
   a.num_tokens = num_tokens;
   return launched(mxs::launch_sparse_mla_attn(a, (hipStream_t)stream), "sparse_mla_attention");
