@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
 // identical to the scatter form (for duplicate slots either form keeps one of
 // the tokens).
 
-constexpr int kSlotsPerWave = 8;
+constexpr int kSlotsPerWave = 4;
 
 __global__ __launch_bounds__(256) void fill_inverse(int32_t* __restrict__ inv, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -239,7 +239,13 @@ __global__ __launch_bounds__(256) void invert_slots(const int64_t* __restrict__ 
   if (s >= 0 && s < (int64_t)num_slots) inv[s] = (int32_t)t;
 }
 
-template <int LATENT, bool kPow2>
+// kStaged: the wave's kSlotsPerWave slots are consecutive rows of the cache (a
+// flat cache, or a block size that is a multiple of kSlotsPerWave; 16-byte
+// aligned), so its rows form one contiguous span; they are assembled in LDS and written as 16-byte chunks
+// (row pitches are multiples of 16, so a chunk never straddles two rows and a
+// skipped row's chunks are simply dropped).  Otherwise each row is written
+// with dword stores.
+template <int LATENT, bool kPow2, bool kStaged>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_kernel(
     const StoreArgs a, const int32_t* __restrict__ inv) {
   static_assert(LATENT >= 512, "slot order is used for latents of 512 and more");
@@ -276,21 +282,68 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_ke
   }
 
   constexpr uint32_t kDrop = 0x7FFFFFF0u;
+  if constexpr (kStaged) {
+    constexpr int kSpan = kSlotsPerWave * (int)kPitch;  // bytes of the wave's rows
+    __shared__ uint32_t stage[kWavesPerBlock][kSpan / 4];
+    uint32_t* st = stage[wave];
+    uint32_t valid = 0;
 #pragma unroll
-  for (int p = 0; p < kSlotsPerWave; ++p) {
-    const bool ok = tok[p] >= 0;
-    const int64_t row_off = ok ? a.map.row<kPow2>((uint32_t)(s0 + p)) * kPitch : 0;
-    const __amdgpu_buffer_rsrc_t rs = buffer_at(a.cache + row_off, ok ? (uint32_t)kPitch : 0u);
+    for (int p = 0; p < kSlotsPerWave; ++p) {
+      valid |= (tok[p] >= 0 ? 1u : 0u) << p;
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) {
-      uint32_t sdw;
-      const uint32_t codes = quantize_slice(v[p][sub], sdw);
-      const uint32_t scale_off = (lane & 15) == 12 ? LATENT / 2 + sub * 16 + (lane >> 4) * 4 : kDrop;
-      // Rows go out in slot order, so plain stores let L2 merge neighbours.
-      __builtin_amdgcn_raw_buffer_store_b32(codes, rs, sub * 256 + lane * 4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, 0);
+      for (int sub = 0; sub < kSub; ++sub) {
+        uint32_t sdw;
+        const uint32_t codes = quantize_slice(v[p][sub], sdw);
+        st[(p * (int)kPitch + sub * 256) / 4 + lane] = codes;
+        if ((lane & 15) == 12) st[(p * (int)kPitch + LATENT / 2 + sub * 16) / 4 + (lane >> 4)] = sdw;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // Rows go out in slot order, so plain stores let L2 merge neighbours.
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_at(a.cache + a.map.row<kPow2>((uint32_t)s0) * kPitch, (uint32_t)kSpan);
+#pragma unroll
+    for (int c0 = 0; c0 < kSpan / 16; c0 += kWave) {
+      const int c = c0 + lane;
+      if (c0 + kWave <= kSpan / 16 || c < kSpan / 16) {
+        const u32x4 d = *reinterpret_cast<const u32x4*>(&st[4 * c]);
+        const uint32_t off = (valid >> (c / ((int)kPitch / 16))) & 1u ? (uint32_t)(16 * c) : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < kSlotsPerWave; ++p) {
+      const bool ok = tok[p] >= 0;
+      const int64_t row_off = ok ? a.map.row<kPow2>((uint32_t)(s0 + p)) * kPitch : 0;
+      const __amdgpu_buffer_rsrc_t rs = buffer_at(a.cache + row_off, ok ? (uint32_t)kPitch : 0u);
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) {
+        uint32_t sdw;
+        const uint32_t codes = quantize_slice(v[p][sub], sdw);
+        const uint32_t scale_off = (lane & 15) == 12 ? LATENT / 2 + sub * 16 + (lane >> 4) * 4 : kDrop;
+        // Rows go out in slot order, so plain stores let L2 merge neighbours.
+        __builtin_amdgcn_raw_buffer_store_b32(codes, rs, sub * 256 + lane * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, 0);
+      }
     }
   }
+}
+
+template <int LATENT, bool kPow2>
+void launch_by_slot_pow2(const StoreArgs& a, const int32_t* inv, unsigned blocks, hipStream_t stream) {
+  // consecutive slots are consecutive rows within a block (the flat form has
+  // a single block); a wave's slots share a block when the block size is a
+  // multiple of kSlotsPerWave
+  const bool flat = a.map.pow2 && a.map.block_shift == 32;
+  const bool staged = (flat || a.map.block_size % kSlotsPerWave == 0) &&
+                      (reinterpret_cast<uintptr_t>(a.cache) & 15u) == 0;
+  if (staged)
+    hipLaunchKernelGGL((mxfp4_store_by_slot_kernel<LATENT, kPow2, true>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, a, inv);
+  else
+    hipLaunchKernelGGL((mxfp4_store_by_slot_kernel<LATENT, kPow2, false>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, a, inv);
 }
 
 template <int LATENT>
@@ -298,11 +351,9 @@ hipError_t launch_by_slot(const StoreArgs& a, const int32_t* inv, hipStream_t st
   constexpr int64_t kPerBlock = (int64_t)kWavesPerBlock * kSlotsPerWave;
   const unsigned blocks = (unsigned)(((int64_t)a.map.num_slots + kPerBlock - 1) / kPerBlock);
   if (a.map.pow2)
-    hipLaunchKernelGGL((mxfp4_store_by_slot_kernel<LATENT, true>), dim3(blocks),
-                       dim3(kWave * kWavesPerBlock), 0, stream, a, inv);
+    launch_by_slot_pow2<LATENT, true>(a, inv, blocks, stream);
   else
-    hipLaunchKernelGGL((mxfp4_store_by_slot_kernel<LATENT, false>), dim3(blocks),
-                       dim3(kWave * kWavesPerBlock), 0, stream, a, inv);
+    launch_by_slot_pow2<LATENT, false>(a, inv, blocks, stream);
   return hipGetLastError();
 }
 

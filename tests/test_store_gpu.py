@@ -253,6 +253,36 @@ def test_slot_order_form(device, latent, nb, bs, stride, ntok):
         assert (got == host).all(), (layer, first_mismatch(got, host, pitch))
 
 
+def test_slot_order_row_writes(device):
+    """The slot-order store assembles a wave's rows (4 slots) in LDS and writes
+    them as 16-byte chunks when they are consecutive in a 16-byte-aligned
+    cache; with a cache that is only 4-byte aligned, or a block of 10 slots (a
+    wave's slots may straddle two blocks), it writes row by row.  All forms
+    give the oracle's bytes, including skipped slots' canaries inside a chunk
+    span."""
+    rng = np.random.default_rng(77)
+    for nb, bs, stride, base in ((200, 128, 128, 4), (900, 10, 14, 0), (300, 64, 64, 0), (700, 12, 20, 0)):
+        num_slots = nb * bs
+        ntok = num_slots * 3 // 4
+        slots = rng.choice(num_slots, ntok, replace=False).astype(np.int64)
+        slots[rng.random(ntok) < 0.05] = -1
+        x = rng.standard_normal((ntok, 512)) * np.exp2(rng.uniform(-10, 10, size=(ntok, 1)))
+        src = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        nbytes = ((nb - 1) * stride + bs) * 272
+        host = np.full(nbytes, 0xA5, dtype=np.uint8)
+        backing = u8_dev(np.full(nbytes + 16, 0xA5, dtype=np.uint8), device)
+        dev_cache = backing[base: base + nbytes]
+        inv = torch.empty(ops.mxfp4_inverse_bytes(nb, bs) // 4, dtype=torch.int32, device=device)
+        log(f"store slot order rows: nb={nb} bs={bs} stride={stride} cache offset {base}")
+        ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
+        ops.mxfp4_store_by_slot(bf16_dev(src, device), ntok, inv, dev_cache, nb, bs, stride)
+        torch.cuda.synchronize()
+        got = backing.cpu().numpy()
+        oracle.mxfp4_store(src, slots, host, nb, bs, stride, threads=oracle_threads())
+        assert (got[base: base + nbytes] == host).all(), first_mismatch(got[base: base + nbytes], host, 272)
+        assert (got[:base] == 0xA5).all() and (got[base + nbytes:] == 0xA5).all()
+
+
 def test_page_api_with_inverse(device):
     """store_mxfp4_mla with an inverse buffer: slot order for a dense batch,
     the scatter form for a sparse one; both match the oracle."""
