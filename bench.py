@@ -98,18 +98,41 @@ def time_launches(fn, steps: int, warmup: int, torch):
     return wall, ev0.elapsed_time(ev1) / 1000.0
 
 
+def cpu_threads() -> tuple[int, int]:
+    """(threads for the all-cores leg, logical CPUs the OS reports).  The
+    all-cores leg uses the CPUs this process may run on, at most 16 (one
+    GPU's share of a shared host)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return max(1, min(16, usable)), os.cpu_count() or 1
+
+
 def cpu_baseline(sample: int):
+    """The oracle's store (plain C, scalar) on the host: all cores over
+    contiguous token ranges on `sample` tokens, and one thread on
+    sample / threads tokens (about the same wall time).  Data generation is
+    outside the timed calls."""
     import numpy as np
 
     import oracle
     from mxfp4_paged_cache_store_amd import workloads
 
-    threads = max(1, min(8, os.cpu_count() or 1))
+    threads, nproc = cpu_threads()
     src, slots = workloads.large_sample_host(sample)
     cache = np.full(sample * 272, 0xA5, dtype=np.uint8)
     t0 = time.perf_counter()
     oracle.mxfp4_store(src, slots, cache, 1, sample, sample, threads=threads)
     dt = time.perf_counter() - t0
+    one = max(1, sample // threads)
+    src1 = np.ascontiguousarray(src[:one])
+    slots1 = np.empty(one, dtype=np.int64)
+    slots1[np.argsort(slots[:one], kind="stable")] = np.arange(one, dtype=np.int64)
+    cache1 = np.full(one * 272, 0xA5, dtype=np.uint8)
+    t0 = time.perf_counter()
+    oracle.mxfp4_store(src1, slots1, cache1, 1, one, one, threads=1)
+    dt1 = time.perf_counter() - t0
     return {
         "value": round(sample / dt, 1),
         "unit": "tokens/s",
@@ -118,7 +141,13 @@ def cpu_baseline(sample: int):
         "sample": f"{sample} tokens x 512 bf16 uniform in [-4, 4], random-permutation slots "
                   f"into a flat cache (same distribution as the timed batch), "
                   f"{threads} threads over contiguous token ranges, {dt:.2f} s wall "
-                  f"({threads * dt:.0f} thread-seconds)",
+                  f"({threads * dt:.0f} thread-seconds); nproc {nproc}",
+        "GBps": round(sample * BYTES_PER_TOKEN / dt / 1e9, 2),
+        "nproc": nproc,
+        "single_thread": {"value": round(one / dt1, 1), "unit": "tokens/s",
+                          "GBps": round(one * BYTES_PER_TOKEN / dt1 / 1e9, 3),
+                          "sample": f"first {one} tokens, their slots ranked into a {one}-slot "
+                                    f"cache, {dt1:.2f} s"},
     }
 
 
@@ -210,47 +239,60 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
     return out
 
 
-def run_sweep(torch, ops):
-    """Store throughput vs token count and slot pattern, both forms, with the
-    Infinity Cache flushed before each repetition by reading a 1 GiB buffer
-    (a write-flush would leave dirty lines to be written back during the
-    timed kernel); median of 20."""
+SWEEP_TOKENS = (16384, 65536, 262144, 1048576, 4500000)
+SWEEP_REPS = 20
+
+
+def run_sweep(torch, ops, workloads):
+    """Store throughput vs token count and slot pattern, both forms.  Slot
+    patterns: prefill-style runs (requests of U[448, 512) tokens, each in its
+    own 512-slot chunk, chunks in random order) and a random permutation.
+    Each case is timed SWEEP_REPS times with the Infinity Cache flushed
+    before every repetition by reading a 1 GiB buffer (a write-flush would
+    leave dirty lines to be written back during the timed kernel), then
+    SWEEP_REPS times warm (back to back, labelled "warm"); medians of HIP
+    event times around single launches, two untimed repetitions first.  The
+    dispatches come in the order the lines are printed (flushed before
+    warm), so a kernel trace of this run splits the same way."""
     import statistics
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    for n in (16384, 65536, 262144, 1048576, 4500000):
+    for n in SWEEP_TOKENS:
         for pattern in ("runs", "random"):
             src = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda").uniform_(-4, 4)
             if pattern == "random":
-                slots = torch.randperm(n, device="cuda")
+                slots, num_slots = torch.randperm(n, device="cuda"), n
             else:
-                slots = torch.arange(n, device="cuda", dtype=torch.int64)
-            cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
-            inv = torch.empty(n, dtype=torch.int32, device="cuda")
-            forms = {"scatter": lambda: ops.mxfp4_store(src, slots, cache, 1, n, n)}
-            if ops.mxfp4_slot_order_advised(n, 512, 1, n):
+                host, num_slots = workloads.request_runs_slots(n)
+                slots = torch.from_numpy(host).to("cuda")
+            cache = torch.zeros(num_slots * 272, dtype=torch.uint8, device="cuda")
+            inv = torch.empty(num_slots, dtype=torch.int32, device="cuda")
+            forms = {"scatter": lambda: ops.mxfp4_store(src, slots, cache, 1, num_slots, num_slots)}
+            if ops.mxfp4_slot_order_advised(n, 512, 1, num_slots):
                 def slot_order():
-                    ops.mxfp4_build_inverse(slots, 1, n, inv)
-                    ops.mxfp4_store_by_slot(src, n, inv, cache, 1, n, n)
+                    ops.mxfp4_build_inverse(slots, 1, num_slots, inv)
+                    ops.mxfp4_store_by_slot(src, n, inv, cache, 1, num_slots, num_slots)
                 forms["slot_order"] = slot_order
             for form, fn in forms.items():
-                times = []
-                for _ in range(22):
-                    flush.sum()
-                    torch.cuda.synchronize()
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    fn()
-                    e1.record()
-                    torch.cuda.synchronize()
-                    times.append(e0.elapsed_time(e1) / 1000.0)
-                t = statistics.median(times[2:])
-                gbs = n * BYTES_PER_TOKEN / t / 1e9
-                print(json.dumps({"sweep": "mxfp4_store", "form": form, "tokens": n, "slots": pattern,
-                                  "us": round(t * 1e6, 2), "GBps": round(gbs, 1),
-                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                  "cache": "flushed"}), flush=True)
+                for state in ("flushed", "warm"):
+                    times = []
+                    for _ in range(SWEEP_REPS + 2):
+                        if state == "flushed":
+                            flush.sum()
+                        torch.cuda.synchronize()
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        fn()
+                        e1.record()
+                        torch.cuda.synchronize()
+                        times.append(e0.elapsed_time(e1) / 1000.0)
+                    t = statistics.median(times[2:])
+                    gbs = n * BYTES_PER_TOKEN / t / 1e9
+                    print(json.dumps({"sweep": "mxfp4_store", "form": form, "tokens": n, "slots": pattern,
+                                      "cache": state, "reps": SWEEP_REPS, "us": round(t * 1e6, 2),
+                                      "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}),
+                          flush=True)
             del src, slots, cache, inv
 
 
@@ -374,7 +416,7 @@ def main():
     if args.sweep:
         del cache
         torch.cuda.empty_cache()
-        run_sweep(torch, ops)
+        run_sweep(torch, ops, workloads)
 
 
 if __name__ == "__main__":

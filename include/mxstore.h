@@ -103,9 +103,11 @@ int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
 int64_t mxfp4_inverse_bytes(int64_t num_blocks, int64_t block_size);
 
 /* 1 when the slot-order form is expected to beat mxfp4_store for this shape:
- * latent in {512, 1024, 2048}, 2^17 <= num_tokens < 2^31 and num_tokens >=
- * half the slots; else 0.  Host-only heuristic (measured on MI355X), no
- * device work. */
+ * latent in {512, 1024, 2048}, num_tokens < 2^31, num_tokens >= half the
+ * slots, and the batch's rows (num_tokens * row bytes) exceed 256 MiB, the
+ * size of MI355X's Infinity Cache (smaller batches merge their scattered
+ * rows there); else 0.  Host-only heuristic (measured on MI355X), no device
+ * work. */
 int mxfp4_slot_order_advised(int64_t num_tokens, int64_t latent,
                              int64_t num_blocks, int64_t block_size);
 

@@ -16,7 +16,15 @@ struct StoreArgs {
   int64_t num_tokens;
   uint8_t* cache;
   SlotMap map;
+  bool plain_stores;     // scatter form: plain stores for scattered rows too
 };
+
+// Rows written by one store launch that fit in MI355X's 256 MiB Infinity
+// Cache: scattered rows of such a batch are written with plain stores (their
+// partial 128-byte lines merge in that cache before they reach HBM); larger
+// scattered batches stream with non-temporal stores, or take the slot-order
+// form when they are dense.
+constexpr int64_t kPlainStoreBytes = int64_t(256) << 20;
 
 struct DequantArgs {
   const uint8_t* cache;

@@ -120,38 +120,58 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
   const int lane_in_tok = lane % kLanesPerTok;
   const int64_t wave_first = ((int64_t)xcd_contiguous_block() * kWavesPerBlock + wave) * kToks;
 
-  // Slots of the wave's tokens: one merged load when the wave is whole.
   int64_t slot[kTokensPerWave];
-  if (wave_first + kToks <= a.num_tokens) {
-#pragma unroll
-    for (int p = 0; p < kTokensPerWave; ++p)
-      slot[p] = a.slots[wave_first + p * kToksPerPass + tok_in_pass];
-  } else {
+  u32x4 v[kTokensPerWave][kSub];
+  if constexpr (kToksPerPass == 1) {
+    // Whole wave on one token per pass.  The wave's slots come in one
+    // vector load (lane p & (kTokensPerWave-1) reads pass p's), issued
+    // before the rows: vector loads return in order, so waiting for the
+    // slots leaves the row loads in flight, where a scalar load would be
+    // waited for together with every other scalar load.  A row does not
+    // wait for its slot: a pad token's row is read and dropped.
+    const int64_t last = a.num_tokens - 1;
+    const int64_t tl = wave_first + (lane & (kTokensPerWave - 1));
+    const int64_t vs = a.slots[tl < last ? tl : last];
 #pragma unroll
     for (int p = 0; p < kTokensPerWave; ++p) {
-      const int64_t t = wave_first + p * kToksPerPass + tok_in_pass;
-      slot[p] = t < a.num_tokens ? a.slots[t] : -1;
-    }
-  }
-
-  u32x4 v[kTokensPerWave][kSub];
-  int64_t row_off[kTokensPerWave];
-#pragma unroll
-  for (int p = 0; p < kTokensPerWave; ++p) {
-    const int64_t t = wave_first + p * kToksPerPass + tok_in_pass;
-    const bool ok = slot[p] >= 0 && slot[p] < (int64_t)a.map.num_slots;
-    row_off[p] = ok ? a.map.row<kPow2>((uint32_t)slot[p]) * kPitch : -1;
-    if constexpr (kToksPerPass == 1) {
-      // Whole wave on one token: a raw buffer over its row, empty for a
-      // skipped token, so the load needs no branch.
+      // Raw buffer over the token's row, empty past the batch: no branch.
+      const int64_t t = wave_first + p;
+      const bool have = t < a.num_tokens;
       const __amdgpu_buffer_rsrc_t rs =
-          buffer_at(a.src + (ok ? t * a.src_stride : 0), ok ? LATENT * 2 : 0);
+          buffer_at(a.src + (have ? t * a.src_stride : 0), have ? LATENT * 2 : 0);
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub)
         v[p][sub] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (sub * 64 + lane_in_tok) * 16, 0, kBufNT));
+    }
+    // Keeps the row loads above this point (the compiler would otherwise
+    // sink them below the slot arithmetic and its wait).
+    int64_t vs_ready = vs;
+    asm volatile("" : "+v"(vs_ready) : : "memory");
+#pragma unroll
+    for (int p = 0; p < kTokensPerWave; ++p) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)vs_ready, p);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)vs_ready >> 32), p);
+      slot[p] = wave_first + p < a.num_tokens ? (int64_t)(((uint64_t)hi << 32) | lo) : -1;
+    }
+  } else {
+    // Several tokens per pass: one merged load of the slots when the wave
+    // is whole; rows of skipped tokens are not read.
+    if (wave_first + kToks <= a.num_tokens) {
+#pragma unroll
+      for (int p = 0; p < kTokensPerWave; ++p)
+        slot[p] = a.slots[wave_first + p * kToksPerPass + tok_in_pass];
     } else {
-      if (ok) {
+#pragma unroll
+      for (int p = 0; p < kTokensPerWave; ++p) {
+        const int64_t t = wave_first + p * kToksPerPass + tok_in_pass;
+        slot[p] = t < a.num_tokens ? a.slots[t] : -1;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kTokensPerWave; ++p) {
+      const int64_t t = wave_first + p * kToksPerPass + tok_in_pass;
+      if (slot[p] >= 0 && slot[p] < (int64_t)a.map.num_slots) {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.src + t * a.src_stride + lane_in_tok * 8);
         v[p][0] = __builtin_nontemporal_load(src);
       } else {
@@ -160,14 +180,23 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
     }
   }
 
+  int64_t row_off[kTokensPerWave];
+#pragma unroll
+  for (int p = 0; p < kTokensPerWave; ++p) {
+    const bool ok = slot[p] >= 0 && slot[p] < (int64_t)a.map.num_slots;
+    row_off[p] = ok ? a.map.row<kPow2>((uint32_t)slot[p]) * kPitch : -1;
+  }
+
   // A wave whose tokens fill consecutive slots writes adjacent rows: plain
   // stores let L2 assemble whole lines from them.  Scattered rows are
   // streamed with non-temporal stores instead (measured faster for rows
-  // whose neighbours are written at unrelated times).
+  // whose neighbours are written at unrelated times), unless the whole
+  // batch fits in the Infinity Cache (plain_stores), where the partial lines
+  // of neighbouring rows merge before they are written back.
   bool run = true;
 #pragma unroll
   for (int p = 1; p < kTokensPerWave; ++p) run = run && slot[p] == slot[p - 1] + kToksPerPass;
-  run = run && row_off[0] >= 0 && row_off[kTokensPerWave - 1] >= 0;
+  run = (run && row_off[0] >= 0 && row_off[kTokensPerWave - 1] >= 0) || a.plain_stores;
 
 #pragma unroll
   for (int p = 0; p < kTokensPerWave; ++p) {
@@ -373,7 +402,9 @@ hipError_t launch_tpw(const StoreArgs& a, hipStream_t stream) {
 }
 
 template <int LATENT>
-hipError_t launch_latent(const StoreArgs& a, hipStream_t stream) {
+hipError_t launch_latent(const StoreArgs& args, hipStream_t stream) {
+  StoreArgs a = args;
+  a.plain_stores = a.num_tokens <= kPlainStoreBytes / (LATENT / 2 + LATENT / 32);
   // Small batches are latency-bound: more, shorter waves finish sooner.
   if (a.num_tokens < (int64_t(1) << 18)) return launch_tpw<LATENT, 2>(a, stream);
   return launch_tpw<LATENT, 4>(a, stream);

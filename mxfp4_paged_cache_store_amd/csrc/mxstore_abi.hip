@@ -170,10 +170,13 @@ int mxfp4_slot_order_advised(int64_t num_tokens, int64_t latent, int64_t num_blo
                              int64_t block_size) {
   if (latent < 512 || latent > 2048 || !is_pow2(latent)) return 0;
   if (mxfp4_inverse_bytes(num_blocks, block_size) < 0) return 0;
-  // The slot order pays for its inverse once a batch is large enough to
-  // stream from HBM and covers at least half of the slots.
+  // The slot order pays for its inverse once a batch covers at least half
+  // of the slots and its rows no longer fit in the Infinity Cache (below
+  // that the scatter form's plain stores merge partial lines there).
   const int64_t num_slots = num_blocks * block_size;
-  return num_tokens >= (int64_t(1) << 17) && num_tokens <= 0x7FFFFFFF && 2 * num_tokens >= num_slots;
+  const int64_t row = latent / 2 + latent / 32;
+  return num_tokens > mxs::kPlainStoreBytes / row && num_tokens <= 0x7FFFFFFF &&
+         2 * num_tokens >= num_slots;
 }
 
 int mxfp4_build_inverse(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,

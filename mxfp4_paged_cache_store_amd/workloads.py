@@ -141,6 +141,25 @@ def prefill_case(seed: int = 2, tokens: int = 16384, requests: int = 32) -> Stor
     return case
 
 
+def request_runs_slots(tokens: int, seed: int = 2, block_size: int = 64) -> tuple[np.ndarray, int]:
+    """The prefill slot pattern at any batch size: requests of U[448, 512)
+    tokens, each a contiguous run of slots from the first slot of its own
+    8-block (512-slot) chunk, chunks in random order, every token valid (the
+    last request is cut to fit).  Returns (slots int64 [tokens], number of
+    slots in the flat cache)."""
+    rng = np.random.default_rng(seed)
+    chunk = 8 * block_size
+    lengths = rng.integers(448, 512, size=tokens // 448 + 1)
+    ends = np.cumsum(lengths)
+    requests = int(np.searchsorted(ends, tokens)) + 1
+    lengths = lengths[:requests].copy()
+    lengths[-1] -= int(ends[requests - 1]) - tokens
+    starts = rng.permutation(requests).astype(np.int64) * chunk
+    first = np.repeat(np.cumsum(lengths) - lengths, lengths)
+    slots = np.repeat(starts, lengths) + (np.arange(tokens, dtype=np.int64) - first)
+    return slots, requests * chunk
+
+
 # ------------------------------------------------------------------ config 3
 
 LARGE_TOKENS = 4_500_000

@@ -146,12 +146,15 @@ def test_inverse_bytes_and_advice(mxlib):
     assert mxlib.mxfp4_inverse_bytes(1 << 30, 64) == _abi.MX_E_RANGE
     adv = mxlib.mxfp4_slot_order_advised
     assert adv(4_500_000, 512, 1, 4_500_000) == 1
-    assert adv(200_000, 1024, 1000, 300) == 1 and adv(200_000, 2048, 1000, 300) == 1
-    assert adv(1 << 17, 512, 1, 1 << 18) == 1
+    # rows past 256 MiB (986,895 rows of 272 B; 493,447 of 544 B; 246,723 of 1088 B)
+    assert adv(986_896, 512, 1, 986_896) == 1 and adv(986_895, 512, 1, 986_895) == 0
+    assert adv(493_448, 1024, 1000, 900) == 1 and adv(493_447, 1024, 1000, 900) == 0
+    assert adv(246_724, 2048, 1000, 400) == 1 and adv(246_723, 2048, 1000, 400) == 0
+    assert adv(1 << 20, 512, 1, 1 << 21) == 1
     assert adv(16_384, 512, 8192, 64) == 0      # sparse prefill: scatter
-    assert adv((1 << 17) - 1, 512, 1, 1 << 17) == 0  # small batch: scatter
-    assert adv(200_000, 256, 1, 200_000) == 0   # latent below 512
-    assert adv(200_000, 512, 1, 400_001) == 0   # under half of the slots
+    assert adv(1 << 17, 512, 1, 1 << 17) == 0   # fits the Infinity Cache: scatter
+    assert adv(2_000_000, 256, 1, 2_000_000) == 0   # latent below 512
+    assert adv(2_000_000, 512, 1, 4_000_001) == 0   # under half of the slots
 
 
 def build_inverse(mxlib, **kw):

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def test_graph_replays_match_eager(device):
-    n = 1 << 17  # large and dense enough for the slot-order form
+    n = 1 << 17  # a dense scattered batch through the slot-order form
     g_src = torch.empty((n, 512), dtype=torch.bfloat16, device=device)
     g_slots = torch.randperm(n, device=device)
     inv = torch.empty(n, dtype=torch.int32, device=device)
@@ -26,10 +26,10 @@ def test_graph_replays_match_eager(device):
     r_lat = bf16_dev(rc.latent, device)
     r_pos, r_cs, r_slots = i64_dev(rc.positions, device), torch.from_numpy(rc.cos_sin).to(device), i64_dev(rc.slots, device)
     r_kv = torch.empty((16, 64, 528), dtype=torch.uint8, device=device)
-    assert ops.mxfp4_slot_order_advised(n, 512, 1, n)
 
     def work():
-        ops.store_mxfp4_mla(g_src, g_slots, g_cache, inverse=inv)
+        ops.mxfp4_build_inverse(g_slots, 1, n, inv)
+        ops.mxfp4_store_by_slot(g_src, n, inv, g_cache, 1, n, n)
         ops.mxfp4_store(p_src, p_slots, p_cache, 1, 1 << 16, 1 << 16)
         ops.mxfp4_gather_dequant(p_cache, 1, 1 << 16, 1 << 16, 512, p_slots, dq_out)
         ops.mxfp8_rope_store(r_lat, r_pos, r_cs, r_kv, r_slots, rc.compress_ratio)

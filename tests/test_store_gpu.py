@@ -230,10 +230,10 @@ def test_large_int64_addressing(device):
 def test_slot_order_form(device, latent, nb, bs, stride, ntok):
     """build_inverse + store_by_slot over dense scattered batches (with pads
     and out-of-range slots) writes the same bytes as the oracle; one inverse
-    serves two layers that share the slot mapping."""
+    serves two layers that share the slot mapping.  (The library advises this
+    form only for batches past 256 MiB of rows; it is correct at any size.)"""
     rng = np.random.default_rng(ntok + latent)
     num_slots = nb * bs
-    assert ops.mxfp4_slot_order_advised(ntok, latent, nb, bs)
     slots = rng.choice(num_slots, ntok, replace=False).astype(np.int64)
     slots[rng.random(ntok) < 0.03] = -1
     slots[:5] = [num_slots, num_slots + 7, 10**13, -2, -(2**40)]
@@ -284,12 +284,17 @@ def test_slot_order_row_writes(device):
 
 
 def test_page_api_with_inverse(device):
-    """store_mxfp4_mla with an inverse buffer: slot order for a dense batch,
-    the scatter form for a sparse one; both match the oracle."""
+    """store_mxfp4_mla with an inverse buffer: slot order for a dense batch
+    past 256 MiB of rows, the scatter form (plain stores: the rows fit in the
+    Infinity Cache) for a smaller one and for a sparse one; all match the
+    oracle."""
     rng = np.random.default_rng(22)
-    for ntok, nslots in ((1 << 17, 1 << 17), (140_000, 1 << 20)):
-        src = (rng.standard_normal((ntok, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for ntok, nslots in ((1 << 20, 1 << 20), (1 << 17, 1 << 17), (140_000, 1 << 20)):
+        # finite bf16 patterns of both signs, magnitudes 2^-31 .. 2^8
+        src = rng.integers(0x3000, 0x4380, size=(ntok, 512), dtype=np.uint16)
+        src |= (rng.integers(0, 2, size=(ntok, 512), dtype=np.uint16) << 15)
         slots = rng.choice(nslots, ntok, replace=False).astype(np.int64)
+        assert ops.mxfp4_slot_order_advised(ntok, 512, 1, nslots) == (ntok == 1 << 20)
         inv = torch.empty(nslots, dtype=torch.int32, device=device)
         cache = torch.full((nslots * 272,), 0xA5, dtype=torch.uint8, device=device)
         log(f"store page API with inverse: {ntok} tokens, {nslots} slots")
