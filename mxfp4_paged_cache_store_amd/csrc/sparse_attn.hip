@@ -10,18 +10,24 @@
 //
 // Work split: one workgroup of 8 waves per (query token, block of HB = 32 or
 // 16 heads = HT head tiles of 16); the token's slots are walked in tiles of
-// 64 keys.  The waves specialise, and the two halves overlap on every SIMD:
-//   producers (waves 0..3, 16 keys each) compute S^T = K Q^T for tile s.
-//            Lane (key l%16, quarter l/16) loads 64 code bytes and one scale
-//            dword of its key's row (one tile ahead); gfx950's
-//            v_cvt_scalef32_pk_bf16_fp4 turns each code dword into 8 exact
-//            bf16 values -- the A operand of a 16x16x32 bf16 MFMA -- and the
-//            query fragments of all HB heads (the B operand, same permuted
-//            512-dim order) stay in registers, so each key is unpacked once.
-//            The packed rows are copied to LDS (280 B apart).  Softmax in
-//            base 2: tile maxima of the 4 producers meet in LDS; the running
-//            maximum moves only past a slack, and when it moves the new
-//            maxima are published with a flag; weights go to LDS as bf16.
+// 64 keys.  The waves specialise by role and by a 128-dim slice of the
+// latent, and two workgroups share a CU (both roles fit in 128 registers):
+//   producers (waves pd = 0..3) compute partial scores S^T = K Q^T over
+//            dims 128pd .. +127 for all 64 keys of tile s.  Lane (li, lq)
+//            loads, one tile ahead, the 16 code bytes of dims 128pd + 32lq
+//            .. +31 of keys 16kt + li (kt = 0..3) and their scale bytes;
+//            gfx950's v_cvt_scalef32_pk_bf16_fp4 turns each code dword into
+//            8 exact bf16 values -- the A operand of a 16x16x32 bf16 MFMA --
+//            against query fragments of the same dims (B operand, all HB
+//            heads, in registers), so every key is unpacked once.  Each
+//            producer copies its slice of the packed rows to LDS for the
+//            consumer of that slice, keeps its partials of key tile pd and
+//            passes the other three through LDS; after a barrier producer pd
+//            adds the four partials of keys 16pd .. +15 in a fixed order.
+//            Softmax in base 2: tile maxima of the 4 producers meet in LDS;
+//            the running maximum moves only past a slack, and when it moves
+//            the new maxima are published with a flag; weights go to LDS as
+//            bf16.
 //   consumers (waves 4..7) own output dims 128*(w-4) .. +127 of all HB
 //            heads and compute O += P V for tile s - 1.  The B operand needs
 //            8 consecutive keys of one dim (a transpose of the cache layout):
@@ -31,9 +37,11 @@
 //            pairs along dims) and re-pairs the halves along keys with
 //            v_perm_b32: 8 B operands for 8 MFMAs whose output column j is
 //            dim 8j + n of the slab.
-// LDS buffers alternate between tiles; a step costs two barriers.  At the
-// end the sink is folded in, the producers' partial sums are added, and
-// O / l is rounded to bf16.
+// LDS buffers alternate between tiles; a step costs three barriers (partials,
+// maxima, weights), and the consumers do all their work before the first.
+// At the end the sink is folded in, the producers' partial sums are added,
+// and O / l is rounded to bf16.
+#include <type_traits>
 #include "kernels.hpp"
 
 namespace mxs {
@@ -113,6 +121,7 @@ struct AttnSmem {
     struct {
       uint8_t kv[2][kTile][kKvPitch];        // packed rows of a tile
       uint16_t p[2][HB * kPitch];            // a tile's weights (bf16): [head][key]
+      f32x4 sp[kProducers][kProducers - 1][HT][kWave];  // partial scores of the key tiles other producers own
       float red[2][HB][kProducers];          // per-producer tile maxima
       float mpub[2][HB];                     // running maxima after a tile
       uint32_t moved[2];                     // some head's running maximum moved
@@ -123,15 +132,16 @@ struct AttnSmem {
   };
 };
 
+// Two workgroups per CU: at most 128 registers per lane (4 waves per SIMD).
 template <int HB, bool kPow2>
-__global__ __launch_bounds__(kWave * kWaves) void sparse_mla_attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void sparse_mla_attn_kernel(const AttnArgs a) {
   constexpr int HT = HB / 16;
   __shared__ AttnSmem<HB> sm;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lq = lane >> 4;
   const bool producer = w < kProducers;
-  const int kg = w;                  // producer: key group (keys 16kg .. +15 of a tile)
   const int dg = w - kProducers;     // consumer: dims 128dg .. +127
   const uint32_t nhb = (uint32_t)(a.num_heads / HB);
   const uint32_t blk = xcd_contiguous_block();
@@ -139,149 +149,203 @@ __global__ __launch_bounds__(kWave * kWaves) void sparse_mla_attn_kernel(const A
   const int h0 = (int)(blk % nhb) * HB;
   const int64_t ntile = (a.topk + kTile - 1) / kTile;
 
-  const int key = 16 * kg + li;  // a producer lane's key within the tile
   const int32_t* idx_row = a.indices + t * a.idx_stride;
   if (threadIdx.x < 2) sm.loop.moved[threadIdx.x] = 0u;  // ordered by the first barrier
 
   // Producers and consumers run separate loops (so their registers are not
-  // live at the same time) with the same barriers: two per step, step s
+  // live at the same time) with the same barriers: three per step, step s
   // producing tile s and consuming tile s - 1, then two in the epilogue.
+  // The producer body is instantiated per slice (pd a constant: its LDS
+  // offsets and own-tile choice fold away).
   if (producer) {
-    // Query fragments of all HB heads (B operand of S^T = K Q^T: lane (head
-    // li, quarter lq) holds dims 128lq + 8ks .. +8 at k-step ks); running
-    // maxima and partial sums of heads 16ht + li.
-    bf16x8 qf[HT][16];
-    float m_qk[HT], lsum[HT];
+    auto produce = [&](auto pdc) {
+      // Producer pd = w owns dims 128pd .. +127 of every key of a tile: lane
+      // (li, lq) holds, for key tile kt = 0..3, the 16 code bytes of dims
+      // 128pd + 32lq .. +31 of key 16kt + li and their scale byte, and the
+      // query fragments of those dims for all HB heads (B operand: head li,
+      // dims 128pd + 32lq + 8ks .. +7 at k-step ks).  Its MFMAs give partial
+      // scores over its 128 dims for all 64 keys; the four partials meet in
+      // LDS, where producer w sums those of key tile w (keys 16w .. +15).
+      constexpr int pd = decltype(pdc)::value;
+      bf16x8 qf[HT][4];
+      float m_qk[HT], lsum[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      m_qk[ht] = -INFINITY;
-      lsum[ht] = 0.0f;
-      const uint16_t* qh = a.q + t * a.q_token_stride + (int64_t)(h0 + 16 * ht + li) * a.q_head_stride + 128 * lq;
+      for (int ht = 0; ht < HT; ++ht) {
+        m_qk[ht] = -INFINITY;
+        lsum[ht] = 0.0f;
+        const uint16_t* qh = a.q + t * a.q_token_stride + (int64_t)(h0 + 16 * ht + li) * a.q_head_stride +
+                             128 * pd + 32 * lq;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks)
-        qf[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 8 * ks));
-    }
-    // Loads are unconditional (addresses clamped, results masked), so the
-    // compiler can count outstanding loads precisely instead of draining
-    // them at every branch join; they run only when topk >= 1.
-    auto load_index = [&](int64_t tile) -> int32_t {
-      const int64_t j = tile * kTile + key;
-      const int32_t v = idx_row[j < a.topk ? j : a.topk - 1];
-      return j < a.topk ? v : -1;
-    };
-    auto row_index = [&](int32_t s) -> int32_t {
-      const bool ok = s >= 0 && (uint32_t)s < a.map.num_slots;
-      return ok ? (int32_t)a.map.template row<kPow2>((uint32_t)s) : -1;
-    };
-    auto gather_k = [&](int32_t row, u32x4 (&c)[4], uint32_t& sd) {
-      const uint8_t* rp = a.cache + (int64_t)(row < 0 ? 0 : row) * kRowBytes;
-      const u32x4* cp = reinterpret_cast<const u32x4*>(rp + 64 * lq);
+        for (int ks = 0; ks < 4; ++ks)
+          qf[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 8 * ks));
+      }
+      // Slot index of key 16lq + li (one load per lane covers the tile);
+      // unconditional (address clamped, result masked) so the compiler's wait
+      // counts stay exact.  Loads run only when topk >= 1.
+      auto load_index = [&](int64_t tile) -> int32_t {
+        const int64_t j = tile * kTile + 16 * lq + li;
+        const int32_t v = idx_row[j < a.topk ? j : a.topk - 1];
+        return j < a.topk ? v : -1;
+      };
+      auto row_index = [&](int32_t s) -> int32_t {
+        const bool ok = s >= 0 && (uint32_t)s < a.map.num_slots;
+        return ok ? (int32_t)a.map.template row<kPow2>((uint32_t)s) : -1;
+      };
+      // Rows of keys 16kt + li, kt = 0..3, from the lanes (li, kt) that hold
+      // them (permlane swaps: lane (li, lq) ends with the value of lane (li, kt)).
+      auto spread_rows = [&](int32_t x, int32_t (&rows)[4]) {
+        const auto ab = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        const auto c0 = __builtin_amdgcn_permlane16_swap(ab[0], ab[0], false, false);
+        const auto c1 = __builtin_amdgcn_permlane16_swap(ab[1], ab[1], false, false);
+        rows[0] = (int32_t)c0[0];
+        rows[1] = (int32_t)c0[1];
+        rows[2] = (int32_t)c1[0];
+        rows[3] = (int32_t)c1[1];
+      };
+      auto gather = [&](const int32_t (&rows)[4], u32x4 (&c)[4], uint32_t (&sd)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = cp[i];
-      sd = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * lq);
-    };
-    // The gather of a tile is issued right after the previous tile's scores
-    // (one tile ahead); slot indices are loaded one tile earlier still.
-    int32_t g_row = -1, g_idx = -1;
-    u32x4 g_cw[4];
-    uint32_t g_sd = 0;
-    if (ntile > 0) {
-      g_row = row_index(load_index(0));
-      gather_k(g_row, g_cw, g_sd);
-      g_idx = load_index(1);
-    }
-
-    for (int64_t step = 0; step <= ntile; ++step) {
-      const int pb = (int)(step & 1), cb = pb ^ 1;
-      float x[HT][4];
-      if (step < ntile) {
-        // ---- scores S^T[key][head]; the packed rows go to LDS for the consumers
-        const bool key_valid = g_row >= 0;
-        const uint32_t vbits = ((uint32_t)__ballot(key_valid) >> (4 * lq)) & 0xFu;  // keys 4lq + r
-        if (!key_valid) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) g_cw[i] = u32x4{0u, 0u, 0u, 0u};
-          g_sd = 0x7F7F7F7Fu;
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint8_t* rp = a.cache + (int64_t)(rows[kt] < 0 ? 0 : rows[kt]) * kRowBytes;
+          c[kt] = *reinterpret_cast<const u32x4*>(rp + 64 * pd + 16 * lq);
+          sd[kt] = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * pd);
         }
-        {
-          uint8_t* dst = sm.loop.kv[pb][key];
+      };
+      // The gather of a tile is issued right after the previous tile's scores
+      // (one tile ahead); slot indices are loaded one tile earlier still.
+      int32_t g_own = -1, g_idx = -1;  // row of key 16lq + li; next tile's index
+      u32x4 g_cw[4];
+      uint32_t g_sd[4];
+      if (ntile > 0) {
+        g_own = row_index(load_index(0));
+        int32_t rows[4];
+        spread_rows(g_own, rows);
+        gather(rows, g_cw, g_sd);
+        g_idx = load_index(1);
+      }
+
+      for (int64_t step = 0; step <= ntile; ++step) {
+        const int pb = (int)(step & 1), cb = pb ^ 1;
+        float x[HT][4];
+        uint32_t vbits = 0;
+        if (step < ntile) {
+          // ---- the packed slice to LDS for consumer pd; partial scores
+          const uint64_t valid = __ballot(g_own >= 0);  // bit k: key k of the tile
+          vbits = (uint32_t)(valid >> (16 * pd + 4 * lq)) & 0xFu;  // keys 16pd + 4lq + r
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint64_t*>(dst + 64 * lq + 16 * i) = (uint64_t)g_cw[i][0] | ((uint64_t)g_cw[i][1] << 32);
-            *reinterpret_cast<uint64_t*>(dst + 64 * lq + 16 * i + 8) = (uint64_t)g_cw[i][2] | ((uint64_t)g_cw[i][3] << 32);
+          for (int kt = 0; kt < 4; ++kt) {
+            if (!((valid >> (16 * kt + li)) & 1u)) {
+              g_cw[kt] = u32x4{0u, 0u, 0u, 0u};
+              g_sd[kt] = 0x7F7F7F7Fu;
+            }
+            uint8_t* dst = sm.loop.kv[pb][16 * kt + li];
+            *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq) = (uint64_t)g_cw[kt][0] | ((uint64_t)g_cw[kt][1] << 32);
+            *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq + 8) = (uint64_t)g_cw[kt][2] | ((uint64_t)g_cw[kt][3] << 32);
+            if (lq == 0) *reinterpret_cast<uint32_t*>(dst + 256 + 4 * pd) = g_sd[kt];
           }
-          *reinterpret_cast<uint32_t*>(dst + 256 + 4 * lq) = g_sd;
+          // Key tile by key tile: partial scores over the 128 dims; those of
+          // the other producers' tiles go to LDS, the own tile's stay in x
+          // (summed in producer order after the barrier).
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            f32x4 s[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) s[ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t sbyte = (g_sd[kt] >> (8 * lq)) & 0xFFu;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const bf16x8 kf = __builtin_bit_cast(bf16x8, unpack8(g_cw[kt][ks], sbyte));
+#pragma unroll
+              for (int ht = 0; ht < HT; ++ht)
+                s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ht][ks], s[ht], 0, 0, 0);
+            }
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+              if (kt != pd) {
+                sm.loop.sp[pd][(kt - pd - 1) & 3][ht][lane] = s[ht];
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[ht][r] = s[ht][r];
+              }
+            }
+          }
+          // ---- next tile's gather (the index load goes first: waiting for it
+          // later must not wait for the gather, as loads complete in order)
+          const int32_t nxt = g_idx;
+          g_idx = load_index(step + 2);
+          g_own = row_index(nxt);
+          int32_t rows[4];
+          spread_rows(g_own, rows);
+          gather(rows, g_cw, g_sd);
         }
-        f32x4 s[HT][2];
+        __syncthreads();
+        if (step < ntile) {
+          // ---- full scores of keys 16pd + 4lq + r (sum over the producers in
+          // a fixed order), tile maxima (base 2); invalid keys become -inf
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) s[ht][0] = s[ht][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int ht = 0; ht < HT; ++ht) {
+            f32x4 part[4];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          const bf16x8 kf =
-              __builtin_bit_cast(bf16x8, unpack8(g_cw[ks >> 2][ks & 3], (g_sd >> (8 * (ks >> 2))) & 0xFFu));
+            for (int v = 0; v < 4; ++v)
+              part[v] = v == pd ? f32x4{x[ht][0], x[ht][1], x[ht][2], x[ht][3]} : sm.loop.sp[v][(pd - v - 1) & 3][ht][lane];
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht)
-            s[ht][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ht][ks], s[ht][ks & 1], 0, 0, 0);
+            for (int r = 0; r < 4; ++r) {
+              const float sc = (part[0][r] + part[1][r]) + (part[2][r] + part[3][r]);
+              x[ht][r] = ((vbits >> r) & 1u) ? sc * a.c : -INFINITY;
+            }
+            const float mx = max_over_quarters(fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])));
+            if (lq == 0) sm.loop.red[pb][16 * ht + li][pd] = mx;
+          }
         }
-        // ---- next tile's gather (the index load goes first: waiting for it
-        // later must not wait for the gather, as loads complete in order)
-        const int32_t nxt = g_idx;
-        g_idx = load_index(step + 2);
-        g_row = row_index(nxt);
-        gather_k(g_row, g_cw, g_sd);
-        // ---- tile maxima (base 2).  Lane (head li, quarter lq) holds
-        // S[head 16ht + li][key 16kg + 4lq + r]; invalid keys become -inf.
+        __syncthreads();
+        if (step < ntile) {
+          // ---- running maxima, weights, partial sums; publish
+          if (threadIdx.x == 0) sm.loop.moved[cb] = 0u;  // the consumers read it before the first barrier
+          bool moved = false;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
+          for (int ht = 0; ht < HT; ++ht) {
+            const float* red = sm.loop.red[pb][16 * ht + li];
+            const float mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            const float mnew = mt > m_qk[ht] + kMaxSlack ? mt : m_qk[ht];
+            const float alpha = mnew != m_qk[ht] ? __builtin_amdgcn_exp2f(m_qk[ht] - mnew) : 1.0f;
+            moved |= mnew != m_qk[ht];
+            m_qk[ht] = mnew;
+            float p[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[ht][r] = ((vbits >> r) & 1u) ? (s[ht][0][r] + s[ht][1][r]) * a.c : -INFINITY;
-          const float mx = max_over_quarters(fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])));
-          if (lq == 0) sm.loop.red[pb][16 * ht + li][kg] = mx;
+            for (int r = 0; r < 4; ++r) p[r] = mnew == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[ht][r] - mnew);
+            lsum[ht] = lsum[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            *reinterpret_cast<uint64_t*>(&sm.loop.p[pb][(16 * ht + li) * kPitch + 16 * pd + 4 * lq]) =
+                (uint64_t)bf16x2_rn(p[0], p[1]) | ((uint64_t)bf16x2_rn(p[2], p[3]) << 32);
+            if (pd == 0 && lq == 0) sm.loop.mpub[pb][16 * ht + li] = mnew;
+          }
+          if (__any(moved) && lane == 0) sm.loop.moved[pb] = 1u;
         }
+        __syncthreads();
       }
-      __syncthreads();
-      if (step < ntile) {
-        // ---- running maxima, weights, partial sums; publish
-        if (threadIdx.x == 0) sm.loop.moved[cb] = 0u;  // the consumers read it before this barrier
-        bool moved = false;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          const float* red = sm.loop.red[pb][16 * ht + li];
-          const float mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-          const float mnew = mt > m_qk[ht] + kMaxSlack ? mt : m_qk[ht];
-          const float alpha = mnew != m_qk[ht] ? __builtin_amdgcn_exp2f(m_qk[ht] - mnew) : 1.0f;
-          moved |= mnew != m_qk[ht];
-          m_qk[ht] = mnew;
-          float p[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = mnew == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[ht][r] - mnew);
-          lsum[ht] = lsum[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-          *reinterpret_cast<uint64_t*>(&sm.loop.p[pb][(16 * ht + li) * kPitch + 16 * kg + 4 * lq]) =
-              (uint64_t)bf16x2_rn(p[0], p[1]) | ((uint64_t)bf16x2_rn(p[2], p[3]) << 32);
-          if (kg == 0 && lq == 0) sm.loop.mpub[pb][16 * ht + li] = mnew;
-        }
-        if (__any(moved) && lane == 0) sm.loop.moved[pb] = 1u;
-      }
-      __syncthreads();
-    }
 
-    // ---- sink and partial sums
-    float l[HT];
+      // ---- sink and partial sums
+      float l[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      l[ht] = sum_over_quarters(lsum[ht]);
-      if (a.sink) {
-        const float s2 = a.sink[h0 + 16 * ht + li] * kLog2e;
-        const float mf = fmaxf(m_qk[ht], s2);
-        l[ht] = m_qk[ht] == -INFINITY ? 0.0f : l[ht] * __builtin_amdgcn_exp2f(m_qk[ht] - mf);
-        if (kg == 0) l[ht] += __builtin_amdgcn_exp2f(s2 - mf);
+      for (int ht = 0; ht < HT; ++ht) {
+        l[ht] = sum_over_quarters(lsum[ht]);
+        if (a.sink) {
+          const float s2 = a.sink[h0 + 16 * ht + li] * kLog2e;
+          const float mf = fmaxf(m_qk[ht], s2);
+          l[ht] = m_qk[ht] == -INFINITY ? 0.0f : l[ht] * __builtin_amdgcn_exp2f(m_qk[ht] - mf);
+          if (pd == 0) l[ht] += __builtin_amdgcn_exp2f(s2 - mf);
+        }
       }
-    }
-    __syncthreads();  // the loop's LDS is reused
+      __syncthreads();  // the loop's LDS is reused
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      if (lq == 0) sm.fin.l[kg][16 * ht + li] = l[ht];
-    __syncthreads();
+      for (int ht = 0; ht < HT; ++ht)
+        if (lq == 0) sm.fin.l[pd][16 * ht + li] = l[ht];
+      __syncthreads();
+    };
+    switch (w) {
+      case 0: produce(std::integral_constant<int, 0>{}); break;
+      case 1: produce(std::integral_constant<int, 1>{}); break;
+      case 2: produce(std::integral_constant<int, 2>{}); break;
+      default: produce(std::integral_constant<int, 3>{}); break;
+    }
   } else {
     // O rows heads 16ht + 4lq + r, columns dims 128dg + 8li + n, and the
     // running maxima of those rows.
@@ -327,9 +391,9 @@ __global__ __launch_bounds__(kWave * kWaves) void sparse_mla_attn_kernel(const A
         }
       }
     };
-    // Tile step - 1 is consumed across the first barrier, overlapping the
-    // producers' softmax between the two barriers (its buffers are not
-    // rewritten before the next step).
+    // Tile step - 1 is consumed before the first barrier, beside the
+    // producers' scores of tile step (its buffers are rewritten only in the
+    // next step).
     for (int64_t step = 0; step <= ntile; ++step) {
       const int cb = (int)(step & 1) ^ 1;
       if (step > 0) {
@@ -348,9 +412,10 @@ __global__ __launch_bounds__(kWave * kWaves) void sparse_mla_attn_kernel(const A
             }
         }
         pv_step(cb, 0);
+        pv_step(cb, 1);
       }
       __syncthreads();
-      if (step > 0) pv_step(cb, 1);
+      __syncthreads();
       __syncthreads();
     }
 
