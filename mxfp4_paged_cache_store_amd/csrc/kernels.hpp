@@ -81,6 +81,8 @@ struct AttnArgs {
   int64_t q_token_stride;
   int64_t q_head_stride;
   const uint8_t* cache;       // MXFP4 rows of 272 bytes
+  uint32_t cache_bytes;       // byte extent of the cache view if at most kAttnBufBytes (gathers
+                              // through a raw buffer), else 0
   SlotMap map;
   const int32_t* indices;     // [num_tokens, topk], row stride idx_stride
   int64_t topk;
@@ -94,6 +96,10 @@ struct AttnArgs {
   int32_t num_heads;          // multiple of 16
   int64_t num_tokens;
 };
+
+// Largest cache view the attention gathers through a raw buffer (32-bit
+// offsets; offsets from here up read as zeros).
+constexpr uint32_t kAttnBufBytes = 0xFFFF0000u;
 
 // Each returns the hipError_t of the launch.
 hipError_t launch_ring_rows(const RingArgs& a, hipStream_t stream);

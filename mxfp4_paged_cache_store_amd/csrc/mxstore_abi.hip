@@ -370,6 +370,10 @@ int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num
   a.q_token_stride = q_token_stride;
   a.q_head_stride = q_head_stride;
   a.cache = cache;
+  {
+    const __int128 extent = ((__int128)(num_blocks - 1) * block_stride_rows + block_size) * 272;
+    a.cache_bytes = extent <= (__int128)mxs::kAttnBufBytes ? (uint32_t)extent : 0u;
+  }
   a.indices = indices;
   a.topk = topk;
   a.idx_stride = indices_stride;

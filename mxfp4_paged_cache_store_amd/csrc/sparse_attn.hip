@@ -105,10 +105,12 @@ __device__ __forceinline__ uint32_t cvt_byte(uint32_t codes, float scale, int se
 constexpr int kTile = 64;
 constexpr int kProducers = 4;
 constexpr int kPitch = kTile + 8;  // bf16 per LDS weight row (rows stay 16-B aligned)
-// Packed rows in LDS are 280 bytes apart (272 + 8): rows 8 apart then start
-// 16 banks apart, so the consumers' reads of keys 8q + k (q = 0..3) do not
-// collide.
-constexpr int kKvPitch = 280;
+// A key's row in LDS: its 256 code bytes, then the 16 group scales as fp32
+// (E8M0 byte in the exponent field, the form the converter takes), 8 bytes
+// of padding: rows 328 bytes apart, so rows 8 apart start 16 banks apart and
+// the consumers' reads of keys 8q + k (q = 0..3) do not collide.
+constexpr int kKvPitch = 328;
+constexpr int kKvScales = 256;
 // The running maximum is raised only when a tile's maximum exceeds it by more
 // than this (base-2 units): weights stay below 2^8, far from fp32 / bf16
 // overflow, and most tiles need no rescaling of O.
@@ -133,7 +135,7 @@ struct AttnSmem {
 };
 
 // Two workgroups per CU: at most 128 registers per lane (4 waves per SIMD).
-template <int HB, bool kPow2>
+template <int HB, bool kPow2, bool kBuf>
 __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void sparse_mla_attn_kernel(const AttnArgs a) {
   constexpr int HT = HB / 16;
@@ -202,12 +204,23 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         rows[2] = (int32_t)c1[0];
         rows[3] = (int32_t)c1[1];
       };
+      // Through a raw buffer over the cache view when it spans less than
+      // kAttnBufBytes: a skipped key's offset lies past the view, so its
+      // codes and scales read as zeros (zero values); otherwise global loads
+      // of row 0, masked where they are used.
+      const __amdgpu_buffer_rsrc_t crs = buffer_at(a.cache, kBuf ? a.cache_bytes : 0u);
       auto gather = [&](const int32_t (&rows)[4], u32x4 (&c)[4], uint32_t (&sd)[4]) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const uint8_t* rp = a.cache + (int64_t)(rows[kt] < 0 ? 0 : rows[kt]) * kRowBytes;
-          c[kt] = *reinterpret_cast<const u32x4*>(rp + 64 * pd + 16 * lq);
-          sd[kt] = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * pd);
+          if constexpr (kBuf) {
+            const uint32_t base = rows[kt] < 0 ? kAttnBufBytes : (uint32_t)rows[kt] * kRowBytes;
+            c[kt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, base + 64 * pd + 16 * lq, 0, 0));
+            sd[kt] = __builtin_amdgcn_raw_buffer_load_b32(crs, base + 256 + 4 * pd, 0, 0);
+          } else {
+            const uint8_t* rp = a.cache + (int64_t)(rows[kt] < 0 ? 0 : rows[kt]) * kRowBytes;
+            c[kt] = *reinterpret_cast<const u32x4*>(rp + 64 * pd + 16 * lq);
+            sd[kt] = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * pd);
+          }
         }
       };
       // The gather of a tile is issued right after the previous tile's scores
@@ -233,14 +246,14 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           vbits = (uint32_t)(valid >> (16 * pd + 4 * lq)) & 0xFu;  // keys 16pd + 4lq + r
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
-            if (!((valid >> (16 * kt + li)) & 1u)) {
+            if (!kBuf && !((valid >> (16 * kt + li)) & 1u)) {
               g_cw[kt] = u32x4{0u, 0u, 0u, 0u};
-              g_sd[kt] = 0x7F7F7F7Fu;
+              g_sd[kt] = 0u;
             }
             uint8_t* dst = sm.loop.kv[pb][16 * kt + li];
             *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq) = (uint64_t)g_cw[kt][0] | ((uint64_t)g_cw[kt][1] << 32);
             *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq + 8) = (uint64_t)g_cw[kt][2] | ((uint64_t)g_cw[kt][3] << 32);
-            if (lq == 0) *reinterpret_cast<uint32_t*>(dst + 256 + 4 * pd) = g_sd[kt];
+            *reinterpret_cast<float*>(dst + kKvScales + 4 * (4 * pd + lq)) = as_f32(((g_sd[kt] >> (8 * lq)) & 0xFFu) << 23);
           }
           // Key tile by key tile: partial scores over the 128 dims; those of
           // the other producers' tiles go to LDS, the own tile's stay in x
@@ -372,7 +385,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       for (int k = 0; k < 8; ++k) {
         const uint8_t* row = sm.loop.kv[cb][kb + 8 * lq + k];
         vc[k] = *reinterpret_cast<const uint32_t*>(row + 64 * dg + 4 * li);
-        vs[k] = as_f32((uint32_t)row[256 + 4 * dg + (li >> 2)] << 23);
+        vs[k] = *reinterpret_cast<const float*>(row + kKvScales + 4 * (4 * dg + (li >> 2)));
       }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
@@ -449,17 +462,21 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
   }
 }
 
+template <int HB, bool kPow2>
+hipError_t launch_map(const AttnArgs& a, unsigned blocks, hipStream_t stream) {
+  if (a.cache_bytes != 0u)
+    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, kPow2, true>), dim3(blocks), dim3(kWave * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, kPow2, false>), dim3(blocks), dim3(kWave * kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int HB>
 hipError_t launch_hb(const AttnArgs& a, hipStream_t stream) {
   const int64_t blocks = a.num_tokens * (a.num_heads / HB);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (a.map.pow2)
-    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, true>), dim3((unsigned)blocks), dim3(kWave * kWaves), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, false>), dim3((unsigned)blocks), dim3(kWave * kWaves), 0,
-                       stream, a);
-  return hipGetLastError();
+  return a.map.pow2 ? launch_map<HB, true>(a, (unsigned)blocks, stream)
+                    : launch_map<HB, false>(a, (unsigned)blocks, stream);
 }
 
 }  // namespace

@@ -165,3 +165,28 @@ def test_attention_workload_sampled(device):
     tol = tolerance(q_s, cache_h, 1, n, n, idx_s, scale, None, want)
     err = np.abs(got - want)
     assert (err <= tol).all(), float((err / tol).max())
+
+
+def test_attention_cache_past_4gib(device):
+    """A paged view spanning more than 4 GiB (two blocks 16M rows apart):
+    the kernel gathers with 64-bit addresses there (below that, through a
+    raw buffer whose range check zeroes skipped keys).  Same result as the
+    oracle on the compact copy of the two blocks."""
+    case = workloads.attention_case(3, 32, 100, 11, num_blocks=2, block_size=64, sink=True)
+    far = 16_000_000
+    backing = torch.empty(((far + 64) * 272,), dtype=torch.uint8, device=device)
+    view = backing.view(far + 64, 272)
+    rows = torch.from_numpy(case.cache.reshape(2 * 64, 272)).to(device)
+    view[:64] = rows[:64]
+    view[far:far + 64] = rows[64:]
+    q = bf16_dev(case.q, device)
+    idx = torch.from_numpy(np.ascontiguousarray(case.indices)).to(device)
+    sink = torch.from_numpy(case.sink).to(device)
+    log(f"attention over a {backing.numel() / 2**30:.2f} GiB paged view")
+    paged = backing.as_strided((2, 64, 272), (far * 272, 272, 1))
+    out = ops.sparse_mla_attention(q, paged, idx, case.scale, sink=sink)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    want = oracle.sparse_mla_attention(case.q, case.cache, 2, 64, 64, case.indices, case.scale, case.sink)
+    tol = tolerance(case.q, case.cache, 2, 64, 64, case.indices, case.scale, case.sink, want)
+    assert (np.abs(got - want) <= tol).all()
