@@ -308,6 +308,42 @@ int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num
                          uint16_t* out_bf16, int64_t out_token_stride, int64_t out_head_stride,
                          void* stream);
 
+/*
+ * Split-key form of sparse_mla_attention for few query tokens (decode), where
+ * one workgroup per (token, head block) leaves most of the GPU idle [P3
+ * Details, follow-ups: split-K decode over the mxfp4_mla cache -- named, not
+ * described; the merge below is the usual log-sum-exp combination, so the
+ * result is the same attention].  Each (token, head block) is walked by
+ * `splits` workgroups over consecutive ranges of whole 64-key tiles; each
+ * writes its unnormalised output, running maximum and weight sum to
+ * `workspace`, and a second launch merges them (sink folded in there) and
+ * rounds to bf16.  Same arguments and result as sparse_mla_attention (up to
+ * fp32 rounding order), plus:
+ * splits           1 .. 64 (1: exactly sparse_mla_attention, no workspace).
+ * workspace        device buffer of >= sparse_mla_attention_workspace_bytes
+ *                  bytes, 16-byte aligned, overwritten; owned by the caller.
+ * Two launches on `stream` (one when splits is 1).
+ */
+int sparse_mla_attention_split(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads,
+                               int64_t latent, int64_t q_token_stride, int64_t q_head_stride,
+                               const uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                               int64_t block_stride_rows, const int32_t* indices, int64_t topk,
+                               int64_t indices_stride, float scale, const float* sink,
+                               uint16_t* out_bf16, int64_t out_token_stride,
+                               int64_t out_head_stride, int32_t splits, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of sparse_mla_attention_split: num_tokens * num_heads *
+ * splits * 514 fp32 values, rounded up to 256 (0 for splits == 1).
+ * MX_E_RANGE for counts out of range.  Host-only. */
+int64_t sparse_mla_attention_workspace_bytes(int64_t num_tokens, int64_t num_heads,
+                                             int64_t splits);
+
+/* Split count expected to be fastest on MI355X: enough workgroups for two per
+ * CU on 256 CUs, at least two 64-key tiles per split, at most 64; 1 when
+ * the batch already fills the GPU.  Host-only heuristic, no device work. */
+int32_t sparse_mla_attention_splits_advised(int64_t num_tokens, int64_t num_heads, int64_t topk);
+
 /* Message for the last nonzero status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
 const char* mx_last_error(void);

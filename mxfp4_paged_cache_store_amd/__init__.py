@@ -29,6 +29,8 @@ from .ops import (
     row_bytes,
     save_ring_rows,
     sparse_mla_attention,
+    sparse_mla_attention_splits_advised,
+    sparse_mla_attention_workspace_bytes,
     store_mxfp4_mla,
 )
 from ._abi import MxError
@@ -54,5 +56,7 @@ __all__ = [
     "row_bytes",
     "save_ring_rows",
     "sparse_mla_attention",
+    "sparse_mla_attention_splits_advised",
+    "sparse_mla_attention_workspace_bytes",
     "store_mxfp4_mla",
 ]

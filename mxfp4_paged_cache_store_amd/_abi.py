@@ -36,6 +36,9 @@ EXPORTED = (
     "save_ring_rows",
     "fused_save_compress_norm_cr1",
     "sparse_mla_attention",
+    "sparse_mla_attention_split",
+    "sparse_mla_attention_workspace_bytes",
+    "sparse_mla_attention_splits_advised",
     "mx_last_error",
 )
 
@@ -91,6 +94,14 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_attention.restype = ctypes.c_int
         L.sparse_mla_attention.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                            _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _i64, _i64, _vp]
+        L.sparse_mla_attention_split.restype = ctypes.c_int
+        L.sparse_mla_attention_split.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                                 _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _i64, _i64,
+                                                 _i32, _vp, _i64, _vp]
+        L.sparse_mla_attention_workspace_bytes.restype = _i64
+        L.sparse_mla_attention_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        L.sparse_mla_attention_splits_advised.restype = _i32
+        L.sparse_mla_attention_splits_advised.argtypes = [_i64, _i64, _i64]
         L.mx_last_error.restype = ctypes.c_char_p
         L.mx_last_error.argtypes = []
         _lib = L

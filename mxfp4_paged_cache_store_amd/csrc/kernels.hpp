@@ -95,6 +95,9 @@ struct AttnArgs {
   bool out_aligned;           // out 16-byte aligned, strides multiples of 8
   int32_t num_heads;          // multiple of 16
   int64_t num_tokens;
+  int32_t splits;             // key ranges per (token, head block); > 1: partials to ws
+  float* ws;                  // splits > 1: fp32 [T*H*splits][512] unnormalised outputs, then
+                              // [T*H*splits][2] (running maximum in base 2, weight sum)
 };
 
 // Largest cache view the attention gathers through a raw buffer (32-bit

@@ -340,12 +340,15 @@ int fused_save_compress_norm_cr1(const float* kv_score, int64_t num_tokens, int6
   return launched(mxs::launch_compress_norm_cr1(a, (hipStream_t)stream), "fused_save_compress_norm_cr1");
 }
 
-int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads, int64_t latent,
+constexpr int kMaxAttnSplits = 64;
+
+static int attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads, int64_t latent,
                          int64_t q_token_stride, int64_t q_head_stride, const uint8_t* cache,
                          int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
                          const int32_t* indices, int64_t topk, int64_t indices_stride, float scale,
                          const float* sink, uint16_t* out_bf16, int64_t out_token_stride,
-                         int64_t out_head_stride, void* stream) {
+                         int64_t out_head_stride, int32_t splits, void* workspace, int64_t workspace_bytes,
+                         void* stream, const char* name) {
   mxs::AttnArgs a{};
   if (latent != 512) return fail(MX_E_SHAPE, "latent must be 512, got %lld", (long long)latent);
   int rc = check_paged(latent, 32, num_blocks, block_size, block_stride_rows, &a.map);
@@ -361,7 +364,16 @@ int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num
     return fail(MX_E_STRIDE, "strides must cover a head row, a token's heads and a token's topk indices");
   if (q_head_stride % 8 || q_token_stride % 8)
     return fail(MX_E_ALIGN, "query strides must be multiples of 8 elements (16-byte rows)");
+  if (splits < 1 || splits > kMaxAttnSplits)
+    return fail(MX_E_RANGE, "splits must be in [1, %d], got %d", kMaxAttnSplits, splits);
+  if (splits > 1) {
+    const int64_t need = sparse_mla_attention_workspace_bytes(num_tokens, num_heads, splits);
+    if (workspace_bytes < need)
+      return fail(MX_E_RANGE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes, (long long)need);
+  }
   if (num_tokens == 0) return ok();
+  if (splits > 1 && !workspace) return fail(MX_E_NULL, "null workspace");
+  if (splits > 1 && !aligned(workspace, 16)) return fail(MX_E_ALIGN, "workspace must be 16-byte aligned");
   if (!q_bf16 || !cache || (!indices && topk > 0) || !out_bf16) return fail(MX_E_NULL, "null device pointer");
   if (!aligned(q_bf16, 16) || !aligned(cache, 16) || !aligned(indices, 4) || !aligned(out_bf16, 2) ||
       (sink && !aligned(sink, 4)))
@@ -385,7 +397,53 @@ int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num
   a.out_aligned = aligned(out_bf16, 16) && out_token_stride % 8 == 0 && out_head_stride % 8 == 0;
   a.num_heads = (int32_t)num_heads;
   a.num_tokens = num_tokens;
-  return launched(mxs::launch_sparse_mla_attn(a, (hipStream_t)stream), "sparse_mla_attention");
+  a.splits = splits;
+  a.ws = static_cast<float*>(workspace);
+  return launched(mxs::launch_sparse_mla_attn(a, (hipStream_t)stream), name);
+}
+
+int sparse_mla_attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads, int64_t latent,
+                         int64_t q_token_stride, int64_t q_head_stride, const uint8_t* cache,
+                         int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
+                         const int32_t* indices, int64_t topk, int64_t indices_stride, float scale,
+                         const float* sink, uint16_t* out_bf16, int64_t out_token_stride,
+                         int64_t out_head_stride, void* stream) {
+  return attention(q_bf16, num_tokens, num_heads, latent, q_token_stride, q_head_stride, cache, num_blocks,
+                   block_size, block_stride_rows, indices, topk, indices_stride, scale, sink, out_bf16,
+                   out_token_stride, out_head_stride, 1, nullptr, 0, stream, "sparse_mla_attention");
+}
+
+int64_t sparse_mla_attention_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t splits) {
+  if (num_tokens < 0 || num_tokens > 0x7FFFFFFF || num_heads < 1 || num_heads > 1024 || splits < 1 ||
+      splits > kMaxAttnSplits)
+    return MX_E_RANGE;
+  if (splits == 1) return 0;
+  return ((num_tokens * num_heads * splits * (512 + 2) * 4 + 255) / 256) * 256;
+}
+
+int32_t sparse_mla_attention_splits_advised(int64_t num_tokens, int64_t num_heads, int64_t topk) {
+  if (num_tokens < 1 || num_heads < 16 || num_heads % 16 || topk < 1) return 1;
+  // Two workgroups per CU on 256 CUs; each key range keeps at least two
+  // 64-key tiles so that its gathers overlap its scores.
+  const int64_t blocks = num_tokens * (num_heads / (num_heads % 32 == 0 ? 32 : 16));
+  const int64_t tiles = (topk + 63) / 64;
+  int64_t s = (512 + blocks - 1) / blocks;
+  if (s > tiles / 2) s = tiles / 2;
+  if (s > kMaxAttnSplits) s = kMaxAttnSplits;
+  return s < 2 ? 1 : (int32_t)s;
+}
+
+int sparse_mla_attention_split(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_heads, int64_t latent,
+                               int64_t q_token_stride, int64_t q_head_stride, const uint8_t* cache,
+                               int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
+                               const int32_t* indices, int64_t topk, int64_t indices_stride, float scale,
+                               const float* sink, uint16_t* out_bf16, int64_t out_token_stride,
+                               int64_t out_head_stride, int32_t splits, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  return attention(q_bf16, num_tokens, num_heads, latent, q_token_stride, q_head_stride, cache, num_blocks,
+                   block_size, block_stride_rows, indices, topk, indices_stride, scale, sink, out_bf16,
+                   out_token_stride, out_head_stride, splits, workspace, workspace_bytes, stream,
+                   "sparse_mla_attention_split");
 }
 
 const char* mx_last_error(void) { return g_err; }

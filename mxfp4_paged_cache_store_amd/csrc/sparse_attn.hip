@@ -135,7 +135,7 @@ struct AttnSmem {
 };
 
 // Two workgroups per CU: at most 128 registers per lane (4 waves per SIMD).
-template <int HB, bool kPow2, bool kBuf>
+template <int HB, bool kPow2, bool kBuf, bool kSplit>
 __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void sparse_mla_attn_kernel(const AttnArgs a) {
   constexpr int HT = HB / 16;
@@ -146,10 +146,18 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
   const bool producer = w < kProducers;
   const int dg = w - kProducers;     // consumer: dims 128dg .. +127
   const uint32_t nhb = (uint32_t)(a.num_heads / HB);
-  const uint32_t blk = xcd_contiguous_block();
+  // Split form: consecutive blocks take consecutive key ranges (whole tiles)
+  // of one (token, head block).
+  const uint32_t nsplit = kSplit ? (uint32_t)a.splits : 1u;
+  const uint32_t blk_all = xcd_contiguous_block();
+  const uint32_t split = kSplit ? blk_all % nsplit : 0u;
+  const uint32_t blk = kSplit ? blk_all / nsplit : blk_all;
   const int64_t t = blk / nhb;
   const int h0 = (int)(blk % nhb) * HB;
-  const int64_t ntile = (a.topk + kTile - 1) / kTile;
+  const int64_t ntile_all = (a.topk + kTile - 1) / kTile;
+  const int64_t per_split = (ntile_all + nsplit - 1) / nsplit;
+  const int64_t tile0 = (int64_t)split * per_split;
+  const int64_t ntile = kSplit ? (tile0 < ntile_all ? min(per_split, ntile_all - tile0) : 0) : ntile_all;
 
   const int32_t* idx_row = a.indices + t * a.idx_stride;
   if (threadIdx.x < 2) sm.loop.moved[threadIdx.x] = 0u;  // ordered by the first barrier
@@ -185,7 +193,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // unconditional (address clamped, result masked) so the compiler's wait
       // counts stay exact.  Loads run only when topk >= 1.
       auto load_index = [&](int64_t tile) -> int32_t {
-        const int64_t j = tile * kTile + 16 * lq + li;
+        const int64_t j = (tile0 + tile) * kTile + 16 * lq + li;
         const int32_t v = idx_row[j < a.topk ? j : a.topk - 1];
         return j < a.topk ? v : -1;
       };
@@ -340,7 +348,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         l[ht] = sum_over_quarters(lsum[ht]);
-        if (a.sink) {
+        if (a.sink && !kSplit) {  // the split form folds the sink in when merging
           const float s2 = a.sink[h0 + 16 * ht + li] * kLog2e;
           const float mf = fmaxf(m_qk[ht], s2);
           l[ht] = m_qk[ht] == -INFINITY ? 0.0f : l[ht] * __builtin_amdgcn_exp2f(m_qk[ht] - mf);
@@ -440,13 +448,27 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 16 * ht + 4 * lq + r;
+        const float lt = (sm.fin.l[0][h] + sm.fin.l[1][h]) + (sm.fin.l[2][h] + sm.fin.l[3][h]);
+        if constexpr (kSplit) {
+          // Unnormalised partial output and (running maximum, weight sum)
+          // of this key range, merged by attn_merge_kernel.
+          const int64_t prow = ((t * a.num_heads + h0 + h) * nsplit + split);
+          f32x4* po = reinterpret_cast<f32x4*>(a.ws + prow * 512 + 128 * dg + 8 * li);
+          po[0] = f32x4{o[ht][0][r], o[ht][1][r], o[ht][2][r], o[ht][3][r]};
+          po[1] = f32x4{o[ht][4][r], o[ht][5][r], o[ht][6][r], o[ht][7][r]};
+          if (dg == 0 && li == 0) {
+            float* pml = a.ws + a.num_tokens * a.num_heads * nsplit * 512 + prow * 2;
+            pml[0] = m_pv[ht][r];
+            pml[1] = lt;
+          }
+          continue;
+        }
         float sc = 1.0f;
         if (a.sink) {
           const float s2 = a.sink[h0 + h] * kLog2e;
           const float mf = fmaxf(m_pv[ht][r], s2);
           sc = m_pv[ht][r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_pv[ht][r] - mf);
         }
-        const float lt = (sm.fin.l[0][h] + sm.fin.l[1][h]) + (sm.fin.l[2][h] + sm.fin.l[3][h]);
         float v[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) v[n] = lt > 0.0f ? (o[ht][n][r] * sc) / lt : 0.0f;
@@ -462,21 +484,84 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
   }
 }
 
-template <int HB, bool kPow2>
+// Merge of the split form: one wave per (token, head); lane l owns dims
+// 8l .. 8l+7.  With M the largest running maximum of the key ranges (and the
+// sink logit, base 2), out = sum_i 2^(m_i - M) O_i / (sum_i 2^(m_i - M) l_i
+// + 2^(sink - M)): the same value as one pass over all keys; zeros when no
+// range saw a valid key.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
+  if (row >= a.num_tokens * a.num_heads) return;
+  const int64_t t = row / a.num_heads;
+  const int h = (int)(row % a.num_heads);
+  const int ns = a.splits;
+  const float* ml = a.ws + a.num_tokens * a.num_heads * ns * 512 + row * ns * 2;
+  float mx = -INFINITY;
+  for (int i = 0; i < ns; ++i) mx = fmaxf(mx, ml[2 * i]);
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float lt = 0.0f;
+  if (mx != -INFINITY) {
+    float mf = mx, sink_w = 0.0f;
+    if (a.sink) {
+      const float s2 = a.sink[h] * kLog2e;
+      mf = fmaxf(mx, s2);
+      sink_w = __builtin_amdgcn_exp2f(s2 - mf);
+    }
+    for (int i = 0; i < ns; ++i) {
+      const float mi = ml[2 * i];
+      if (mi == -INFINITY) continue;
+      const float wi = __builtin_amdgcn_exp2f(mi - mf);
+      lt += ml[2 * i + 1] * wi;
+      const f32x4* po = reinterpret_cast<const f32x4*>(a.ws + (row * ns + i) * 512 + 8 * lane);
+      const f32x4 p0 = po[0], p1 = po[1];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        acc[n] += p0[n] * wi;
+        acc[4 + n] += p1[n] * wi;
+      }
+    }
+    lt += sink_w;
+  }
+  float v[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) v[n] = lt > 0.0f ? acc[n] / lt : 0.0f;
+  const u32x4 b = {bf16x2_rn(v[0], v[1]), bf16x2_rn(v[2], v[3]), bf16x2_rn(v[4], v[5]), bf16x2_rn(v[6], v[7])};
+  uint16_t* orow = a.out + t * a.out_token_stride + (int64_t)h * a.out_head_stride + 8 * lane;
+  if (a.out_aligned) {
+    *reinterpret_cast<u32x4*>(orow) = b;
+  } else {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) orow[n] = (uint16_t)(b[n >> 1] >> (16 * (n & 1)));
+  }
+}
+
+template <int HB, bool kPow2, bool kSplit>
 hipError_t launch_map(const AttnArgs& a, unsigned blocks, hipStream_t stream) {
   if (a.cache_bytes != 0u)
-    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, kPow2, true>), dim3(blocks), dim3(kWave * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, kPow2, true, kSplit>), dim3(blocks), dim3(kWave * kWaves), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, kPow2, false>), dim3(blocks), dim3(kWave * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_attn_kernel<HB, kPow2, false, kSplit>), dim3(blocks), dim3(kWave * kWaves), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
 template <int HB>
 hipError_t launch_hb(const AttnArgs& a, hipStream_t stream) {
-  const int64_t blocks = a.num_tokens * (a.num_heads / HB);
+  const int64_t blocks = a.num_tokens * (a.num_heads / HB) * a.splits;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  return a.map.pow2 ? launch_map<HB, true>(a, (unsigned)blocks, stream)
-                    : launch_map<HB, false>(a, (unsigned)blocks, stream);
+  hipError_t e;
+  if (a.splits > 1) {
+    e = a.map.pow2 ? launch_map<HB, true, true>(a, (unsigned)blocks, stream)
+                   : launch_map<HB, false, true>(a, (unsigned)blocks, stream);
+    if (e != hipSuccess) return e;
+    const int64_t rows = a.num_tokens * a.num_heads;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  return a.map.pow2 ? launch_map<HB, true, false>(a, (unsigned)blocks, stream)
+                    : launch_map<HB, false, false>(a, (unsigned)blocks, stream);
 }
 
 }  // namespace

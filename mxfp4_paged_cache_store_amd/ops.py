@@ -223,13 +223,30 @@ def fused_save_compress_norm_cr1(kv_score: torch.Tensor, slot_mapping: torch.Ten
         _stream(stream)))
 
 
+def sparse_mla_attention_splits_advised(num_tokens: int, num_heads: int, topk: int) -> int:
+    """Split count the library advises for this shape (1: no split)."""
+    return int(_abi.lib().sparse_mla_attention_splits_advised(num_tokens, num_heads, topk))
+
+
+def sparse_mla_attention_workspace_bytes(num_tokens: int, num_heads: int, splits: int) -> int:
+    n = int(_abi.lib().sparse_mla_attention_workspace_bytes(num_tokens, num_heads, splits))
+    if n < 0:
+        _abi.check(n)
+    return n
+
+
 def sparse_mla_attention(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, scale: float,
                          sink: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                         stream=None) -> torch.Tensor:
+                         stream=None, splits: int | None = None,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Sparse MLA attention of bf16 queries [T, H, 512] over the listed slots
     (int32 [T, topk], invalid entries skipped) of a paged MXFP4 cache (the
     view rules of ``store_mxfp4_mla``), keys = values = the dequantized rows;
-    optional fp32 per-head sinks [P3 read path].  Returns bf16 [T, H, 512]."""
+    optional fp32 per-head sinks [P3 read path].  Returns bf16 [T, H, 512].
+    ``splits`` > 1 walks each (token, head block) as that many key ranges
+    and merges them (the split form for few tokens); None takes the library's
+    advice.  The split form needs a device ``workspace`` (uint8, at least
+    ``sparse_mla_attention_workspace_bytes``); one is allocated when None."""
     _need_cuda(q, cache, indices)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 512 or q.stride(2) != 1:
         raise ValueError("q must be bf16 [tokens, heads, 512] with unit inner stride")
@@ -244,12 +261,23 @@ def sparse_mla_attention(q: torch.Tensor, cache: torch.Tensor, indices: torch.Te
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if out.dtype != torch.bfloat16 or out.shape != q.shape or out.stride(2) != 1:
         raise ValueError("out must be bf16 shaped like q with unit inner stride")
-    _abi.check(_abi.lib().sparse_mla_attention(
-        q.data_ptr(), q.shape[0], q.shape[1], 512, q.stride(0), q.stride(1), cache.data_ptr(),
-        num_blocks, block_size, stride_rows, indices.data_ptr(), indices.shape[1],
-        max(indices.stride(0), indices.shape[1]),
-        float(scale), None if sink is None else sink.data_ptr(), out.data_ptr(), out.stride(0),
-        out.stride(1), _stream(stream)))
+    tokens, heads, topk = q.shape[0], q.shape[1], indices.shape[1]
+    if splits is None:
+        splits = sparse_mla_attention_splits_advised(tokens, heads, topk)
+    args = (q.data_ptr(), tokens, heads, 512, q.stride(0), q.stride(1), cache.data_ptr(),
+            num_blocks, block_size, stride_rows, indices.data_ptr(), topk,
+            max(indices.stride(0), topk), float(scale), None if sink is None else sink.data_ptr(),
+            out.data_ptr(), out.stride(0), out.stride(1))
+    if splits == 1:
+        _abi.check(_abi.lib().sparse_mla_attention(*args, _stream(stream)))
+        return out
+    need = sparse_mla_attention_workspace_bytes(tokens, heads, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the query's device")
+    _abi.check(_abi.lib().sparse_mla_attention_split(*args, int(splits), workspace.data_ptr(),
+                                                     workspace.numel(), _stream(stream)))
     return out
 
 

@@ -288,3 +288,41 @@ def test_attention_rejects(mxlib, kw, status):
 
 def test_attention_empty_is_a_noop(mxlib):
     assert attn(mxlib, n=0, q=0, cache=0, idx=0, out=0) == _abi.MX_OK
+
+
+def attn_split(mxlib, splits, ws, ws_bytes, **kw):
+    a = dict(q=FAKE, n=3, h=16, latent=512, qts=16 * 512, qhs=512, cache=FAKE, nb=4, bs=64, bsr=64,
+             idx=FAKE, topk=128, istride=128, scale=0.05, sink=None, out=FAKE, ots=16 * 512, ohs=512)
+    a.update(kw)
+    return mxlib.sparse_mla_attention_split(a["q"], a["n"], a["h"], a["latent"], a["qts"], a["qhs"], a["cache"],
+                                            a["nb"], a["bs"], a["bsr"], a["idx"], a["topk"], a["istride"],
+                                            a["scale"], a["sink"], a["out"], a["ots"], a["ohs"], splits, ws,
+                                            ws_bytes, None)
+
+
+def test_attention_split_workspace_and_advice(mxlib):
+    wsb = mxlib.sparse_mla_attention_workspace_bytes
+    assert wsb(3, 16, 1) == 0
+    assert wsb(3, 16, 4) == ((3 * 16 * 4 * 514 * 4 + 255) // 256) * 256
+    assert wsb(64, 32, 8) == 64 * 32 * 8 * 514 * 4          # already a multiple of 256
+    assert wsb(3, 16, 0) == _abi.MX_E_RANGE and wsb(3, 16, 65) == _abi.MX_E_RANGE
+    assert wsb(-1, 16, 2) == _abi.MX_E_RANGE and wsb(3, 0, 2) == _abi.MX_E_RANGE
+    adv = mxlib.sparse_mla_attention_splits_advised
+    assert adv(4096, 32, 2048) == 1          # 4096 workgroups already fill the GPU
+    assert adv(64, 32, 2048) == 8            # 64 workgroups -> 512
+    assert adv(1, 32, 2048) == 16            # capped at two tiles per range (32 tiles)
+    assert adv(1, 128, 65536) == 64          # capped at 64 ranges
+    assert adv(8, 32, 64) == 1               # one tile: nothing to split
+    assert adv(8, 48, 2048) == 16            # 16-head blocks: 8 * 3 workgroups
+    assert adv(0, 32, 2048) == 1 and adv(8, 24, 2048) == 1 and adv(8, 32, 0) == 1
+
+
+def test_attention_split_rejects(mxlib):
+    need = mxlib.sparse_mla_attention_workspace_bytes(3, 16, 4)
+    assert attn_split(mxlib, 0, FAKE, need) == _abi.MX_E_RANGE
+    assert attn_split(mxlib, 65, FAKE, need) == _abi.MX_E_RANGE
+    assert attn_split(mxlib, 4, FAKE, need - 1) == _abi.MX_E_RANGE
+    assert attn_split(mxlib, 4, None, need) == _abi.MX_E_NULL
+    assert attn_split(mxlib, 4, FAKE + 8, need) == _abi.MX_E_ALIGN
+    assert attn_split(mxlib, 4, FAKE, need, h=24) == _abi.MX_E_SHAPE   # the shared checks still apply
+    assert attn_split(mxlib, 4, None, 0, n=0, q=0, cache=0, idx=0, out=0) == _abi.MX_OK

@@ -63,7 +63,7 @@ def tolerance(q_bits, cache, nb, bs, bsr, idx, scale, sink, exact):
     return tol
 
 
-def run_gpu(device, case: workloads.AttnCase, out_pad: int = 0):
+def run_gpu(device, case: workloads.AttnCase, out_pad: int = 0, splits: int = 1):
     t, h, _ = case.q.shape
     cache = u8_dev(case.cache, device)
     if case.block_stride_rows != case.block_size or case.num_blocks > 1:
@@ -73,16 +73,16 @@ def run_gpu(device, case: workloads.AttnCase, out_pad: int = 0):
     sink = None if case.sink is None else torch.from_numpy(case.sink).to(device)
     backing = torch.full((t, h, 512 + out_pad), -7.0, dtype=torch.bfloat16, device=device)
     out = backing[:, :, :512]
-    log(f"attention T={t} H={h} topk={case.indices.shape[1]} sink={case.sink is not None}")
-    ops.sparse_mla_attention(q, cache, idx, case.scale, sink=sink, out=out)
+    log(f"attention T={t} H={h} topk={case.indices.shape[1]} sink={case.sink is not None} splits={splits}")
+    ops.sparse_mla_attention(q, cache, idx, case.scale, sink=sink, out=out, splits=splits)
     torch.cuda.synchronize()
     if out_pad:
         assert (backing[:, :, 512:] == -7.0).all(), "padding written"
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def check_case(device, case: workloads.AttnCase, out_pad: int = 0):
-    got = run_gpu(device, case, out_pad)
+def check_case(device, case: workloads.AttnCase, out_pad: int = 0, splits: int = 1):
+    got = run_gpu(device, case, out_pad, splits)
     want = oracle.sparse_mla_attention(case.q, case.cache, case.num_blocks, case.block_size,
                                        case.block_stride_rows, case.indices, case.scale, case.sink)
     tol = tolerance(case.q, case.cache, case.num_blocks, case.block_size, case.block_stride_rows,
@@ -151,7 +151,7 @@ def test_attention_workload_sampled(device):
     oracle, all heads."""
     q, cache, idx, scale = workloads.attention_workload_device()
     log(f"attention workload T={q.shape[0]} H={q.shape[1]} topk={idx.shape[1]}")
-    out = ops.sparse_mla_attention(q, cache, idx, scale)
+    out = ops.sparse_mla_attention(q, cache, idx, scale, splits=1)
     torch.cuda.synchronize()
     rng = np.random.default_rng(9)
     pick = np.unique(np.concatenate([[0, q.shape[0] - 1], rng.choice(q.shape[0], 4, replace=False)]))
@@ -184,9 +184,68 @@ def test_attention_cache_past_4gib(device):
     sink = torch.from_numpy(case.sink).to(device)
     log(f"attention over a {backing.numel() / 2**30:.2f} GiB paged view")
     paged = backing.as_strided((2, 64, 272), (far * 272, 272, 1))
-    out = ops.sparse_mla_attention(q, paged, idx, case.scale, sink=sink)
+    out = ops.sparse_mla_attention(q, paged, idx, case.scale, sink=sink, splits=1)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     want = oracle.sparse_mla_attention(case.q, case.cache, 2, 64, 64, case.indices, case.scale, case.sink)
     tol = tolerance(case.q, case.cache, 2, 64, 64, case.indices, case.scale, case.sink, want)
     assert (np.abs(got - want) <= tol).all()
+
+
+@pytest.mark.parametrize("tokens,heads,topk,sink,seed,splits", [
+    (4, 16, 256, True, 21, 2),     # two ranges of two tiles
+    (5, 32, 200, True, 22, 3),     # ragged last tile; the third range is empty
+    (3, 48, 130, False, 23, 5),    # three tiles over five ranges (two empty)
+    (2, 64, 512, True, 24, 8),     # one tile per range
+    (3, 32, 1000, False, 25, 64),  # the largest split count
+])
+def test_attention_split_parity(device, tokens, heads, topk, sink, seed, splits):
+    """The split-key form (partials per key range, merged by log-sum-exp)
+    against the oracle, within the same tolerance as one pass."""
+    case = workloads.attention_case(tokens, heads, topk, seed, sink=sink)
+    worst = check_case(device, case, splits=splits)
+    log(f"split {splits}: worst error / tolerance = {worst:.3f}")
+
+
+def test_attention_split_degenerate_tokens(device):
+    """Split form: a token with no valid slot gives zeros (with sinks too);
+    a token with one valid slot listed once reproduces that row exactly."""
+    case = workloads.attention_case(3, 16, 320, 26, sink=False)
+    idx = np.full((3, 320), -1, dtype=np.int32)
+    idx[1, 250] = 17
+    idx[2, ::3] = np.arange(107) % 64
+    case.indices = idx
+    for sink in (None, np.linspace(-2, 2, 16).astype(np.float32)):
+        case.sink = sink
+        got = run_gpu(device, case, splits=4)
+        assert (got[0] == 0).all()
+        if sink is None:
+            row = dequant_rows(case.cache, case.num_blocks, case.block_size, case.block_stride_rows,
+                               np.array([17]))[0]
+            assert (got[1] == row[None, :]).all()
+        check_case(device, case, splits=4)
+
+
+def test_attention_decode_workload_split(device):
+    """64 decode queries (the last 64 of a 16,384-token context, top-2048
+    slots each) in the advised split form and in one pass: 8 sampled tokens
+    of both against the oracle."""
+    q, cache, idx, scale = workloads.attention_workload_device(tokens=64)
+    splits = ops.sparse_mla_attention_splits_advised(64, q.shape[1], idx.shape[1])
+    assert splits > 1
+    log(f"attention decode workload T=64 splits={splits}")
+    out = ops.sparse_mla_attention(q, cache, idx, scale)
+    one = ops.sparse_mla_attention(q, cache, idx, scale, splits=1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    pick = np.sort(rng.choice(64, 8, replace=False))
+    pick_dev = torch.from_numpy(pick).to(q.device)
+    q_s = q[pick_dev].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    idx_s = idx[pick_dev].cpu().numpy()
+    cache_h = cache.cpu().numpy().reshape(-1)
+    n = cache.shape[0]
+    want = oracle.sparse_mla_attention(q_s, cache_h, 1, n, n, idx_s, scale)
+    tol = tolerance(q_s, cache_h, 1, n, n, idx_s, scale, None, want)
+    for form in (out, one):
+        got = form[pick_dev].float().cpu().numpy().astype(np.float64)
+        assert (np.abs(got - want) <= tol).all(), float((np.abs(got - want) / tol).max())
