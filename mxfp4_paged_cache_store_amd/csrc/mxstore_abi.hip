@@ -367,6 +367,8 @@ static int attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_hea
   if (splits < 1 || splits > kMaxAttnSplits)
     return fail(MX_E_RANGE, "splits must be in [1, %d], got %d", kMaxAttnSplits, splits);
   if (splits > 1) {
+    if (num_tokens * num_heads * splits > 0x7FFFFFFF)
+      return fail(MX_E_RANGE, "num_tokens * num_heads * splits must stay below 2^31");
     const int64_t need = sparse_mla_attention_workspace_bytes(num_tokens, num_heads, splits);
     if (workspace_bytes < need)
       return fail(MX_E_RANGE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes, (long long)need);

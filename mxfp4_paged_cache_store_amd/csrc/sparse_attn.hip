@@ -484,50 +484,98 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
   }
 }
 
-// Merge of the split form: one wave per (token, head); lane l owns dims
-// 8l .. 8l+7.  With M the largest running maximum of the key ranges (and the
-// sink logit, base 2), out = sum_i 2^(m_i - M) O_i / (sum_i 2^(m_i - M) l_i
-// + 2^(sink - M)): the same value as one pass over all keys; zeros when no
-// range saw a valid key.
-__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
+// Merge of the split form.  With M the largest running maximum of the key
+// ranges (and the sink logit, base 2), out = sum_i 2^(m_i - M) O_i /
+// (sum_i 2^(m_i - M) l_i + 2^(sink - M)): the same value as one pass over
+// all keys; zeros when no range saw a valid key.  A (token, head) row is
+// merged by wpr = 1, 2, 4 or 8 waves (ceil(ranges / 8), at most 64 ranges):
+// lane i reads range i's (m, l); wave sub of the row adds the outputs of
+// ranges sub, sub + wpr, ... (lane l: dims 8l .. +7, all loads issued at
+// once) and the row's waves meet in LDS.  A workgroup of 8 waves holds
+// 8 / wpr rows.
+constexpr int kMergeWaves = 8;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_add(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(kWave * kMergeWaves) void attn_merge_kernel(const AttnArgs a, int wpr) {
+  __shared__ f32x4 part[kMergeWaves][kWave][2];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
-  if (row >= a.num_tokens * a.num_heads) return;
-  const int64_t t = row / a.num_heads;
-  const int h = (int)(row % a.num_heads);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = w % wpr;
+  const int64_t row = (int64_t)blockIdx.x * (kMergeWaves / wpr) + w / wpr;  // t * num_heads + h
+  const bool live = row < a.num_tokens * a.num_heads;
   const int ns = a.splits;
-  const float* ml = a.ws + a.num_tokens * a.num_heads * ns * 512 + row * ns * 2;
-  float mx = -INFINITY;
-  for (int i = 0; i < ns; ++i) mx = fmaxf(mx, ml[2 * i]);
-  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  float lt = 0.0f;
-  if (mx != -INFINITY) {
+  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+  float mx = -INFINITY, lt = 0.0f;
+  if (live) {
+    const float* ml = a.ws + a.num_tokens * a.num_heads * ns * 512 + row * ns * 2;
+    float mi = -INFINITY, li_ = 0.0f;
+    if (lane < ns) {
+      mi = ml[2 * lane];
+      li_ = ml[2 * lane + 1];
+    }
+    mx = wave_max(mi);
     float mf = mx, sink_w = 0.0f;
-    if (a.sink) {
-      const float s2 = a.sink[h] * kLog2e;
+    if (a.sink && mx != -INFINITY) {
+      const float s2 = a.sink[row % a.num_heads] * kLog2e;
       mf = fmaxf(mx, s2);
       sink_w = __builtin_amdgcn_exp2f(s2 - mf);
     }
-    for (int i = 0; i < ns; ++i) {
-      const float mi = ml[2 * i];
-      if (mi == -INFINITY) continue;
-      const float wi = __builtin_amdgcn_exp2f(mi - mf);
-      lt += ml[2 * i + 1] * wi;
-      const f32x4* po = reinterpret_cast<const f32x4*>(a.ws + (row * ns + i) * 512 + 8 * lane);
-      const f32x4 p0 = po[0], p1 = po[1];
+    const float wi = mi == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mi - mf);
+    lt = wave_add(li_ * wi) + sink_w;
+    f32x4 p[8][2];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        acc[n] += p0[n] * wi;
-        acc[4 + n] += p1[n] * wi;
+    for (int k = 0; k < 8; ++k) {
+      const int i = sub + wpr * k;
+      if (i < ns) {
+        const f32x4* po = reinterpret_cast<const f32x4*>(a.ws + (row * ns + i) * 512 + 8 * lane);
+        p[k][0] = po[0];
+        p[k][1] = po[1];
       }
     }
-    lt += sink_w;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = sub + wpr * k;
+      if (i < ns) {
+        const float wk = __shfl(wi, i);
+        acc0 += p[k][0] * wk;
+        acc1 += p[k][1] * wk;
+      }
+    }
   }
+  if (wpr > 1) {
+    part[w][lane][0] = acc0;
+    part[w][lane][1] = acc1;
+    __syncthreads();
+    if (sub != 0) return;
+#pragma unroll
+    for (int k = 1; k < kMergeWaves; ++k) {
+      if (k < wpr) {
+        acc0 += part[w + k][lane][0];
+        acc1 += part[w + k][lane][1];
+      }
+    }
+  }
+  if (!live) return;
   float v[8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) v[n] = lt > 0.0f ? acc[n] / lt : 0.0f;
+  for (int n = 0; n < 4; ++n) {
+    v[n] = mx != -INFINITY && lt > 0.0f ? acc0[n] / lt : 0.0f;
+    v[4 + n] = mx != -INFINITY && lt > 0.0f ? acc1[n] / lt : 0.0f;
+  }
   const u32x4 b = {bf16x2_rn(v[0], v[1]), bf16x2_rn(v[2], v[3]), bf16x2_rn(v[4], v[5]), bf16x2_rn(v[6], v[7])};
-  uint16_t* orow = a.out + t * a.out_token_stride + (int64_t)h * a.out_head_stride + 8 * lane;
+  const int64_t t = row / a.num_heads;
+  uint16_t* orow = a.out + t * a.out_token_stride + (row % a.num_heads) * a.out_head_stride + 8 * lane;
   if (a.out_aligned) {
     *reinterpret_cast<u32x4*>(orow) = b;
   } else {
@@ -557,7 +605,10 @@ hipError_t launch_hb(const AttnArgs& a, hipStream_t stream) {
                    : launch_map<HB, false, true>(a, (unsigned)blocks, stream);
     if (e != hipSuccess) return e;
     const int64_t rows = a.num_tokens * a.num_heads;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    const int wpr = a.splits <= 8 ? 1 : a.splits <= 16 ? 2 : a.splits <= 32 ? 4 : 8;
+    const int64_t mblocks = (rows * wpr + kMergeWaves - 1) / kMergeWaves;
+    if (mblocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mblocks), dim3(kWave * kMergeWaves), 0, stream, a, wpr);
     return hipGetLastError();
   }
   return a.map.pow2 ? launch_map<HB, true, false>(a, (unsigned)blocks, stream)
