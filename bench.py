@@ -7,9 +7,11 @@ A step is one MXFP4 store of the whole batch: 4,500,000 tokens x 512 bf16
 scattered batch the library advises its slot-order form, so a step is
 mxfp4_build_inverse + mxfp4_store_by_slot; the scatter form (mxfp4_store) is
 timed beside it.  The roofline entry is for the dominant kernel (the
-slot-order store), timed alone with HIP events.  The gather-dequant and the
-two RoPE+quant inserts are timed after it, each on its own workload, and
-reported under "companions".
+slot-order store): HIP events around its launch in every timed step give
+its average duration there.  The companions (gather-dequant, ring save,
+CR1 norm, the read-side attention in one pass and in the split-key decode
+form, the three RoPE+quant inserts) are timed after it, each on its own
+workload, and reported under "companions".
 
 Output: one JSON line (see the fields below).  `--sweep` prints further
 lines for the token-count / slot-pattern sweep with the Infinity Cache
@@ -366,16 +368,39 @@ def main():
 
     print(f"[bench] timing {args.steps} steps ({'slot order' if slot_order else 'scatter'})",
           file=sys.stderr, flush=True)
-    wall, ev = time_launches(step, args.steps, args.warmup, torch)
-    step_s = ev / args.steps
+    # The timed region: K steps back to back.  HIP events around the store
+    # kernel's launch inside each step give its average duration there (all
+    # launches go to torch's current stream).
+    stream = torch.cuda.current_stream()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def timed_step(i):
+        if slot_order:
+            ops.mxfp4_build_inverse(slots, 1, num_slots, inv)
+        kev[i][0].record(stream)
+        store_by_slot() if slot_order else scatter_step()
+        kev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        timed_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = ev0.elapsed_time(ev1) / 1000.0 / args.steps
+    per_launch = sum(a.elapsed_time(b) for a, b in kev) / 1000.0 / args.steps
     if slot_order:
         kernel = "mxfp4_store_by_slot_kernel<512>"
-        _, kev = time_launches(store_by_slot, args.steps, args.warmup, torch)
-        per_launch = kev / args.steps
         algo_bytes = valid * BY_SLOT_BYTES_PER_TOKEN + num_slots * BY_SLOT_BYTES_PER_SLOT
     else:
         kernel = "mxfp4_store_kernel<512>"
-        per_launch = step_s
         algo_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
     _, sev = time_launches(scatter_step, args.steps, args.warmup, torch)
     scatter_s = sev / args.steps
