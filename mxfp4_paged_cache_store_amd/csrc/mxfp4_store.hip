@@ -29,13 +29,17 @@
 //   * The 16 scale bytes are gathered with row_shr DPP moves into four
 //     dwords held by lanes 12, 28, 44 and 60.  The row is written as whole
 //     dwords: 64 code dwords + 4 scale dwords.  When a wave's tokens fill
-//     consecutive slots the stores are plain (L2 merges neighbouring rows
-//     into whole lines); scattered rows use non-temporal stores.
-//   * Slots are read by the scalar unit, a whole wave's in one load.  A pad
-//     or out-of-range slot skips the token's load as well as its store: the
-//     load goes through a raw buffer descriptor whose range is the token's
-//     row, or empty for a skipped token (the hardware range check returns
-//     zeros without touching memory).  All addressing is 64-bit.
+//     consecutive slots, or the whole batch's rows fit in the Infinity
+//     Cache, the stores are plain (L2 and that cache merge neighbouring rows
+//     into whole lines); other scattered rows use non-temporal stores.
+//   * A wave's slots come in one vector load issued ahead of its rows, and
+//     the rows do not wait for them: a pad or out-of-range slot skips the
+//     token's store (its row is read and dropped).  Loads and stores go
+//     through raw buffer descriptors whose range is the token's row / the
+//     slot's row, empty past the batch or for a skipped slot (the hardware
+//     range check returns zeros or drops the access without touching
+//     memory).  Latents below 512 put several tokens in a pass and skip a
+//     pad token's load too.  All addressing is 64-bit.
 #include "kernels.hpp"
 
 namespace mxs {
