@@ -226,6 +226,30 @@ def test_attention_split_degenerate_tokens(device):
         check_case(device, case, splits=4)
 
 
+def test_attention_split_workspace_reuse(device):
+    """A workspace full of arbitrary bytes, reused across calls with different
+    token counts and split counts (and each call made twice), gives the
+    oracle's result every time: the split form keeps no state in it between
+    calls."""
+    ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device=device)
+    for tokens, splits, seed in ((3, 4, 31), (5, 2, 32), (2, 8, 33), (3, 4, 34)):
+        case = workloads.attention_case(tokens, 32, 300, seed, sink=True)
+        q = bf16_dev(case.q, device)
+        idx = torch.from_numpy(np.ascontiguousarray(case.indices)).to(device)
+        sink = torch.from_numpy(case.sink).to(device)
+        log(f"attention split workspace reuse T={tokens} splits={splits}")
+        for _ in range(2):
+            out = ops.sparse_mla_attention(q, u8_dev(case.cache, device), idx, case.scale, sink=sink,
+                                           splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy().astype(np.float64)
+            want = oracle.sparse_mla_attention(case.q, case.cache, case.num_blocks, case.block_size,
+                                               case.block_stride_rows, case.indices, case.scale, case.sink)
+            tol = tolerance(case.q, case.cache, case.num_blocks, case.block_size, case.block_stride_rows,
+                            case.indices, case.scale, case.sink, want)
+            assert (np.abs(got - want) <= tol).all()
+
+
 def test_attention_decode_workload_split(device):
     """64 decode queries (the last 64 of a 16,384-token context, top-2048
     slots each) in the advised split form and in one pass: 8 sampled tokens
