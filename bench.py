@@ -161,6 +161,39 @@ def cpu_baseline(sample: int):
     }
 
 
+def small_stores(torch, ops, workloads, steps, warmup):
+    """The store on the decode-shaped batch (256 tokens into a paged cache
+    with other layers' rows interleaved) and on the prefill chunk (16,384
+    tokens in 32 request runs, then gather-dequant of the stored slots):
+    both are latency-bound, so they are reported in microseconds per launch
+    (HIP events over back-to-back launches, launch overhead included)."""
+    out = {}
+    reps = max(20, steps)
+    for name, case in (("mxfp4_store_decode", workloads.decode_case()),
+                       ("mxfp4_store_prefill", workloads.prefill_case())):
+        src = torch.from_numpy(case.src.view("int16")).cuda().view(torch.bfloat16)
+        slots = torch.from_numpy(case.slots).cuda()
+        cache = torch.from_numpy(case.fresh_cache()).cuda()
+        nb, bs, bsr = case.num_blocks, case.block_size, case.block_stride_rows
+        _, ev = time_launches(lambda: ops.mxfp4_store(src, slots, cache, nb, bs, bsr), reps, warmup, torch)
+        per = ev / reps
+        valid = int((case.slots >= 0).sum())
+        entry = {
+            "workload": f"{case.src.shape[0]} tokens ({valid} valid) into {nb} blocks x {bs} slots, "
+                        f"block stride {bsr} rows",
+            "us_per_launch": round(per * 1e6, 2),
+            "tokens_per_s": round(valid / per, 1),
+        }
+        if case.gather_slots is not None:
+            gs = torch.from_numpy(case.gather_slots).cuda()
+            dq = torch.empty((gs.numel(), 512), dtype=torch.bfloat16, device="cuda")
+            _, ev = time_launches(lambda: ops.mxfp4_gather_dequant(cache, nb, bs, bsr, 512, gs, dq), reps,
+                                  warmup, torch)
+            entry["gather_dequant_us_per_launch"] = round(ev / reps * 1e6, 2)
+        out[name] = entry
+    return out
+
+
 def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
     out = {}
     # gather-dequant of every slot of the large cache back to bf16
@@ -460,6 +493,7 @@ def main():
     if not args.no_companions:
         print("[bench] companions", file=sys.stderr, flush=True)
         result["companions"] = companions(torch, ops, workloads, args.steps, args.warmup, cache, n)
+        result["companions"].update(small_stores(torch, ops, workloads, args.steps, args.warmup))
     del src, slots, inv
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
