@@ -482,6 +482,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes,
             "kernel_us_per_launch": round(per_launch * 1e6, 2),
+            "traffic_bytes_per_token": None if traffic is None else round(traffic / valid, 1),
         },
         "scatter_form": {
             "kernel": "mxfp4_store_kernel<512>",
