@@ -1,6 +1,7 @@
 """The entry points can be captured in a HIP graph: every replay, with eager
 work and synchronisations in between, writes the same bytes as eager calls.
-(No entry point records a memset: the inverse map is cleared by a kernel.)"""
+(No entry point records a memset: the inverse map is cleared by a kernel,
+and the split attention keeps nothing in its workspace between calls.)"""
 
 import numpy as np
 import pytest
@@ -26,6 +27,13 @@ def test_graph_replays_match_eager(device):
     r_lat = bf16_dev(rc.latent, device)
     r_pos, r_cs, r_slots = i64_dev(rc.positions, device), torch.from_numpy(rc.cos_sin).to(device), i64_dev(rc.slots, device)
     r_kv = torch.empty((16, 64, 528), dtype=torch.uint8, device=device)
+    # a decode step's read side over the cache the scatter store just wrote:
+    # one pass and the split-key form (its workspace allocated up front)
+    a_q = torch.empty((8, 32, 512), dtype=torch.bfloat16, device=device)
+    a_idx = torch.randint(-1, 1 << 16, (8, 512), dtype=torch.int32, device=device)
+    a_out = torch.empty_like(a_q)
+    a_out1 = torch.empty_like(a_q)
+    a_ws = torch.empty(ops.sparse_mla_attention_workspace_bytes(8, 32, 4), dtype=torch.uint8, device=device)
 
     def work():
         ops.mxfp4_build_inverse(g_slots, 1, n, inv)
@@ -33,6 +41,8 @@ def test_graph_replays_match_eager(device):
         ops.mxfp4_store(p_src, p_slots, p_cache, 1, 1 << 16, 1 << 16)
         ops.mxfp4_gather_dequant(p_cache, 1, 1 << 16, 1 << 16, 512, p_slots, dq_out)
         ops.mxfp8_rope_store(r_lat, r_pos, r_cs, r_kv, r_slots, rc.compress_ratio)
+        ops.sparse_mla_attention(a_q, p_cache, a_idx, 0.04, out=a_out, splits=4, workspace=a_ws)
+        ops.sparse_mla_attention(a_q, p_cache, a_idx, 0.04, out=a_out1, splits=1)
 
     def reset(seed):
         gen = torch.Generator(device=device)
@@ -43,6 +53,9 @@ def test_graph_replays_match_eager(device):
         p_cache.fill_(0xA5)
         dq_out.fill_(0)
         r_kv.fill_(0xA5)
+        a_q.normal_(generator=gen)
+        a_out.fill_(0)
+        a_out1.fill_(0)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -62,10 +75,12 @@ def test_graph_replays_match_eager(device):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [g_cache.clone(), p_cache.clone(), dq_out.clone(), r_kv.clone()]
+        got = [g_cache.clone(), p_cache.clone(), dq_out.clone(), r_kv.clone(), a_out.clone(), a_out1.clone()]
         reset(100 + rep)
         work()  # eager
         torch.cuda.synchronize()
-        want = [g_cache, p_cache, dq_out, r_kv]
-        for name, a, b in zip(("slot-order store", "scatter store", "dequant", "mxfp8 insert"), got, want):
+        want = [g_cache, p_cache, dq_out, r_kv, a_out, a_out1]
+        names = ("slot-order store", "scatter store", "dequant", "mxfp8 insert", "attention split",
+                 "attention one pass")
+        for name, a, b in zip(names, got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rep, name)
