@@ -273,3 +273,29 @@ def test_attention_decode_workload_split(device):
     for form in (out, one):
         got = form[pick_dev].float().cpu().numpy().astype(np.float64)
         assert (np.abs(got - want) <= tol).all(), float((np.abs(got - want) / tol).max())
+
+
+def test_attention_most_heads(device):
+    """The largest head count (1024 = 32 blocks of 32 heads), one pass and
+    split, against the oracle."""
+    case = workloads.attention_case(2, 1024, 100, 41, sink=True)
+    check_case(device, case)
+    check_case(device, case, splits=2)
+
+
+def test_attention_long_sparse_list(device):
+    """A listed-slot row of 1,048,576 entries of which 300 are valid, spread
+    over the whole row (16,384 tiles, most of them empty): one pass and 16
+    key ranges, against the oracle; the index loads reach past 2^20
+    entries."""
+    case = workloads.attention_case(2, 16, 0, 42, sink=True)
+    topk = 1 << 20
+    rng = np.random.default_rng(43)
+    idx = np.full((2, topk), -1, dtype=np.int32)
+    for t in range(2):
+        pos = rng.choice(topk, 300, replace=False)
+        idx[t, pos] = rng.integers(0, case.num_blocks * case.block_size, size=300)
+    idx[1, -1] = 5   # the very last entry
+    case.indices = idx
+    check_case(device, case)
+    check_case(device, case, splits=16)
