@@ -299,3 +299,28 @@ def test_attention_long_sparse_list(device):
     case.indices = idx
     check_case(device, case)
     check_case(device, case, splits=16)
+
+
+def test_attention_strided_query(device):
+    """The query as the first 512 of 576 values per head (the rope-free part
+    of a [T, H, 576] MLA query), one pass and split; same result as the
+    contiguous query."""
+    case = workloads.attention_case(3, 32, 200, 44, sink=True)
+    t, h, _ = case.q.shape
+    wide = torch.zeros((t, h, 576), dtype=torch.bfloat16, device=device)
+    wide[:, :, :512] = bf16_dev(case.q, device)
+    wide[:, :, 512:] = 1e4  # must not be read
+    q = wide[:, :, :512]
+    cache = u8_dev(case.cache, device)
+    idx = torch.from_numpy(np.ascontiguousarray(case.indices)).to(device)
+    sink = torch.from_numpy(case.sink).to(device)
+    want = oracle.sparse_mla_attention(case.q, case.cache, case.num_blocks, case.block_size,
+                                       case.block_stride_rows, case.indices, case.scale, case.sink)
+    tol = tolerance(case.q, case.cache, case.num_blocks, case.block_size, case.block_stride_rows,
+                    case.indices, case.scale, case.sink, want)
+    for splits in (1, 3):
+        log(f"attention strided query splits={splits}")
+        out = ops.sparse_mla_attention(q, cache, idx, case.scale, sink=sink, splits=splits)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert (np.abs(got - want) <= tol).all()
