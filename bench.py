@@ -298,6 +298,29 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
             "us_per_launch": round(per * 1e6, 2),
             "GBps": round(nbytes / per / 1e9, 1),
         }
+    del lat, pos, sl, kv
+    # the same inserts at bandwidth scale: 1,048,576 tokens, compress ratio 1
+    # (every token written), random positions and a permutation of the slots
+    n_big = 1 << 20
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    lat = torch.empty((n_big, 512), dtype=torch.float32, device="cuda").normal_(generator=g).to(torch.bfloat16)
+    pos = torch.randint(0, cs.shape[0], (n_big,), generator=g, device="cuda")
+    sl = torch.randperm(n_big, generator=g, device="cuda")
+    for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
+                            ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
+                            ("v4_rope_store", ops.v4_rope_store, 584)):
+        kv = torch.zeros((n_big // 64, 64, width), dtype=torch.uint8, device="cuda")
+        _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, 1), max(3, steps // 3), warmup, torch)
+        per = ev / max(3, steps // 3)
+        nbytes = n_big * (1024 + 256 + 16 + width)
+        out[name + "_large"] = {
+            "workload": f"{n_big} tokens, CR 1 (all written), {width}-byte records, scattered slots",
+            "us_per_launch": round(per * 1e6, 2),
+            "GBps": round(nbytes / per / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        del kv
     return out
 
 

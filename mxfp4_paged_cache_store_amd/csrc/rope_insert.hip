@@ -26,11 +26,14 @@
 //          rotated RoPE values as bf16 (nearest-even, NaN -> 0x7FC0), then
 //          7 UE8M0 bytes and one zero padding byte in the page's scale area.
 //
-// Layout on CDNA4: one wave per token; lane l holds values 8l..8l+7 (pairs
-// 4l..4l+3), so the RoPE pairs live in lanes 56..63, an MXFP8 group is a DPP
-// quad, a V4 group a half-row of 8 lanes and an NVFP4 tile a lane pair.
-// E4M3 and E2M1 conversions use gfx950's v_cvt_scalef32_pk_fp8_f32 /
-// v_cvt_scalef32_pk_fp4_f32 with scale 1.0.
+// Layout on CDNA4: a wave quantizes one token at a time (at ratio 1 and from
+// 2^16 tokens up, 2 or 4 tokens per wave with every load issued up front);
+// lane l holds values 8l..8l+7 (pairs 4l..4l+3), so the RoPE pairs live in
+// lanes 56..63, an MXFP8 group is a DPP quad, a V4 group a half-row of 8
+// lanes and an NVFP4 tile a lane pair.  E4M3 and E2M1 conversions use
+// gfx950's v_cvt_scalef32_pk_fp8_f32 / v_cvt_scalef32_pk_fp4_f32 with scale
+// 1.0; the NVFP4 quotient r / S is a product with an fp64 reciprocal that
+// leads to the same E2M1 code as the correctly rounded fp32 quotient.
 #include "kernels.hpp"
 
 namespace mxs {
@@ -40,8 +43,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTokensPerWave = 1;  // measured: more waves beat a per-wave token loop
 constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ void load_cs(const RopeArgs& a, int64_t base, int lane, float c[4], float sn[4]);
+__device__ __forceinline__ void rotate_cs(const RopeArgs& a, const u32x4 w, const float c[4], const float sn[4],
+                                          float r[8]);
+__device__ __forceinline__ void page_of(const RopeArgs& a, int64_t s, int64_t& page_off, uint32_t& in_page);
 
 // Gate + rotation for one token.  Returns false (uniformly) when the token is
 // not written.  On success r[0..7] hold the lane's rotated values.
@@ -62,16 +69,31 @@ __device__ __forceinline__ bool rope_token(const RopeArgs& a, int64_t t, int lan
   if (base < 0 || base >= a.cos_rows) return false;
 
   const u32x4 w = *reinterpret_cast<const u32x4*>(a.latent + t * 512 + lane * 8);
-  float c[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-  float sn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (lane >= 56) {
-    const float* cs = a.cos_sin + base * a.cos_stride + (lane - 56) * 4;
+  float c[4], sn[4];
+  load_cs(a, base, lane, c, sn);
+  rotate_cs(a, w, c, sn, r);
+  page_of(a, s, page_off, in_page);
+  return true;
+}
+
+// cos/sin of the lane's 4 pairs from row `base` (lanes 56..63, the RoPE
+// pairs); (1, 0) for the NoPE lanes.  Every lane loads (from a row of the
+// table), so the loads need no branch.
+__device__ __forceinline__ void load_cs(const RopeArgs& a, int64_t base, int lane, float c[4], float sn[4]) {
+  const float* cs = a.cos_sin + base * a.cos_stride + (lane & 7) * 4;
+  const bool rope = lane >= 56;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = cs[i];
-      sn[i] = cs[32 + i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const float ci = cs[i], si = cs[32 + i];
+    c[i] = rope ? ci : 1.0f;
+    sn[i] = rope ? si : 0.0f;
   }
+}
+
+// The lane's 8 values of a token after the rotation, NaN -> +0 when
+// sanitising.
+__device__ __forceinline__ void rotate_cs(const RopeArgs& a, const u32x4 w, const float c[4], const float sn[4],
+                                          float r[8]) {
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -88,6 +110,10 @@ __device__ __forceinline__ bool rope_token(const RopeArgs& a, int64_t t, int lan
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = (r[i] == r[i]) ? r[i] : 0.0f;
   }
+}
+
+// Page byte offset and row within the page of a valid slot.
+__device__ __forceinline__ void page_of(const RopeArgs& a, int64_t s, int64_t& page_off, uint32_t& in_page) {
   const uint32_t s32 = (uint32_t)s;
   uint32_t page;
   if (a.block_shift >= 0) {
@@ -98,7 +124,6 @@ __device__ __forceinline__ bool rope_token(const RopeArgs& a, int64_t t, int lan
     in_page = s32 - page * a.block;
   }
   page_off = (int64_t)page * a.page_stride;
-  return true;
 }
 
 __device__ __forceinline__ float max_abs8(const float r[8]) {
@@ -115,20 +140,12 @@ __device__ __forceinline__ uint32_t e4m3x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p) & 0xFFFFu;
 }
 
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp8_rope_kernel(const RopeArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kTokensPerWave;
-  const float inv448 = (float)(1.0 / 448.0);
-
-  for (int p = 0; p < kTokensPerWave; ++p) {
-    const int64_t t = first + p;
-    if (t >= a.num_tokens) break;
-    float r[8];
-    int64_t page_off;
-    uint32_t in_page;
-    if (!rope_token(a, t, lane, r, page_off, in_page)) continue;
-
+// MXFP8 record of one token (r: the lane's rotated values).
+struct Mxfp8 {
+  static constexpr int kTpw = 2;  // tokens per wave at ratio 1 (measured)
+  static __device__ __forceinline__ void finish(const RopeArgs& a, int lane, const float r[8],
+                                                int64_t page_off, uint32_t in_page) {
+    const float inv448 = (float)(1.0 / 448.0);
     float amax = max_abs8(r);
     amax = fmaxf(amax, as_f32(dpp<kQuadSwap1>(as_u32(amax))));
     amax = fmaxf(amax, as_f32(dpp<kQuadSwap2>(as_u32(amax))));
@@ -157,22 +174,14 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp8_rope_kernel(cons
     *reinterpret_cast<u32x2*>(values + lane * 8) = u32x2{lo, hi};
     if ((lane & 15) == 12) reinterpret_cast<uint32_t*>(scales)[lane >> 4] = sdw;
   }
-}
+};
 
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void nvfp4_rope_kernel(const RopeArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kTokensPerWave;
-  const float inv6 = (float)(1.0 / 6.0);
-
-  for (int p = 0; p < kTokensPerWave; ++p) {
-    const int64_t t = first + p;
-    if (t >= a.num_tokens) break;
-    float r[8];
-    int64_t page_off;
-    uint32_t in_page;
-    if (!rope_token(a, t, lane, r, page_off, in_page)) continue;
-
+// NVFP4 record of one token.
+struct Nvfp4 {
+  static constexpr int kTpw = 4;
+  static __device__ __forceinline__ void finish(const RopeArgs& a, int lane, const float r[8],
+                                                int64_t page_off, uint32_t in_page) {
+    const float inv6 = (float)(1.0 / 6.0);
     float amax = max_abs8(r);
     amax = fmaxf(amax, as_f32(dpp<kQuadSwap1>(as_u32(amax))));  // tile = lane pair
     float sf = amax * inv6;
@@ -182,10 +191,22 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void nvfp4_rope_kernel(cons
     const uint32_t ef = s8 >> 3, mf = s8 & 7u;
     const float S = ef == 0u ? (float)mf * 0.001953125f : as_f32(((ef + 120u) << 23) | (mf << 20));
 
+    // r / S without a division.  S has at most 4 significant bits, so in the
+    // fp32 normal range r / S is never halfway between two floats and lies
+    // at least 2^-30 (relative) from every such halfway point: r * (1/S) in
+    // fp64, with 1/S known to within 2^-43, rounds to the same float.  1/S
+    // is taken low by 2^-51..2^-43 so that the product is always smaller in
+    // magnitude than r / S; then in the subnormal range, where only the sign
+    // reaches the code, a quotient of exactly half the smallest subnormal
+    // rounds to zero as round-to-nearest-even does.  (1/S: one Newton step
+    // in fp64 from the 1-ulp hardware reciprocal; the step's residual is
+    // exact and leaves the estimate low by its error squared.)
+    const double sd = S, y0 = __builtin_amdgcn_rcpf(S);
+    const double inv_s = __builtin_fma(y0, __builtin_fma(-sd, y0, 1.0), y0) * (1.0 - 0x1p-50);
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float q = __fdiv_rn(r[i], S);
+      float q = (float)((double)r[i] * inv_s);
       q = (q == q) ? q : 0.0f;           // NaN (only without sanitising) -> code 0
       q = fminf(fmaxf(q, -6.0f), 6.0f);  // saturate; leaves [-6, 6] unchanged
       y[i] = q + 0.0f;                   // -0.0 -> +0.0: sign only below zero
@@ -206,7 +227,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void nvfp4_rope_kernel(cons
     reinterpret_cast<uint32_t*>(values)[lane] = codes;
     if ((lane & 7) == 6) reinterpret_cast<uint32_t*>(scales)[lane >> 3] = sdw;
   }
-}
+};
 
 constexpr int kRowHalfMirror = 0x141;  // lane i reads lane 7-i of its half-row
 
@@ -217,20 +238,12 @@ __device__ __forceinline__ uint32_t bf16_rn(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void v4_rope_kernel(const RopeArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kTokensPerWave;
-  const float inv448 = (float)(1.0 / 448.0);
-
-  for (int p = 0; p < kTokensPerWave; ++p) {
-    const int64_t t = first + p;
-    if (t >= a.num_tokens) break;
-    float r[8];
-    int64_t page_off;
-    uint32_t in_page;
-    if (!rope_token(a, t, lane, r, page_off, in_page)) continue;
-
+// V4 record of one token.
+struct V4 {
+  static constexpr int kTpw = 2;
+  static __device__ __forceinline__ void finish(const RopeArgs& a, int lane, const float r[8],
+                                                int64_t page_off, uint32_t in_page) {
+    const float inv448 = (float)(1.0 / 448.0);
     // Group of 64 = lanes 8g..8g+7 (lanes 56..63, the RoPE dims, form their
     // own half-row and their scale is not used).
     float amax = max_abs8(r);
@@ -268,28 +281,96 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void v4_rope_kernel(const R
       *reinterpret_cast<u32x2*>(scales) =
           u32x2{s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24), s[4] | (s[5] << 8) | (s[6] << 16)};
   }
+};
+
+// One wave per token; TPW tokens per wave.  kCr1 (compress ratio 1: every
+// token with a valid slot is written): the wave's latent rows are loaded
+// before, and independent of, its slots and positions, which come in one
+// vector load each (lane p holds token p's; vector loads return in order, so
+// waiting for them leaves the rows in flight), and all cos/sin loads are
+// issued before any rotation.  Otherwise (a ratio that writes one token in
+// cr) a token's row is loaded only once its gate has passed.
+template <class F, int TPW, bool kCr1>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void rope_kernel(const RopeArgs a) {
+  static_assert(TPW >= 1 && TPW <= kWave && (TPW & (TPW - 1)) == 0, "lane p holds token p's slot");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * TPW;
+  if constexpr (kCr1) {
+    const int64_t last = a.num_tokens - 1;
+    u32x4 w[TPW];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const int64_t t = first + p;
+      w[p] = *reinterpret_cast<const u32x4*>(a.latent + (t < last ? t : last) * 512 + lane * 8);
+    }
+    const int64_t tl = first + (lane & (TPW - 1));
+    int64_t vs = a.slots[tl < last ? tl : last];
+    int64_t vp = a.positions[tl < last ? tl : last];
+    // keeps the row loads above the slot arithmetic and its wait
+    asm volatile("" : "+v"(vs), "+v"(vp) : : "memory");
+    int64_t slot[TPW];
+    bool ok[TPW];
+    float c[TPW][4], sn[TPW][4];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      slot[p] = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)vs >> 32), p) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)vs, p));
+      const int64_t pos =
+          (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)vp >> 32), p) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((uint32_t)vp, p));
+      ok[p] = first + p < a.num_tokens && slot[p] >= 0 && slot[p] < (int64_t)a.num_slots && pos >= 0 &&
+              pos < a.cos_rows;
+      load_cs(a, ok[p] ? pos : 0, lane, c[p], sn[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      if (!ok[p]) continue;
+      float r[8];
+      rotate_cs(a, w[p], c[p], sn[p], r);
+      int64_t page_off;
+      uint32_t in_page;
+      page_of(a, slot[p], page_off, in_page);
+      F::finish(a, lane, r, page_off, in_page);
+    }
+  } else {
+    for (int p = 0; p < TPW; ++p) {
+      const int64_t t = first + p;
+      if (t >= a.num_tokens) break;
+      float r[8];
+      int64_t page_off;
+      uint32_t in_page;
+      if (!rope_token(a, t, lane, r, page_off, in_page)) continue;
+      F::finish(a, lane, r, page_off, in_page);
+    }
+  }
 }
 
-hipError_t launch_rope(void (*kernel)(const RopeArgs), const RopeArgs& a, hipStream_t stream) {
-  constexpr int64_t kToksPerBlock = (int64_t)kWavesPerBlock * kTokensPerWave;
-  const int64_t blocks = (a.num_tokens + kToksPerBlock - 1) / kToksPerBlock;
+template <class F>
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
+  // Ratio 1 with a table: F::kTpw tokens per wave from 2^16 tokens up, else
+  // one (small batches are latency-bound: more, shorter waves finish sooner).
+  const bool cr1 = a.cr == 1 && a.cos_rows >= 1;
+  const int tpw = cr1 && a.num_tokens >= (int64_t(1) << 16) ? F::kTpw : 1;
+  const int64_t per_block = (int64_t)kWavesPerBlock * tpw;
+  const int64_t blocks = (a.num_tokens + per_block - 1) / per_block;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kWave * kWavesPerBlock), 0, stream, a);
+  const dim3 grid((unsigned)blocks), block(kWave * kWavesPerBlock);
+  if (!cr1)
+    hipLaunchKernelGGL((rope_kernel<F, 1, false>), grid, block, 0, stream, a);
+  else if (tpw > 1)
+    hipLaunchKernelGGL((rope_kernel<F, F::kTpw, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((rope_kernel<F, 1, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream) {
-  return launch_rope(mxfp8_rope_kernel, a, stream);
-}
+hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream) { return launch_rope<Mxfp8>(a, stream); }
 
-hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream) {
-  return launch_rope(nvfp4_rope_kernel, a, stream);
-}
+hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream) { return launch_rope<Nvfp4>(a, stream); }
 
-hipError_t launch_v4_rope(const RopeArgs& a, hipStream_t stream) {
-  return launch_rope(v4_rope_kernel, a, stream);
-}
+hipError_t launch_v4_rope(const RopeArgs& a, hipStream_t stream) { return launch_rope<V4>(a, stream); }
 
 }  // namespace mxs

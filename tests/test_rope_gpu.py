@@ -78,6 +78,39 @@ def test_rope_ratios_extremes(device, variant, cr):
 
 
 @pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
+def test_rope_ratio_one_many_tokens(device, variant):
+    """Compress ratio 1 at 70001 tokens, the size at which a wave takes
+    several tokens: a ragged last wave, negative and out-of-table positions,
+    pad and out-of-range slots, wide value ranges and specials.  Most slots
+    are pads (the oracle's cost is per written token); the first 4096
+    tokens are all valid, so whole waves of written tokens are covered."""
+    rng = np.random.default_rng(31)
+    n = 70001
+    x = rng.standard_normal((n, 512)) * np.exp2(rng.uniform(-130, 120, size=(n, 1)))
+    with np.errstate(over="ignore", under="ignore"):
+        xf = x.astype(np.float32)
+    latent = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    latent[(latent & 0x7F80) == 0x7F80] = 0x3F80
+    latent[::97, 5] = 0x7FC0
+    latent[::89, 470] = 0xFF80
+    latent[::83, 30:40] = 0x8000
+    table = workloads.rope_cos_sin_table(rows=5000)
+    positions = rng.integers(0, 5200, size=n).astype(np.int64)
+    positions[::101] = -1
+    positions[::103] = -(2**40)
+    block, nb = 64, 1100
+    slots = rng.permutation(nb * block)[:n].astype(np.int64)
+    pad = rng.random(n) < 0.85
+    pad[:4096] = False
+    slots[pad] = -1
+    slots[1::997] = nb * block + 3
+    slots[-1] = 0 if slots[-1] < 0 else slots[-1]
+    log(f"rope {variant} cr=1, {n} tokens, {int((slots >= 0).sum())} with a slot")
+    got, want = run_both(device, variant, latent, positions, table, slots, block, nb, 1)
+    assert (got == want).all(), first_mismatch(got, want)
+
+
+@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
 def test_rope_exponent_sweep(device, variant):
     """Every positive finite bf16 value as the only nonzero in its group or
     tile, positive and negative, through the real table."""
