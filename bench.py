@@ -212,10 +212,9 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
     del dq, slots
     # ring-state save: 262,144 fp32 [kv, score] rows (1024 wide) to scattered
     # slots of an 8192-block x 32-row ring
-    n_rows = 262_144
-    rows = torch.empty((n_rows, 1024), dtype=torch.float32, device="cuda").uniform_(-1, 1)
-    ring = torch.zeros((8192, 32, 1024), dtype=torch.float32, device="cuda")
-    ring_slots = torch.randperm(8192 * 32, device="cuda")[:n_rows].contiguous()
+    rows, ring_slots, ring_shape = workloads.ring_large_device()
+    n_rows = rows.shape[0]
+    ring = torch.zeros(ring_shape, dtype=torch.float32, device="cuda")
     _, ev = time_launches(lambda: ops.save_ring_rows(rows, ring_slots, ring), steps, warmup, torch)
     per = ev / steps
     out["save_ring_rows"] = {
@@ -301,12 +300,8 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
     del lat, pos, sl, kv
     # the same inserts at bandwidth scale: 1,048,576 tokens, compress ratio 1
     # (every token written), random positions and a permutation of the slots
-    n_big = 1 << 20
-    g = torch.Generator(device="cuda")
-    g.manual_seed(4)
-    lat = torch.empty((n_big, 512), dtype=torch.float32, device="cuda").normal_(generator=g).to(torch.bfloat16)
-    pos = torch.randint(0, cs.shape[0], (n_big,), generator=g, device="cuda")
-    sl = torch.randperm(n_big, generator=g, device="cuda")
+    lat, pos, cs, sl = workloads.rope_large_device()
+    n_big = lat.shape[0]
     for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
                             ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
                             ("v4_rope_store", ops.v4_rope_store, 584)):

@@ -229,6 +229,56 @@ def rope_case(seed: int = 4, tokens: int = 16384, compress_ratio: int = 4) -> Ro
     return RopeCase(latent, positions, rope_cos_sin_table(), slots, 64, tokens // 64, compress_ratio)
 
 
+
+ROPE_LARGE_TOKENS = 1 << 20
+
+
+def rope_large_device(tokens: int = ROPE_LARGE_TOKENS, seed: int = 4, device: str = "cuda"):
+    """The RoPE inserts at bandwidth scale: 1,048,576 tokens of N(0,1) bf16,
+    positions U[0, 65536) into the 65536-row table of rope_case, compress
+    ratio 1 (every token written), slots a random permutation of a
+    [tokens / 64, 64] cache.  Drawn on the device with torch's seeded
+    generator.  Returns (latent bf16 [T, 512], positions int64 [T], table
+    fp32 [65536, 64], slots int64 [T])."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    table = torch.from_numpy(rope_cos_sin_table()).to(device)
+    latent = torch.empty((tokens, LATENT), dtype=torch.float32, device=device).normal_(generator=g)
+    latent = latent.to(torch.bfloat16)
+    positions = torch.randint(0, table.shape[0], (tokens,), generator=g, device=device)
+    slots = torch.randperm(tokens, generator=g, device=device)
+    return latent, positions, table, slots
+
+
+RING_ROWS = 262_144
+
+
+def ring_large_device(rows: int = RING_ROWS, blocks: int = 8192, capacity: int = 32, width: int = 1024,
+                      seed: int = 5, device: str = "cuda"):
+    """The ring-state save at bandwidth scale: 262,144 fp32 rows of 1024
+    values U(-1, 1) to distinct random slots of an 8192 x 32-row ring.
+    Returns (rows fp32 [R, width], slots int64 [R], ring shape)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    src = torch.empty((rows, width), dtype=torch.float32, device=device).uniform_(-1.0, 1.0, generator=g)
+    slots = torch.randperm(blocks * capacity, generator=g, device=device)[:rows].contiguous()
+    return src, slots, (blocks, capacity, width)
+
+
+def random_cache_device(rows: int, seed: int = 6, device: str = "cuda"):
+    """A flat cache of `rows` 272-byte rows of uniformly random bytes (every
+    code and every scale byte, 0xFF included), drawn on the device: the
+    gather-dequant input at bandwidth scale.  Returns uint8 [rows * 272]."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(0, 256, (rows * ROW_BYTES,), generator=g, device=device, dtype=torch.uint8)
+
 # ------------------------------------------------------------------ attention (read side)
 
 @dataclass
