@@ -54,9 +54,11 @@ __device__ __forceinline__ void page_of(const RopeArgs& a, int64_t s, int64_t& p
 // not written.  On success r[0..7] hold the lane's rotated values.
 __device__ __forceinline__ bool rope_token(const RopeArgs& a, int64_t t, int lane,
                                            float r[8], int64_t& page_off, uint32_t& in_page) {
-  const int64_t s = a.slots[t];
+  int64_t s = a.slots[t];
+  int64_t pos = a.positions[t];
+  // both loads in flight before either is waited for (one round trip)
+  asm volatile("" : "+s"(s), "+s"(pos));
   if (s < 0 || s >= (int64_t)a.num_slots) return false;
-  const int64_t pos = a.positions[t];
   int64_t base;
   if ((uint64_t)pos < 0x7FFFFFFFull) {
     const uint32_t p32 = (uint32_t)pos, cr = (uint32_t)a.cr;
