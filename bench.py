@@ -270,8 +270,8 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
                             ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
                             ("v4_rope_store", ops.v4_rope_store, 584)):
         kv = torch.zeros((n_big // 64, 64, width), dtype=torch.uint8, device="cuda")
-        _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, 1), max(3, steps // 3), warmup, torch)
-        per = ev / max(3, steps // 3)
+        _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, 1), max(10, steps), warmup, torch)
+        per = ev / max(10, steps)
         nbytes = n_big * (1024 + 256 + 16 + width)
         out[name + "_large"] = {
             "workload": f"{n_big} tokens, CR 1 (all written), {width}-byte records, scattered slots",
