@@ -27,6 +27,11 @@ def test_graph_replays_match_eager(device):
     r_lat = bf16_dev(rc.latent, device)
     r_pos, r_cs, r_slots = i64_dev(rc.positions, device), torch.from_numpy(rc.cos_sin).to(device), i64_dev(rc.slots, device)
     r_kv = torch.empty((16, 64, 528), dtype=torch.uint8, device=device)
+    # compress ratio 1 at 70,000 tokens: the path where a wave takes several tokens
+    r1_lat = torch.empty((70_000, 512), dtype=torch.bfloat16, device=device)
+    r1_pos = torch.randint(0, r_cs.shape[0], (70_000,), device=device)
+    r1_slots = torch.randperm(1094 * 64, device=device)[:70_000].contiguous()
+    r1_kv = torch.empty((1094, 64, 288), dtype=torch.uint8, device=device)
     # a decode step's read side over the cache the scatter store just wrote:
     # one pass and the split-key form (its workspace allocated up front)
     a_q = torch.empty((8, 32, 512), dtype=torch.bfloat16, device=device)
@@ -41,6 +46,7 @@ def test_graph_replays_match_eager(device):
         ops.mxfp4_store(p_src, p_slots, p_cache, 1, 1 << 16, 1 << 16)
         ops.mxfp4_gather_dequant(p_cache, 1, 1 << 16, 1 << 16, 512, p_slots, dq_out)
         ops.mxfp8_rope_store(r_lat, r_pos, r_cs, r_kv, r_slots, rc.compress_ratio)
+        ops.nvfp4_rope_store(r1_lat, r1_pos, r_cs, r1_kv, r1_slots, 1)
         ops.sparse_mla_attention(a_q, p_cache, a_idx, 0.04, out=a_out, splits=4, workspace=a_ws)
         ops.sparse_mla_attention(a_q, p_cache, a_idx, 0.04, out=a_out1, splits=1)
 
@@ -53,6 +59,8 @@ def test_graph_replays_match_eager(device):
         p_cache.fill_(0xA5)
         dq_out.fill_(0)
         r_kv.fill_(0xA5)
+        r1_lat.normal_(generator=gen)
+        r1_kv.fill_(0xA5)
         a_q.normal_(generator=gen)
         a_out.fill_(0)
         a_out1.fill_(0)
@@ -75,12 +83,13 @@ def test_graph_replays_match_eager(device):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [g_cache.clone(), p_cache.clone(), dq_out.clone(), r_kv.clone(), a_out.clone(), a_out1.clone()]
+        got = [g_cache.clone(), p_cache.clone(), dq_out.clone(), r_kv.clone(), r1_kv.clone(), a_out.clone(),
+               a_out1.clone()]
         reset(100 + rep)
         work()  # eager
         torch.cuda.synchronize()
-        want = [g_cache, p_cache, dq_out, r_kv, a_out, a_out1]
-        names = ("slot-order store", "scatter store", "dequant", "mxfp8 insert", "attention split",
-                 "attention one pass")
+        want = [g_cache, p_cache, dq_out, r_kv, r1_kv, a_out, a_out1]
+        names = ("slot-order store", "scatter store", "dequant", "mxfp8 insert", "nvfp4 insert, ratio 1",
+                 "attention split", "attention one pass")
         for name, a, b in zip(names, got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rep, name)
