@@ -35,6 +35,27 @@ def _need_cuda(*tensors: torch.Tensor) -> None:
             raise ValueError("libmxstore works on device tensors only")
 
 
+def _extent_bytes(t: torch.Tensor) -> int:
+    """Bytes from t's data pointer to the end of its last element (what a
+    kernel given only the pointer may touch without leaving the tensor)."""
+    if t.numel() == 0:
+        return 0
+    return (1 + sum((n - 1) * st for n, st in zip(t.shape, t.stride()))) * t.element_size()
+
+
+def _need_cache_extent(cache: torch.Tensor, num_blocks: int, block_size: int, block_stride_rows: int,
+                       latent: int, group: int) -> None:
+    """The C ABI receives only the cache pointer: check here that the paged
+    geometry stays inside the tensor (other argument errors are the ABI's)."""
+    if num_blocks < 1 or block_size < 1 or block_stride_rows < block_size or latent < group \
+            or group < 1 or latent % group:
+        return
+    need = ((num_blocks - 1) * block_stride_rows + block_size) * (latent // 2 + latent // group)
+    if _extent_bytes(cache) < need:
+        raise ValueError(f"cache holds {_extent_bytes(cache)} bytes from its data pointer; "
+                         f"{num_blocks} blocks of {block_size} rows at stride {block_stride_rows} need {need}")
+
+
 def row_bytes(latent: int, group: int = GROUP_SIZE) -> int:
     """Bytes of one packed MXFP4 row: latent/2 + latent/group."""
     n = int(_abi.lib().mx_row_bytes(latent, group))
@@ -61,6 +82,7 @@ def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tens
     num_tokens = slot_mapping.numel()
     if num_tokens > src.shape[0]:
         raise ValueError("slot_mapping has more entries than src has rows")
+    _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
     _abi.check(_abi.lib().mxfp4_store(
         src.data_ptr(), num_tokens, src.shape[1], src.stride(0), slot_mapping.data_ptr(),
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
@@ -109,6 +131,7 @@ def mxfp4_store_by_slot(src: torch.Tensor, num_tokens: int, inverse: torch.Tenso
         raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
     if num_tokens > src.shape[0]:
         raise ValueError("num_tokens exceeds the rows of src")
+    _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
     _abi.check(_abi.lib().mxfp4_store_by_slot(
         src.data_ptr(), num_tokens, src.shape[1], src.stride(0), inverse.data_ptr(),
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
@@ -125,6 +148,7 @@ def mxfp4_gather_dequant(cache: torch.Tensor, num_blocks: int, block_size: int,
         raise ValueError("out must be a bf16 [n, latent] tensor with unit inner stride")
     if out.shape[0] < slots.numel() or out.shape[1] != latent:
         raise ValueError("out must have at least len(slots) rows of `latent` values")
+    _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, latent, group)
     _abi.check(_abi.lib().mxfp4_gather_dequant(
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, latent, group,
         slots.data_ptr(), slots.numel(), out.data_ptr(), out.stride(0), _stream(stream)))

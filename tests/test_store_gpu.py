@@ -324,6 +324,32 @@ def test_inverse_map_contents(device):
     assert (got[nb * bs:] == 12345).all()  # nothing past the map
 
 
+def test_cache_extent_checked(device):
+    """The C ABI gets only the cache pointer, so the binding refuses a paged
+    geometry that reaches past the tensor (nothing is launched)."""
+    nb, bs, stride = 4, 16, 24
+    need = ((nb - 1) * stride + bs) * 272
+    src = torch.zeros((8, 512), dtype=torch.bfloat16, device=device)
+    slots = torch.arange(8, dtype=torch.int64, device=device)
+    inv = torch.full((nb * bs,), -1, dtype=torch.int32, device=device)
+    out = torch.empty((8, 512), dtype=torch.bfloat16, device=device)
+    short = torch.full((need - 1,), 0xA5, dtype=torch.uint8, device=device)
+    with pytest.raises(ValueError, match="cache holds"):
+        ops.mxfp4_store(src, slots, short, nb, bs, stride)
+    with pytest.raises(ValueError, match="cache holds"):
+        ops.mxfp4_store_by_slot(src, 8, inv, short, nb, bs, stride)
+    with pytest.raises(ValueError, match="cache holds"):
+        ops.mxfp4_gather_dequant(short, nb, bs, stride, 512, slots, out)
+    torch.cuda.synchronize()
+    assert (short.cpu().numpy() == 0xA5).all()
+    # exactly enough, also as the strided paged view of interleaved layers
+    backing = torch.full((nb * stride * 272,), 0xA5, dtype=torch.uint8, device=device)
+    view = backing.view(nb, stride, 272)[:, :bs, :]
+    ops.mxfp4_store(src, slots, backing[:need], nb, bs, stride)
+    ops.mxfp4_store(src, slots, view, nb, bs, stride)
+    torch.cuda.synchronize()
+
+
 def test_large_batch_ragged_generic_paging(device):
     """A batch past the 2^18-token switch (4 tokens per wave) with a ragged
     tail, a non-power-of-two block, interleaved blocks and scattered slots."""
