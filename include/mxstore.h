@@ -339,7 +339,7 @@ int sparse_mla_attention_split(const uint16_t* q_bf16, int64_t num_tokens, int64
 int64_t sparse_mla_attention_workspace_bytes(int64_t num_tokens, int64_t num_heads,
                                              int64_t splits);
 
-/* Split count expected to be fastest on MI355X: enough workgroups for two per
+/* Split count expected to be fastest on MI355X: enough workgroups for one per
  * CU on 256 CUs, at least two 64-key tiles per split, at most 64; 1 when
  * the batch already fills the GPU.  Host-only heuristic, no device work. */
 int32_t sparse_mla_attention_splits_advised(int64_t num_tokens, int64_t num_heads, int64_t topk);

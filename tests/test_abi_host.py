@@ -309,11 +309,13 @@ def test_attention_split_workspace_and_advice(mxlib):
     assert wsb(-1, 16, 2) == _abi.MX_E_RANGE and wsb(3, 0, 2) == _abi.MX_E_RANGE
     adv = mxlib.sparse_mla_attention_splits_advised
     assert adv(4096, 32, 2048) == 1          # 4096 workgroups already fill the GPU
-    assert adv(64, 32, 2048) == 8            # 64 workgroups -> 512
+    assert adv(64, 32, 2048) == 4            # 64 workgroups -> 256
+    assert adv(256, 32, 2048) == 1           # 256 workgroups: one per CU already
+    assert adv(128, 32, 2048) == 2
     assert adv(1, 32, 2048) == 16            # capped at two tiles per range (32 tiles)
     assert adv(1, 128, 65536) == 64          # capped at 64 ranges
     assert adv(8, 32, 64) == 1               # one tile: nothing to split
-    assert adv(8, 48, 2048) == 16            # 16-head blocks: 8 * 3 workgroups
+    assert adv(8, 48, 2048) == 11            # 16-head blocks: 8 * 3 workgroups -> 264
     assert adv(0, 32, 2048) == 1 and adv(8, 24, 2048) == 1 and adv(8, 32, 0) == 1
 
 
