@@ -108,6 +108,39 @@ def time_launches(fn, steps: int, warmup: int, torch):
     return wall, ev0.elapsed_time(ev1) / 1000.0
 
 
+def time_graph(fn, per_graph: int, replays: int, torch) -> float:
+    """Seconds per launch of `fn` captured `per_graph` times into one HIP
+    graph and replayed `replays` times (HIP events around the replays): the
+    device's back-to-back rate without the host's per-call submission cost,
+    which bounds eager launches of latency-bound kernels."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return ev0.elapsed_time(ev1) / 1000.0 / (replays * per_graph)
+
+
+GRAPH_LAUNCHES = 50  # launches per captured graph for the latency-bound companions
+GRAPH_REPLAYS = 10
+
+
 def cpu_threads() -> tuple[int, int]:
     """(threads for the all-cores leg, logical CPUs the OS reports).  The
     all-cores leg uses the CPUs this process may run on, at most 16 (one
@@ -165,8 +198,9 @@ def small_stores(torch, ops, workloads, steps, warmup):
     """The store on the decode-shaped batch (256 tokens into a paged cache
     with other layers' rows interleaved) and on the prefill chunk (16,384
     tokens in 32 request runs, then gather-dequant of the stored slots):
-    both are latency-bound, so they are reported in microseconds per launch
-    (HIP events over back-to-back launches, launch overhead included)."""
+    both are latency-bound, so they are reported in microseconds per launch:
+    HIP events over back-to-back eager launches (the host's per-call cost
+    included) and over replays of a HIP graph of the same launches."""
     out = {}
     reps = max(20, steps)
     for name, case in (("mxfp4_store_decode", workloads.decode_case()),
@@ -175,21 +209,27 @@ def small_stores(torch, ops, workloads, steps, warmup):
         slots = torch.from_numpy(case.slots).cuda()
         cache = torch.from_numpy(case.fresh_cache()).cuda()
         nb, bs, bsr = case.num_blocks, case.block_size, case.block_stride_rows
-        _, ev = time_launches(lambda: ops.mxfp4_store(src, slots, cache, nb, bs, bsr), reps, warmup, torch)
+        store = lambda: ops.mxfp4_store(src, slots, cache, nb, bs, bsr)  # noqa: E731
+        _, ev = time_launches(store, reps, warmup, torch)
         per = ev / reps
+        per_graph = time_graph(store, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
         valid = int((case.slots >= 0).sum())
         entry = {
             "workload": f"{case.src.shape[0]} tokens ({valid} valid) into {nb} blocks x {bs} slots, "
                         f"block stride {bsr} rows",
             "us_per_launch": round(per * 1e6, 2),
             "tokens_per_s": round(valid / per, 1),
+            "graph_us_per_launch": round(per_graph * 1e6, 2),
+            "graph_tokens_per_s": round(valid / per_graph, 1),
         }
         if case.gather_slots is not None:
             gs = torch.from_numpy(case.gather_slots).cuda()
             dq = torch.empty((gs.numel(), 512), dtype=torch.bfloat16, device="cuda")
-            _, ev = time_launches(lambda: ops.mxfp4_gather_dequant(cache, nb, bs, bsr, 512, gs, dq), reps,
-                                  warmup, torch)
+            gather = lambda: ops.mxfp4_gather_dequant(cache, nb, bs, bsr, 512, gs, dq)  # noqa: E731
+            _, ev = time_launches(gather, reps, warmup, torch)
             entry["gather_dequant_us_per_launch"] = round(ev / reps * 1e6, 2)
+            entry["gather_dequant_graph_us_per_launch"] = round(
+                time_graph(gather, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch) * 1e6, 2)
         out[name] = entry
     return out
 
@@ -252,14 +292,17 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
                             ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
                             ("v4_rope_store", ops.v4_rope_store, 584)):
         kv = torch.zeros((case.num_blocks, case.block, width), dtype=torch.uint8, device="cuda")
-        _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, case.compress_ratio), steps, warmup, torch)
+        insert = lambda: fn(lat, pos, cs, kv, sl, case.compress_ratio)  # noqa: E731
+        _, ev = time_launches(insert, steps, warmup, torch)
         per = ev / steps
+        per_graph = time_graph(insert, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
         nbytes = written * (1024 + 256 + 16 + width) + (case.latent.shape[0] - written) * 16
         out[name] = {
             "workload": f"{case.latent.shape[0]} tokens, CR {case.compress_ratio} ({written} written), "
                         f"{width}-byte records",
             "us_per_launch": round(per * 1e6, 2),
             "GBps": round(nbytes / per / 1e9, 1),
+            "graph_us_per_launch": round(per_graph * 1e6, 2),
         }
     del lat, pos, sl, kv
     # the same inserts at bandwidth scale: 1,048,576 tokens, compress ratio 1
@@ -305,10 +348,11 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
     splits = ops.sparse_mla_attention_splits_advised(64, q.shape[1], aidx.shape[1])
     ws = torch.empty(max(256, ops.sparse_mla_attention_workspace_bytes(64, q.shape[1], splits)),
                      dtype=torch.uint8, device="cuda")
-    _, ev = time_launches(lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout, splits=splits,
-                                                           workspace=ws),
-                          max(10, steps), warmup, torch)
+    decode = lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout,  # noqa: E731
+                                              splits=splits, workspace=ws)
+    _, ev = time_launches(decode, max(10, steps), warmup, torch)
     per = ev / max(10, steps)
+    per_graph = time_graph(decode, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
     valid = int((aidx >= 0).sum())
     flops = 4.0 * q.shape[1] * 512 * valid
     out["sparse_mla_attention_decode"] = {
@@ -316,6 +360,7 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
                     f"{acache.shape[0]}-token MXFP4 cache, {splits} key ranges + merge",
         "us_per_call": round(per * 1e6, 2),
         "TFLOPs": round(flops / per / 1e12, 1),
+        "graph_us_per_call": round(per_graph * 1e6, 2),
     }
     del q, acache, aidx, aout, ws
     return out
