@@ -181,8 +181,19 @@ struct Mxfp8 {
 // NVFP4 record of one token.
 struct Nvfp4 {
   static constexpr int kTpw = 4;
+  // With sanitising on, r holds no NaN, and neither can the quotient (S is
+  // finite and positive), so its NaN check is left out of that branch.
   static __device__ __forceinline__ void finish(const RopeArgs& a, int lane, const float r[8],
                                                 int64_t page_off, uint32_t in_page) {
+    if (a.sanitize)
+      finish_impl<false>(a, lane, r, page_off, in_page);
+    else
+      finish_impl<true>(a, lane, r, page_off, in_page);
+  }
+
+  template <bool kNaN>
+  static __device__ __forceinline__ void finish_impl(const RopeArgs& a, int lane, const float r[8],
+                                                     int64_t page_off, uint32_t in_page) {
     const float inv6 = (float)(1.0 / 6.0);
     float amax = max_abs8(r);
     amax = fmaxf(amax, as_f32(dpp<kQuadSwap1>(as_u32(amax))));  // tile = lane pair
@@ -209,10 +220,11 @@ struct Nvfp4 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float q = (float)((double)r[i] * inv_s);
-      q = (q == q) ? q : 0.0f;           // NaN (only without sanitising) -> code 0
-      q = fminf(fmaxf(q, -6.0f), 6.0f);  // saturate; leaves [-6, 6] unchanged
-      y[i] = q + 0.0f;                   // -0.0 -> +0.0: sign only below zero
+      if (kNaN) q = (q == q) ? q : 0.0f;  // NaN -> code 0 (the converter gives 7)
+      y[i] = q + 0.0f;                    // -0.0 -> +0.0: sign only below zero
     }
+    // The converter saturates: magnitudes above 6, up to +-Inf, give code 7
+    // with the sign (checked on the device), as the E2M1 rule asks.
     uint32_t codes = 0;
     codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[0], y[1], 1.0f, 0);
     codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);

@@ -77,8 +77,9 @@ def test_rope_ratios_extremes(device, variant, cr):
     assert (got == want).all(), first_mismatch(got, want)
 
 
+@pytest.mark.parametrize("sanitize", [True, False])
 @pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
-def test_rope_ratio_one_many_tokens(device, variant):
+def test_rope_ratio_one_many_tokens(device, variant, sanitize):
     """Compress ratio 1 at 70001 tokens, the size at which a wave takes
     several tokens: a ragged last wave, negative and out-of-table positions,
     pad and out-of-range slots, wide value ranges and specials.  Most slots
@@ -105,8 +106,8 @@ def test_rope_ratio_one_many_tokens(device, variant):
     slots[pad] = -1
     slots[1::997] = nb * block + 3
     slots[-1] = 0 if slots[-1] < 0 else slots[-1]
-    log(f"rope {variant} cr=1, {n} tokens, {int((slots >= 0).sum())} with a slot")
-    got, want = run_both(device, variant, latent, positions, table, slots, block, nb, 1)
+    log(f"rope {variant} cr=1, {n} tokens, {int((slots >= 0).sum())} with a slot, sanitize={sanitize}")
+    got, want = run_both(device, variant, latent, positions, table, slots, block, nb, 1, sanitize=sanitize)
     assert (got == want).all(), first_mismatch(got, want)
 
 
