@@ -142,6 +142,15 @@ __device__ __forceinline__ uint32_t e4m3x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p) & 0xFFFFu;
 }
 
+// Four fp32 -> four E4M3 bytes in one dword, a first: the second convert
+// writes the upper half-word of the first one's result.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  i16x2 p = {0, 0};
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, a, b, 1.0f, false);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, c, d, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 // MXFP8 record of one token (r: the lane's rotated values).
 struct Mxfp8 {
   static constexpr int kTpw = 2;  // tokens per wave at ratio 1 (measured)
@@ -160,8 +169,8 @@ struct Mxfp8 {
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(r[i] * mul, -448.0f), 448.0f);
-    const uint32_t lo = e4m3x2(y[0], y[1]) | (e4m3x2(y[2], y[3]) << 16);
-    const uint32_t hi = e4m3x2(y[4], y[5]) | (e4m3x2(y[6], y[7]) << 16);
+    const uint32_t lo = e4m3x4(y[0], y[1], y[2], y[3]);
+    const uint32_t hi = e4m3x4(y[4], y[5], y[6], y[7]);
 
     int enc = E + 127;
     enc = max(enc, 0);
@@ -245,6 +254,15 @@ struct Nvfp4 {
 
 constexpr int kRowHalfMirror = 0x141;  // lane i reads lane 7-i of its half-row
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> a bf16 pair (lo in the low half), nearest-even, by the
+// hardware converter; not for NaN (whose payload it may keep).
+__device__ __forceinline__ uint32_t bf16x2_hw(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // fp32 -> bf16, nearest-even; NaN -> 0x7FC0.
 __device__ __forceinline__ uint32_t bf16_rn(float f) {
   const uint32_t u = as_u32(f);
@@ -255,8 +273,21 @@ __device__ __forceinline__ uint32_t bf16_rn(float f) {
 // V4 record of one token.
 struct V4 {
   static constexpr int kTpw = 2;
+  // With sanitising on, r holds no NaN and the RoPE values take gfx950's
+  // bf16 pack (v_cvt_pk_bf16_f32), which rounds every non-NaN fp32 exactly
+  // as bf16_rn does (checked on the device over all 2^32 bit patterns);
+  // otherwise bf16_rn keeps NaN at 0x7FC0.
   static __device__ __forceinline__ void finish(const RopeArgs& a, int lane, const float r[8],
                                                 int64_t page_off, uint32_t in_page) {
+    if (a.sanitize)
+      finish_impl<true>(a, lane, r, page_off, in_page);
+    else
+      finish_impl<false>(a, lane, r, page_off, in_page);
+  }
+
+  template <bool kNoNaN>
+  static __device__ __forceinline__ void finish_impl(const RopeArgs& a, int lane, const float r[8],
+                                                     int64_t page_off, uint32_t in_page) {
     const float inv448 = (float)(1.0 / 448.0);
     // Group of 64 = lanes 8g..8g+7 (lanes 56..63, the RoPE dims, form their
     // own half-row and their scale is not used).
@@ -280,12 +311,17 @@ struct V4 {
       float y[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(r[i] * mul, -448.0f), 448.0f);
-      const uint32_t lo = e4m3x2(y[0], y[1]) | (e4m3x2(y[2], y[3]) << 16);
-      const uint32_t hi = e4m3x2(y[4], y[5]) | (e4m3x2(y[6], y[7]) << 16);
+      const uint32_t lo = e4m3x4(y[0], y[1], y[2], y[3]);
+      const uint32_t hi = e4m3x4(y[4], y[5], y[6], y[7]);
       *reinterpret_cast<u32x2*>(values + lane * 8) = u32x2{lo, hi};
     } else {
-      const u32x4 h = {bf16_rn(r[0]) | (bf16_rn(r[1]) << 16), bf16_rn(r[2]) | (bf16_rn(r[3]) << 16),
-                       bf16_rn(r[4]) | (bf16_rn(r[5]) << 16), bf16_rn(r[6]) | (bf16_rn(r[7]) << 16)};
+      u32x4 h;
+      if (kNoNaN) {
+        h = u32x4{bf16x2_hw(r[0], r[1]), bf16x2_hw(r[2], r[3]), bf16x2_hw(r[4], r[5]), bf16x2_hw(r[6], r[7])};
+      } else {
+        h = u32x4{bf16_rn(r[0]) | (bf16_rn(r[1]) << 16), bf16_rn(r[2]) | (bf16_rn(r[3]) << 16),
+                  bf16_rn(r[4]) | (bf16_rn(r[5]) << 16), bf16_rn(r[6]) | (bf16_rn(r[7]) << 16)};
+      }
       *reinterpret_cast<u32x4*>(values + 448 + (lane - 56) * 16) = h;
     }
     uint32_t s[7];
