@@ -109,8 +109,14 @@ __device__ __forceinline__ void rotate_cs(const RopeArgs& a, const u32x4 w, cons
     r[2 * i + 1] = oc + es;
   }
   if (a.sanitize) {
+    // A NaN among the lane's values makes their sum NaN (so can Inf - Inf,
+    // which only costs the replacement pass); waves with no such lane skip
+    // the per-value replacement.
+    const float sum = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+    if (__builtin_amdgcn_ballot_w64(sum != sum)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (r[i] == r[i]) ? r[i] : 0.0f;
+      for (int i = 0; i < 8; ++i) r[i] = (r[i] == r[i]) ? r[i] : 0.0f;
+    }
   }
 }
 
