@@ -469,9 +469,12 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           const float mf = fmaxf(m_pv[ht][r], s2);
           sc = m_pv[ht][r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_pv[ht][r] - mf);
         }
+        // One division per row, then products (within an fp32 ulp of
+        // dividing each value; the bf16 rounding that follows dominates).
+        const float inv = lt > 0.0f ? sc / lt : 0.0f;
         float v[8];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) v[n] = lt > 0.0f ? (o[ht][n][r] * sc) / lt : 0.0f;
+        for (int n = 0; n < 8; ++n) v[n] = lt > 0.0f ? o[ht][n][r] * inv : 0.0f;
         const u32x4 b = {bf16x2_rn(v[0], v[1]), bf16x2_rn(v[2], v[3]), bf16x2_rn(v[4], v[5]), bf16x2_rn(v[6], v[7])};
         uint16_t* orow = a.out + t * a.out_token_stride + (int64_t)(h0 + h) * a.out_head_stride + 128 * dg + 8 * li;
         if (a.out_aligned) {
