@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw)
 // LATENT: values per token (power of two, 128..2048).  A token occupies
 // min(LATENT/8, 64) lanes per pass; LATENT > 512 takes LATENT/512 passes.
 // kPow2: slot -> row by shift/mask (else a 32-bit division).
-// kTokensPerWave: passes per wave (2 for small batches, 4 for large: measured).
+// kTokensPerWave: passes per wave (1, 2 or 4 by batch size: measured).
 template <int LATENT, bool kPow2, int kTokensPerWave>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(const StoreArgs a) {
   constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
@@ -409,8 +409,13 @@ template <int LATENT>
 hipError_t launch_latent(const StoreArgs& args, hipStream_t stream) {
   StoreArgs a = args;
   a.plain_stores = a.num_tokens <= kPlainStoreBytes / (LATENT / 2 + LATENT / 32);
-  // Small batches are latency-bound: more, shorter waves finish sooner.
-  if (a.num_tokens < (int64_t(1) << 18)) return launch_tpw<LATENT, 2>(a, stream);
+  // Passes per wave by batch size, from HIP-graph timings of back-to-back
+  // launches (random slots, latent 512): one up to 8,192 tokens (shorter
+  // waves finish sooner: 256 tokens 1.97 vs 2.22 us with two), two up to
+  // 16,384 (4.9 vs 5.3 us), four above (32,768 tokens 8.3 vs 8.8 us,
+  // 262,143 tokens 59 vs 65 us).
+  if (a.num_tokens <= 8192) return launch_tpw<LATENT, 1>(a, stream);
+  if (a.num_tokens <= 16384) return launch_tpw<LATENT, 2>(a, stream);
   return launch_tpw<LATENT, 4>(a, stream);
 }
 
