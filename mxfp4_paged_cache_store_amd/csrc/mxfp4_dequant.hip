@@ -22,7 +22,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kSlotsPerWave = 8;
 constexpr int kWavesPerBlock = 4;
 
 __device__ __forceinline__ u32x4 dequant8(uint32_t codes, uint32_t scale_byte) {
@@ -36,7 +35,9 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t codes, uint32_t scale_byte) {
   return r;
 }
 
-template <int LATENT, bool kPow2>
+// kSlotsPerWave: passes per wave, 1 for small lists and 2 otherwise (chosen
+// at launch from measurements).
+template <int LATENT, bool kPow2, int kSlotsPerWave>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_dequant_kernel(const DequantArgs a) {
   constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
   constexpr int kToksPerPass = kWave / kLanesPerTok;
@@ -109,20 +110,29 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_dequant_kernel(c
   }
 }
 
-template <int LATENT>
-hipError_t launch_latent(const DequantArgs& a, hipStream_t stream) {
+template <int LATENT, int SPW>
+hipError_t launch_spw(const DequantArgs& a, hipStream_t stream) {
   constexpr int kLanesPerTok = LATENT >= 512 ? 64 : LATENT / 8;
-  constexpr int64_t kToksPerBlock =
-      (int64_t)kWavesPerBlock * kSlotsPerWave * (kWave / kLanesPerTok);
+  constexpr int64_t kToksPerBlock = (int64_t)kWavesPerBlock * SPW * (kWave / kLanesPerTok);
   const int64_t blocks = (a.n + kToksPerBlock - 1) / kToksPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (a.map.pow2)
-    hipLaunchKernelGGL((mxfp4_dequant_kernel<LATENT, true>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((mxfp4_dequant_kernel<LATENT, true, SPW>), dim3((unsigned)blocks),
                        dim3(kWave * kWavesPerBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((mxfp4_dequant_kernel<LATENT, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((mxfp4_dequant_kernel<LATENT, false, SPW>), dim3((unsigned)blocks),
                        dim3(kWave * kWavesPerBlock), 0, stream, a);
   return hipGetLastError();
+}
+
+// Slots per wave (latent 512, random slots; HIP-graph replays and single
+// launches after a cache flush): 1 up to 4,096 slots (256 slots 1.92 vs 2.79
+// us with 8), 2 above (16,384 slots 4.1 vs 5.1 us, 4.5M slots 1074 vs
+// 1139 us); 1 is slower from 65,536 slots on when the rows come from HBM.
+template <int LATENT>
+hipError_t launch_latent(const DequantArgs& a, hipStream_t stream) {
+  if (a.n <= 4096) return launch_spw<LATENT, 1>(a, stream);
+  return launch_spw<LATENT, 2>(a, stream);
 }
 
 }  // namespace
