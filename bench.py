@@ -160,7 +160,7 @@ def cpu_baseline(sample: int):
     import numpy as np
 
     import oracle
-    from mxfp4_paged_cache_store_amd import workloads
+    import workloads
 
     threads, nproc = cpu_threads()
     src, slots = workloads.large_sample_host(sample)
@@ -432,7 +432,8 @@ def main():
 
     import torch
 
-    from mxfp4_paged_cache_store_amd import build, ops, workloads
+    import workloads
+    from mxfp4_paged_cache_store_amd import build, ops
 
     if not os.path.exists(build.LIB_PATH):
         build.build()

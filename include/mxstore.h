@@ -24,8 +24,8 @@
  *     past the last slot is skipped.
  *   - num_tokens == 0 (or an empty slot list) launches nothing and returns
  *     MX_OK [P1 `store_mxfp4_mla`; P2 `rope_quant_insert`].
- *   - Two tokens mapping to the same slot race (which one lands is
- *     unspecified).
+ *   - Two tokens mapping to the same slot race: the row's contents are then
+ *     unspecified and may mix bytes of both tokens.
  */
 #ifndef MXSTORE_H
 #define MXSTORE_H
@@ -93,8 +93,11 @@ int mxfp4_store(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
  * inverse[s] = token of slot s (or -1) is built once per slot mapping -- it
  * serves every layer that stores with that mapping in the step -- and the
  * store then walks the slots in order, gathers each slot's latent row and
- * writes the rows sequentially.  It writes exactly the bytes mxfp4_store
- * writes (for a slot used by several tokens, one of them lands in both).
+ * writes the rows sequentially.  For distinct slots it writes exactly the
+ * bytes mxfp4_store writes.  A slot named by several tokens is a race in
+ * both forms: the slot-order form writes the whole row of the token whose
+ * inverse entry won, while the scatter form may leave a row that mixes one
+ * token's code bytes with another's scale bytes.
  */
 
 /* Bytes of the inverse map: one int32 per slot (num_blocks * block_size),
@@ -126,12 +129,17 @@ int mxfp4_build_inverse(const int64_t* slot_mapping, int64_t num_tokens,
  * MXFP4 store in slot order: same arguments and result as mxfp4_store, with
  * the slot mapping replaced by its inverse map (built by mxfp4_build_inverse
  * for the same num_blocks and block_size; entries outside [0, num_tokens) are
- * skipped).  latent must be 512, 1024 or 2048; inverse 16-byte aligned.  One
- * launch over all num_blocks * block_size slots, so it is meant for batches
- * that cover a large share of them (mxfp4_slot_order_advised).
+ * skipped).  latent must be 512, 1024 or 2048; inverse 16-byte aligned and
+ * inverse_bytes (its size) at least mxfp4_inverse_bytes(num_blocks,
+ * block_size), else MX_E_RANGE.  The library cannot tell whether the inverse
+ * belongs to the slot mapping of this batch: a map built from another
+ * mapping writes the rows its own entries name, and the call still returns
+ * MX_OK.  Rebuild it whenever the mapping changes.  One launch over all
+ * num_blocks * block_size slots, so it is meant for batches that cover a
+ * large share of them (mxfp4_slot_order_advised).
  */
 int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
-                        int64_t src_row_stride, const int32_t* inverse,
+                        int64_t src_row_stride, const int32_t* inverse, int64_t inverse_bytes,
                         uint8_t* cache, int64_t num_blocks, int64_t block_size,
                         int64_t block_stride_rows, int32_t group, void* stream);
 

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_build_inverse.restype = ctypes.c_int
         L.mxfp4_build_inverse.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
         L.mxfp4_store_by_slot.restype = ctypes.c_int
-        L.mxfp4_store_by_slot.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
+        L.mxfp4_store_by_slot.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp]
         L.mxfp4_gather_dequant.restype = ctypes.c_int
         L.mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp]
         for name in ("mxfp8_rope_store", "nvfp4_rope_store", "v4_rope_store"):

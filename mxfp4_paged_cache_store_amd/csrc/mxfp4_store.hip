@@ -249,9 +249,11 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
 // random sub-line writes at well under half.  So the scatter is inverted:
 // inv[s] = t is built once per slot mapping (it serves every layer that
 // stores with that mapping), then waves walk slots in order, gather the token
-// row inv[s] (or nothing) and write rows sequentially.  The bytes written are
-// identical to the scatter form (for duplicate slots either form keeps one of
-// the tokens).
+// row inv[s] (or nothing) and write rows sequentially.  For distinct slots the
+// bytes written are identical to the scatter form's.  A slot named by several
+// tokens races in both: here the whole row of the token whose inverse entry
+// won lands, while the scatter form may mix one token's code dwords with
+// another's scale dwords.
 
 constexpr int kSlotsPerWave = 4;
 
@@ -331,7 +333,12 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_ke
         if ((lane & 15) == 12) st[(p * (int)kPitch + LATENT / 2 + sub * 16) / 4 + (lane >> 4)] = sdw;
       }
     }
+    // Each lane reads back chunks written by other lanes of the wave: the
+    // fences order the LDS writes before the barrier and the reads after it
+    // for the compiler (the hardware keeps one wave's LDS accesses in order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // Rows go out in slot order, so plain stores let L2 merge neighbours.
     const __amdgpu_buffer_rsrc_t rs =
         buffer_at(a.cache + a.map.row<kPow2>((uint32_t)s0) * kPitch, (uint32_t)kSpan);

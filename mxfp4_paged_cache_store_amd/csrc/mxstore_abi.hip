@@ -196,9 +196,9 @@ int mxfp4_build_inverse(const int64_t* slot_mapping, int64_t num_tokens, int64_t
 }
 
 int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
-                        int64_t src_row_stride, const int32_t* inverse, uint8_t* cache,
-                        int64_t num_blocks, int64_t block_size, int64_t block_stride_rows,
-                        int32_t group, void* stream) {
+                        int64_t src_row_stride, const int32_t* inverse, int64_t inverse_bytes,
+                        uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                        int64_t block_stride_rows, int32_t group, void* stream) {
   mxs::StoreArgs a{};
   bool empty = false;
   int rc = check_store(src_bf16, num_tokens, latent, src_row_stride, inverse, cache, num_blocks,
@@ -207,6 +207,10 @@ int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t la
   if (latent < 512)
     return fail(MX_E_SHAPE, "the slot-order store needs latent >= 512, got %lld", (long long)latent);
   if (empty) return ok();
+  const int64_t need = mxfp4_inverse_bytes(num_blocks, block_size);
+  if (inverse_bytes < need)
+    return fail(MX_E_RANGE, "inverse holds %lld bytes, %lld slots need %lld",
+                (long long)inverse_bytes, (long long)(num_blocks * block_size), (long long)need);
   if (!aligned(inverse, 16)) return fail(MX_E_ALIGN, "inverse must be 16-byte aligned");
   return launched(mxs::launch_mxfp4_store_by_slot(a, (int)latent, inverse, (hipStream_t)stream),
                   "mxfp4_store_by_slot");

@@ -78,7 +78,7 @@ def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tens
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int64 tensor")
     if cache.dtype != torch.uint8:
-        raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
+        raise ValueError(f"the cache is raw bytes (torch.uint8), not {cache.dtype}")
     num_tokens = slot_mapping.numel()
     if num_tokens > src.shape[0]:
         raise ValueError("slot_mapping has more entries than src has rows")
@@ -124,17 +124,17 @@ def mxfp4_store_by_slot(src: torch.Tensor, num_tokens: int, inverse: torch.Tenso
     _need_cuda(src, inverse, cache)
     if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
         raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
-    if inverse.dtype != torch.int32 or not inverse.is_contiguous() \
-            or inverse.numel() < num_blocks * block_size:
-        raise ValueError("inverse must be a contiguous int32 tensor with one entry per slot")
+    if inverse.dtype != torch.int32 or not inverse.is_contiguous():
+        raise ValueError("inverse must be a contiguous int32 tensor")
     if cache.dtype != torch.uint8:
-        raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
+        raise ValueError(f"the cache is raw bytes (torch.uint8), not {cache.dtype}")
     if num_tokens > src.shape[0]:
         raise ValueError("num_tokens exceeds the rows of src")
     _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
     _abi.check(_abi.lib().mxfp4_store_by_slot(
         src.data_ptr(), num_tokens, src.shape[1], src.stride(0), inverse.data_ptr(),
-        cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
+        inverse.numel() * 4, cache.data_ptr(), num_blocks, block_size, block_stride_rows, group,
+        _stream(stream)))
 
 
 def mxfp4_gather_dequant(cache: torch.Tensor, num_blocks: int, block_size: int,
@@ -312,18 +312,19 @@ def resolve_paged_view(cache: torch.Tensor, latent: int, group: int = GROUP_SIZE
     `store_mxfp4_mla`]: a 3-D paged [blocks, block, row_bytes] view whose block
     stride is a whole number of rows, or any tensor viewable as flat rows."""
     if cache.dtype != torch.uint8:
-        raise ValueError(f"expected a uint8 cache, got {cache.dtype}")
+        raise ValueError(f"the cache is raw bytes (torch.uint8), not {cache.dtype}")
     pitch = row_bytes(latent, group)
     if cache.dim() == 3:
         num_blocks, block_size, width = cache.shape
         if width != pitch or tuple(cache.stride()[1:]) != (pitch, 1) or cache.stride(0) % pitch:
             raise ValueError(
-                f"paged cache {tuple(cache.shape)} with strides {cache.stride()} "
-                f"is not a whole number of {pitch}-byte rows per block")
+                f"a paged cache is [blocks, block, {pitch}] with {pitch}-byte rows packed "
+                f"in each block and blocks a multiple of {pitch} bytes apart; this one has "
+                f"shape {tuple(cache.shape)}, strides {cache.stride()}")
         return num_blocks, block_size, cache.stride(0) // pitch
     flat = cache.view(-1)
     if flat.numel() % pitch:
-        raise ValueError(f"cache of {flat.numel()} bytes is not a multiple of {pitch}")
+        raise ValueError(f"a flat cache holds whole {pitch}-byte rows; {flat.numel()} bytes do not divide")
     n = flat.numel() // pitch
     return 1, n, n
 
@@ -338,7 +339,7 @@ def store_mxfp4_mla(kv_c_normed: torch.Tensor, slot_mapping: torch.Tensor,
     for this shape, it is ``mxfp4_build_inverse`` + ``mxfp4_store_by_slot``
     instead (same bytes)."""
     if kv_c_normed.dim() != 2:
-        raise ValueError(f"expected kv_c_normed=[tokens, latent], got {tuple(kv_c_normed.shape)}")
+        raise ValueError(f"kv_c_normed is a 2-D [tokens, latent] tensor; this one is {tuple(kv_c_normed.shape)}")
     num_blocks, block_size, stride_rows = resolve_paged_view(cache, kv_c_normed.shape[1], group)
     num_tokens = slot_mapping.numel()
     if num_tokens == 0:
@@ -363,7 +364,8 @@ def rope_quant_insert(latent, positions, cos_sin_cache, kv_cache, slot_mapping,
     fns = {MXFP8_RECORD_BYTES: mxfp8_rope_store, NVFP4_RECORD_BYTES: nvfp4_rope_store,
            V4_RECORD_BYTES: v4_rope_store}
     if kv_cache.dtype != torch.uint8 or width not in fns:
-        raise ValueError(f"unsupported paged KV record: dtype {kv_cache.dtype}, width {width}")
+        raise ValueError(f"no insert writes {width}-byte records of {kv_cache.dtype} "
+                         f"(uint8 records of 528, 288 or 584 bytes are known)")
     fn = fns[width]
     fn(latent, positions, cos_sin_cache, kv_cache, slot_mapping, compress_ratio,
        sanitize_nans, stream)

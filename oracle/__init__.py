@@ -73,6 +73,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32]
+    lib.orc_rope_rotate.restype = ctypes.c_int
+    lib.orc_rope_rotate.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp]
     lib.orc_sparse_mla_attention.restype = ctypes.c_int
     lib.orc_sparse_mla_attention.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
                                              ctypes.c_double, _vp, _vp]
@@ -194,42 +196,72 @@ class Oracle:
         _check(rc, "mxfp4_gather_dequant")
         return out
 
-    def _rope_store(self, fn_name, latent, positions, cos_sin, cache, block, num_blocks,
-                    cache_block_stride, slot_mapping, compress_ratio, sanitize) -> None:
+    def _rope_store(self, fn_name, width, latent, positions, cos_sin, cache, block, num_blocks,
+                    cache_block_stride, slot_mapping, compress_ratio, sanitize, threads) -> None:
         assert latent.dtype == np.uint16 and latent.flags.c_contiguous
         assert latent.shape[1] == 512
         assert positions.dtype == np.int64 and slot_mapping.dtype == np.int64
+        assert positions.flags.c_contiguous and slot_mapping.flags.c_contiguous
         assert cos_sin.dtype == np.float32 and cos_sin.strides[1] == 4
         assert cache.dtype == np.uint8 and cache.flags.c_contiguous
+        stride = block * width if cache_block_stride is None else cache_block_stride
+        assert cache.size >= (num_blocks - 1) * stride + block * width, \
+            "cache buffer smaller than the paged view"
         n = slot_mapping.size
         assert n <= min(latent.shape[0], positions.size)
-        rc = getattr(self.lib, fn_name)(
-            _ptr(latent), _ptr(positions), cos_sin.ctypes.data,
-            cos_sin.strides[0] // 4, cos_sin.shape[0], _ptr(cache),
-            cache_block_stride, block, num_blocks, _ptr(slot_mapping), n,
-            compress_ratio, int(bool(sanitize)))
-        _check(rc, fn_name)
+        fn = getattr(self.lib, fn_name)
+
+        def run(lo: int, hi: int) -> None:
+            rc = fn(_ptr(latent) + lo * 1024, _ptr(positions) + lo * 8, cos_sin.ctypes.data,
+                    cos_sin.strides[0] // 4, cos_sin.shape[0], _ptr(cache), stride, block,
+                    num_blocks, _ptr(slot_mapping) + lo * 8, hi - lo, compress_ratio,
+                    int(bool(sanitize)))
+            _check(rc, fn_name)
+
+        _run_chunks(run, n, threads)
+
+    def rope_rotate(self, latent, positions, cos_sin, compress_ratio, sanitize=True):
+        """The inserts' rotated fp32 latent: (float32 [T, 512], bool [T]
+        written); rows of tokens the gate rejects are NaN."""
+        assert latent.dtype == np.uint16 and latent.flags.c_contiguous
+        assert latent.shape[1] == 512
+        assert positions.dtype == np.int64 and positions.flags.c_contiguous
+        assert cos_sin.dtype == np.float32 and cos_sin.strides[1] == 4
+        n = positions.size
+        assert latent.shape[0] >= n
+        out = np.full((n, 512), np.nan, dtype=np.float32)
+        written = np.zeros(n, dtype=np.uint8)
+        rc = self.lib.orc_rope_rotate(
+            _ptr(latent), _ptr(positions), cos_sin.ctypes.data, cos_sin.strides[0] // 4,
+            cos_sin.shape[0], n, compress_ratio, int(bool(sanitize)), _ptr(out), _ptr(written))
+        _check(rc, "rope_rotate")
+        return out, written.astype(bool)
 
     def mxfp8_rope_store(self, latent, positions, cos_sin, cache, block, num_blocks,
                          slot_mapping, compress_ratio, sanitize=True,
-                         cache_block_stride=None) -> None:
-        stride = block * 528 if cache_block_stride is None else cache_block_stride
-        self._rope_store("orc_mxfp8_rope_store", latent, positions, cos_sin, cache, block,
-                         num_blocks, stride, slot_mapping, compress_ratio, sanitize)
+                         cache_block_stride=None, threads: int = 1) -> None:
+        """MXFP8 insert into the flat uint8 ``cache`` (pages ``cache_block_stride``
+        bytes apart, default one block of records).  ``threads > 1`` runs
+        contiguous token ranges concurrently (distinct slots never share bytes)."""
+        self._rope_store("orc_mxfp8_rope_store", 528, latent, positions, cos_sin, cache, block,
+                         num_blocks, cache_block_stride, slot_mapping, compress_ratio, sanitize,
+                         threads)
 
     def nvfp4_rope_store(self, latent, positions, cos_sin, cache, block, num_blocks,
                          slot_mapping, compress_ratio, sanitize=True,
-                         cache_block_stride=None) -> None:
-        stride = block * 288 if cache_block_stride is None else cache_block_stride
-        self._rope_store("orc_nvfp4_rope_store", latent, positions, cos_sin, cache, block,
-                         num_blocks, stride, slot_mapping, compress_ratio, sanitize)
+                         cache_block_stride=None, threads: int = 1) -> None:
+        """NVFP4 insert; arguments as for ``mxfp8_rope_store``."""
+        self._rope_store("orc_nvfp4_rope_store", 288, latent, positions, cos_sin, cache, block,
+                         num_blocks, cache_block_stride, slot_mapping, compress_ratio, sanitize,
+                         threads)
 
     def v4_rope_store(self, latent, positions, cos_sin, cache, block, num_blocks,
                       slot_mapping, compress_ratio, sanitize=True,
-                      cache_block_stride=None) -> None:
-        stride = block * 584 if cache_block_stride is None else cache_block_stride
-        self._rope_store("orc_v4_rope_store", latent, positions, cos_sin, cache, block,
-                         num_blocks, stride, slot_mapping, compress_ratio, sanitize)
+                      cache_block_stride=None, threads: int = 1) -> None:
+        """V4 insert; arguments as for ``mxfp8_rope_store``."""
+        self._rope_store("orc_v4_rope_store", 584, latent, positions, cos_sin, cache, block,
+                         num_blocks, cache_block_stride, slot_mapping, compress_ratio, sanitize,
+                         threads)
 
     def sparse_mla_attention(self, q_bits: np.ndarray, cache: np.ndarray, num_blocks: int,
                              block_size: int, block_stride_rows: int, indices: np.ndarray,
@@ -321,6 +353,7 @@ dequant_bf16 = _forward("dequant_bf16")
 quantize_row = _forward("quantize_row")
 mxfp4_store = _forward("mxfp4_store")
 mxfp4_gather_dequant = _forward("mxfp4_gather_dequant")
+rope_rotate = _forward("rope_rotate")
 mxfp8_rope_store = _forward("mxfp8_rope_store")
 nvfp4_rope_store = _forward("nvfp4_rope_store")
 save_ring_rows = _forward("save_ring_rows")

@@ -462,6 +462,25 @@ static int rope_token(const uint16_t* latent_row, int64_t position,
 }
 
 /*
+ * The rotated fp32 latent of each token, as the three inserts below see it
+ * (their shared preamble above, with the slot gate left open): out[t, :] is
+ * written and written[t] = 1 when the compress-ratio gate and the table row
+ * admit token t, else written[t] = 0 and out[t, :] is left as it is.  Exposed
+ * so that the rotation itself can be checked value by value.
+ */
+int orc_rope_rotate(const uint16_t* latent, const int64_t* positions,
+                    const float* cos_sin, int64_t cos_stride, int64_t cos_rows,
+                    int64_t num_tokens, int32_t cr, int32_t sanitize, float* out,
+                    uint8_t* written) {
+  if (num_tokens < 0 || cr < 1) return ORC_EINVAL;
+  for (int64_t t = 0; t < num_tokens; ++t)
+    written[t] = (uint8_t)rope_token(latent + t * ROPE_LATENT, positions[t], cos_sin,
+                                     cos_stride, cos_rows, 0, 1, 1, cr, sanitize,
+                                     out + t * ROPE_LATENT);
+  return ORC_OK;
+}
+
+/*
  * MXFP8 record insert [P2 `_rope_quant_insert_mxfp8_kernel`].  Page of B
  * tokens = [B x 512 E4M3 values | B x 16 UE8M0 scales]; page p starts at
  * byte p * cache_block_stride.  Per group of 32 rotated values:

@@ -177,10 +177,11 @@ def test_build_inverse_rejects(mxlib, kw, status):
 
 
 def store_by_slot(mxlib, **kw):
-    a = dict(src=FAKE, n=4, latent=512, stride=512, inv=FAKE, cache=FAKE, nb=1, bs=8, bsr=8, group=32)
+    a = dict(src=FAKE, n=4, latent=512, stride=512, inv=FAKE, nbytes=32, cache=FAKE, nb=1, bs=8,
+             bsr=8, group=32)
     a.update(kw)
-    return mxlib.mxfp4_store_by_slot(a["src"], a["n"], a["latent"], a["stride"], a["inv"], a["cache"],
-                                     a["nb"], a["bs"], a["bsr"], a["group"], None)
+    return mxlib.mxfp4_store_by_slot(a["src"], a["n"], a["latent"], a["stride"], a["inv"], a["nbytes"],
+                                     a["cache"], a["nb"], a["bs"], a["bsr"], a["group"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -190,6 +191,8 @@ def store_by_slot(mxlib, **kw):
     (dict(inv=FAKE + 8), _abi.MX_E_ALIGN),
     (dict(bsr=4), _abi.MX_E_STRIDE),
     (dict(n=-3), _abi.MX_E_RANGE),
+    (dict(nbytes=16), _abi.MX_E_RANGE),          # 8 slots need 32 bytes of map
+    (dict(nb=3, bsr=8, nbytes=64), _abi.MX_E_RANGE),  # 24 slots need 96
 ])
 def test_store_by_slot_rejects(mxlib, kw, status):
     assert store_by_slot(mxlib, **kw) == status

@@ -23,7 +23,8 @@ import pytest
 import torch
 
 import oracle
-from mxfp4_paged_cache_store_amd import ops, workloads
+import workloads
+from mxfp4_paged_cache_store_amd import ops
 from tests.gpu_util import bf16_dev, log, u8_dev
 
 pytestmark = pytest.mark.gpu

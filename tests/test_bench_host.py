@@ -7,7 +7,7 @@ import sys
 import numpy as np
 import pytest
 
-from mxfp4_paged_cache_store_amd import workloads
+import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from mxfp4_paged_cache_store_amd import ops, workloads
+import workloads
+from mxfp4_paged_cache_store_amd import ops
 from tests.gpu_util import bf16_host, first_mismatch, log
 
 pytestmark = pytest.mark.gpu

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import oracle
-from mxfp4_paged_cache_store_amd import ops, workloads
+import workloads
+from mxfp4_paged_cache_store_amd import ops
 from tests.gpu_util import bf16_dev, bf16_host, first_mismatch, i64_dev, log, oracle_threads, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -52,17 +53,18 @@ def test_prefill_round_trip(device):
 
 
 @pytest.mark.parametrize("latent", [128, 256, 512, 1024, 2048])
-def test_latents_paged_bad_slots_strided_out(device, latent):
-    rng = np.random.default_rng(latent)
+@pytest.mark.parametrize("n", [333, 5001])
+def test_latents_paged_bad_slots_strided_out(device, latent, n):
+    """Every latent, paged with interleaved blocks, random slots with bad
+    ones, a strided output; 5,001 slots run the two-slots-per-wave kernel."""
+    rng = np.random.default_rng(latent + n)
     pitch = latent // 2 + latent // 32
     nb, bs, stride = 20, 48, 70
     cache = rng.integers(0, 256, size=((nb - 1) * stride + bs) * pitch, dtype=np.uint8)
-    # keep scale bytes finite-ish but cover all of them somewhere
-    n = 333
     slots = rng.integers(-3, nb * bs + 3, size=n).astype(np.int64)
     out_host = np.full((n, latent + 16), 0x5555, dtype=np.uint16)
     out_dev = bf16_dev(out_host, device)
-    log(f"dequant latent={latent}")
+    log(f"dequant latent={latent} n={n}")
     ops.mxfp4_gather_dequant(u8_dev(cache, device), nb, bs, stride, latent, i64_dev(slots, device),
                              out_dev[:, :latent])
     torch.cuda.synchronize()

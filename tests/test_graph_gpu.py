@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from mxfp4_paged_cache_store_amd import ops, workloads
+import workloads
+from mxfp4_paged_cache_store_amd import ops
 from tests.gpu_util import bf16_dev, i64_dev, log
 
 pytestmark = pytest.mark.gpu

@@ -34,6 +34,9 @@ CHECKS = [
     (pins.test_attention_hard_limit_and_order, {}),
     (pins.test_rope_gate_and_canaries, {}),
     (pins.test_rope_exact_angles_pin_pairing_and_row, {}),
+    (pins.test_rope_strided_table_and_pages, {}),
+    (pins.test_rope_rotation_general_angles_against_numpy, {}),
+    (pins.test_rope_inserts_at_general_angles, {}),
     (pins.test_nvfp4_huge_tiles_saturate, {}),
     (pins.test_e4m3_encode_matches_torch, {}),
     (pins.test_nvfp4_scales_and_codes, {}),
@@ -74,6 +77,15 @@ MUTANTS = {
         "c = cs[p - ROPE_FIRST_PAIR];\n      s = cs[32 + p - ROPE_FIRST_PAIR];",
         "s = cs[p - ROPE_FIRST_PAIR];\n      c = cs[32 + p - ROPE_FIRST_PAIR];"),
     "RoPE rotation sign": ("r[2 * p] = ec - os;", "r[2 * p] = ec + os;"),
+    "RoPE rotation fused (fmaf)": ("r[2 * p] = ec - os;", "r[2 * p] = fmaf(even, c, -os); (void)ec;"),
+    "RoPE rotation in double": (
+        "r[2 * p] = ec - os;\n    r[2 * p + 1] = oc + es;",
+        "r[2 * p] = (float)((double)even * c - (double)odd * s);\n"
+        "    r[2 * p + 1] = (float)((double)odd * c + (double)even * s); (void)ec; (void)os; (void)oc; (void)es;"),
+    "RoPE table stride ignored": ("const float* cs = cos_sin + base * cos_stride;",
+                                  "const float* cs = cos_sin + base * 64; (void)cos_stride;"),
+    "insert page stride ignored": ("uint8_t* page = cache + (slot / block) * cache_block_stride;",
+                                   "uint8_t* page = cache + (slot / block) * block * 528;"),
     "no NaN sanitising": ("if (isnan(r[d])) r[d] = 0.0f;", "(void)r;"),
     "NVFP4 scale not rounded to E4M3": ("float S = (float)e4m3_value(s8);", "float S = sf;"),
     "ring row from block stride": (

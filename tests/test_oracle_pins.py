@@ -488,6 +488,212 @@ def test_rope_gate_and_canaries(orc=oracle):
                 assert (v == 0xA5).all() and (sc == 0xA5).all(), s
 
 
+def _rope_table():
+    from workloads import rope_cos_sin_table
+
+    return rope_cos_sin_table()
+
+
+def _rope_latents(n, seed):
+    """bf16 N(0,1) rows, some scaled by 2^-130 (subnormal products) or
+    2^125 (sums near the top of the range), with signed zeros and
+    infinities in a few NoPE and RoPE dims."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    x[n // 8: n // 4] *= np.float32(2.0 ** -130)
+    x[n // 4: 3 * n // 8] *= np.float32(2.0 ** 125)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    picks = rng.integers(0, 512, (n, 6))
+    rows = np.arange(n)[:, None]
+    bits[rows, picks[:, :2]] = 0x0000
+    bits[rows, picks[:, 2:4]] = 0x8000
+    bits[n - 4:, 448:452] = [0x7F80, 0xFF80, 0x7F80, 0x3F80]
+    return bits
+
+
+def _numpy_rope(bits, positions, table, cr):
+    """The pages' GPT-J rotation [P2 `_rope_quant_insert_mxfp8_kernel`: even*c
+    - odd*s, odd*c + even*s on the interleaved pairs] in numpy float32
+    element-wise operations (each product and each sum rounds once; numpy
+    does not fuse), over all 256 pairs with (c, s) = (1, 0) for the NoPE
+    pairs, using table row (position // cr) * cr."""
+    x = (bits.astype(np.uint32) << 16).view(np.float32)
+    n = x.shape[0]
+    base = positions // cr * cr
+    c = np.ones((n, 256), dtype=np.float32)
+    s = np.zeros((n, 256), dtype=np.float32)
+    c[:, 224:] = table[base, :32]
+    s[:, 224:] = table[base, 32:64]
+    e, o = x[:, 0::2], x[:, 1::2]
+    r = np.empty_like(x)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r[:, 0::2] = e * c - o * s
+        r[:, 1::2] = o * c + e * s
+    return r
+
+
+def _same_f32(a, b):
+    """Bitwise equality, NaN matching NaN whatever its payload."""
+    return (a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))
+
+
+def _e2m1_codes(y):
+    """The pages' midpoint count [P1 `_quantize_e2m1`] on fp32 quotients,
+    vectorised: index = number of midpoints below |y| (strict at 0.25, 1.25,
+    2.5, 5; inclusive at 0.75, 1.75, 3.5), sign bit when y < 0, NaN -> 0."""
+    a = np.abs(y)
+    idx = sum((a > m) if st else (a >= m) for m, st in zip(MIDS, STRICT))
+    code = idx.astype(np.uint8) | np.where(y < 0, 8, 0).astype(np.uint8)
+    return np.where(np.isnan(y), 0, code).astype(np.uint8)
+
+
+def _exact_ceil_log2_f32(v):
+    """Exact ceil(log2 v) of positive finite fp32 values (frexp of the exact
+    double: v = m * 2^k, m in [0.5, 1), ceil is k - 1 at m = 0.5, else k)."""
+    m, k = np.frexp(v.astype(np.float64))
+    return np.where(m == 0.5, k - 1, k).astype(np.int64)
+
+
+def _mxfp8_expected(r, group=32, sanitize=True):
+    """MXFP8 values and scale bytes of rotated rows r [n, D] in groups of
+    `group` [P2 `_rope_quant_insert_mxfp8_kernel`; readings R11, R14]."""
+    n, d = r.shape
+    g = r.reshape(n, d // group, group)
+    amax = np.maximum(np.abs(g).max(axis=2), np.float32(1e-4))
+    v = (amax * np.float32(1.0 / 448.0)).astype(np.float32)
+    fin = np.isfinite(v)
+    E = np.where(fin, _exact_ceil_log2_f32(np.where(fin, v, 1.0)), 128)
+    mult = np.ldexp(np.float32(1.0), -E).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        y = np.clip((g * mult[:, :, None]).astype(np.float32), -448, 448)
+    vals = _torch_e4m3(y.reshape(n, d))
+    scales = np.clip(E + 127, 0, 254 if sanitize else 255).astype(np.uint8)
+    return vals, scales
+
+
+def _nvfp4_expected(r):
+    """NVFP4 code bytes and E4M3 scales of rotated rows r [n, 512] [P2
+    `_rope_quant_insert_nvfp4_kernel`; readings R15, R16]: the quotient is
+    numpy's correctly rounded fp32 division."""
+    n = r.shape[0]
+    t = r.reshape(n, 32, 16)
+    sf = np.clip((np.abs(t).max(axis=2) * np.float32(1.0 / 6.0)).astype(np.float32),
+                 np.float32(2.0 ** -9), np.float32(448))
+    s8 = _torch_e4m3(sf)
+    S = torch.from_numpy(s8).view(torch.float8_e4m3fn).float().numpy()
+    codes = _e2m1_codes((t / S[:, :, None]).astype(np.float32)).reshape(n, 512)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), s8
+
+
+def test_rope_rotation_general_angles_against_numpy(orc=oracle):
+    """Reading R12 pinned at general angles: the oracle's rotated latent
+    equals numpy's float32 element-wise rotation bit for bit, on the real
+    65,536-row GPT-J table (theta 10^4) at random positions, for ratios 1 and
+    4, with and without sanitising.  An FMA in the rotation, or the rotation
+    evaluated in double and rounded once, changes the last bit of many
+    values and fails here."""
+    table = _rope_table()
+    rng = np.random.default_rng(41)
+    n = 4096
+    bits = _rope_latents(n, 42)
+    for cr in (1, 4):
+        positions = rng.integers(0, 65536, n).astype(np.int64)
+        if cr > 1:
+            positions[: n // 2] = positions[: n // 2] // cr * cr + cr - 1  # half pass the gate
+        want = _numpy_rope(bits, positions, table, cr)
+        gate = (positions + 1) % cr == 0
+        for sanitize in (True, False):
+            got, written = orc.rope_rotate(bits, positions, table, cr, sanitize)
+            assert (written == gate).all()
+            w = want[gate].copy()
+            if sanitize:
+                w[np.isnan(w)] = 0.0
+            ok = _same_f32(got[gate], w)
+            assert ok.all(), f"cr={cr} sanitize={sanitize}: {np.count_nonzero(~ok)} values differ"
+            assert np.isnan(got[~gate]).all()
+
+
+def test_rope_inserts_at_general_angles(orc=oracle):
+    """The three records built from numpy's rotation (above) through encoders
+    restated from the pages' rules: V4's RoPE dims are torch's bf16
+    (nearest-even) of the rotated values byte for byte, its NoPE dims and
+    the MXFP8 record follow the E8M0/E4M3 rule, NVFP4 the E4M3 tile scale and
+    the midpoint count of the fp32 quotient.  Real table, random positions,
+    ratio 1, every record compared."""
+    table = _rope_table()
+    rng = np.random.default_rng(43)
+    n = 2048
+    bits = _rope_latents(n, 44)
+    positions = rng.integers(0, 65536, n).astype(np.int64)
+    slots = rng.permutation(n).astype(np.int64)
+    r = _numpy_rope(bits, positions, table, 1)
+    r[np.isnan(r)] = 0.0
+    block = 64
+    nb = n // block
+    inv = np.argsort(slots)  # token of each slot
+
+    cache = np.full(nb * block * 528, 0xA5, dtype=np.uint8)
+    orc.mxfp8_rope_store(bits, positions, table, cache, block, nb, slots, 1)
+    pages = cache.reshape(nb, block * 528)
+    vals = pages[:, : block * 512].reshape(n, 512)
+    scales = pages[:, block * 512:].reshape(n, 16)
+    wv, ws = _mxfp8_expected(r[inv])
+    assert (vals == wv).all() and (scales == ws).all()
+
+    cache = np.full(nb * block * 288, 0xA5, dtype=np.uint8)
+    orc.nvfp4_rope_store(bits, positions, table, cache, block, nb, slots, 1)
+    pages = cache.reshape(nb, block * 288)
+    vals = pages[:, : block * 256].reshape(n, 256)
+    scales = pages[:, block * 256:].reshape(n, 32)
+    wv, ws = _nvfp4_expected(r[inv])
+    assert (scales == ws).all() and (vals == wv).all()
+
+    cache = np.full(nb * block * 584, 0xA5, dtype=np.uint8)
+    orc.v4_rope_store(bits, positions, table, cache, block, nb, slots, 1)
+    pages = cache.reshape(nb, block * 584)
+    vals = pages[:, : block * 576].reshape(n, 576)
+    scales = pages[:, block * 576:].reshape(n, 8)
+    rs = r[inv]
+    rope_bf16 = torch.from_numpy(np.ascontiguousarray(rs[:, 448:])).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+    assert (vals[:, 448:].copy().view(np.uint16) == rope_bf16).all()
+    wv, ws = _mxfp8_expected(np.ascontiguousarray(rs[:, :448]), group=64)
+    assert (vals[:, :448] == wv).all()
+    assert (scales[:, :7] == ws).all() and (scales[:, 7] == 0).all()
+
+
+def test_rope_strided_table_and_pages(orc=oracle):
+    """The table may be a column slice of a wider one (row stride > 64) and
+    pages may sit further apart than one block of records [P2
+    `rope_quant_insert` passes `cos_sin_cache.stride(0)` and
+    `kv_cache.stride(0)`].  Hand-placed: the wider table's extra columns and
+    the rows the gate never selects are NaN; pages are 48 bytes apart beyond
+    their records, the gaps (and a spare page past the last) hold canaries.
+    The result page by page equals the dense one, and every gap byte is
+    still 0xA5."""
+    table = _rope_table()[:512]
+    rng = np.random.default_rng(45)
+    n, block, nb = 96, 8, 16
+    bits = _rope_latents(n, 46)
+    positions = rng.integers(0, 512, n).astype(np.int64)
+    slots = rng.permutation(nb * block)[:n].astype(np.int64)
+    slots[::7] = -1
+    wide = np.full((512, 80), np.nan, dtype=np.float32)
+    wide[:, :64] = table
+    for fn, width in ((orc.mxfp8_rope_store, 528), (orc.nvfp4_rope_store, 288),
+                      (orc.v4_rope_store, 584)):
+        for cr in (1, 4):
+            dense = np.full(nb * block * width, 0xA5, dtype=np.uint8)
+            fn(bits, positions, table, dense, block, nb, slots, cr)
+            stride = block * width + 48
+            strided = np.full((nb + 1) * stride, 0xA5, dtype=np.uint8)
+            fn(bits, positions, wide[:, :64], strided, block, nb, slots, cr,
+               cache_block_stride=stride)
+            pages = strided.reshape(nb + 1, stride)
+            assert (pages[:nb, : block * width].reshape(-1) == dense).all(), (width, cr)
+            assert (pages[:nb, block * width:] == 0xA5).all() and (pages[nb] == 0xA5).all()
+
+
 def test_nvfp4_scales_and_codes(orc=oracle):
     """NVFP4 tile scale = torch E4M3 of clamp(fp32(amax * fl(1/6)), 2^-9, 448);
     codes = the pages' midpoint count on the numpy fp32 quotient r / scale,

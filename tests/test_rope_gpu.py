@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import oracle
-from mxfp4_paged_cache_store_amd import ops, workloads
+import workloads
+from mxfp4_paged_cache_store_amd import ops
 from tests.gpu_util import bf16_dev, first_mismatch, i64_dev, log, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -198,3 +199,42 @@ def test_mxfp8_exponent_just_above_powers_of_two(device):
     assert (got == want).all(), first_mismatch(got, want)
     scales = want[n * 512:].reshape(n, 16)[:, 14]
     assert [int(b) - 127 for b in scales] == [k + 1 for k in ks]
+
+
+@pytest.mark.parametrize("variant", ["mxfp8", "nvfp4", "v4"])
+@pytest.mark.parametrize("cr,n", [(1, 70_001), (4, 16_384)])
+def test_rope_strided_table_and_interleaved_pages(device, variant, cr, n):
+    """The table as a column slice of a wider one (row stride 96 floats, the
+    extra columns NaN) and pages 48 bytes further apart than one block of
+    records (the gaps, and a spare page past the last, hold canaries)
+    [P2 `rope_quant_insert` passes the table's and the cache's row strides].
+    Ratio 1 at 70,001 tokens runs the several-tokens-per-wave kernels with a
+    ragged tail; ratio 4 the gated one.  Every byte of the backing buffer is
+    compared with the oracle's."""
+    from tests.gpu_util import oracle_threads
+
+    gpu_fn, orc_fn, width = VARIANTS[variant]
+    rng = np.random.default_rng(300 + cr)
+    x = rng.standard_normal((n, 512)) * np.exp2(rng.uniform(-20, 20, size=(n, 1)))
+    latent = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    positions = rng.integers(0, 65536, n).astype(np.int64)
+    block = 64
+    nb = -(-n * 21 // 20 // block)
+    slots = rng.permutation(nb * block)[:n].astype(np.int64)
+    slots[rng.random(n) < 0.05] = -1
+    wide = np.full((65536, 96), np.nan, dtype=np.float32)
+    wide[:, :64] = workloads.rope_cos_sin_table()
+    stride = block * width + 48
+    host = np.full((nb + 1) * stride, 0xA5, dtype=np.uint8)
+    backing = u8_dev(host, device)
+    view = torch.as_strided(backing, (nb, block, width), (stride, width, 1))
+    table_dev = torch.from_numpy(wide).to(device)[:, :64]
+    assert table_dev.stride(0) == 96 and view.stride(0) == stride
+    log(f"rope {variant}: {n} tokens, cr={cr}, table stride 96, page stride {stride}")
+    gpu_fn(bf16_dev(latent, device), i64_dev(positions, device), table_dev, view,
+           i64_dev(slots, device), cr)
+    torch.cuda.synchronize()
+    got = backing.cpu().numpy()
+    orc_fn(latent, positions, wide[:, :64], host, block, nb, slots, cr,
+           cache_block_stride=stride, threads=oracle_threads())
+    assert (got == host).all(), first_mismatch(got, host)

@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import oracle
-from mxfp4_paged_cache_store_amd import ops, workloads
+import workloads
+from mxfp4_paged_cache_store_amd import ops
 from tests.gpu_util import bf16_dev, first_mismatch, i64_dev, log, oracle_threads, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -103,16 +104,17 @@ def test_extreme_scale_rows(device):
 
 
 @pytest.mark.parametrize("latent", [128, 256, 1024, 2048])
-@pytest.mark.parametrize("ntok", [1, 37, 1001])
+@pytest.mark.parametrize("ntok", [1, 37, 1001, 9001, 20001])
 def test_other_latents_ragged(device, latent, ntok):
     """Power-of-two latents other than 512, ragged token counts (partial
-    waves and blocks), a non-power-of-two block with interleaved blocks, and
-    a row-strided source (the first `latent` columns of a wider tensor)."""
+    waves and blocks; 9,001 and 20,001 tokens run the two- and four-pass
+    kernels), a non-power-of-two block with interleaved blocks, and a
+    row-strided source (the first `latent` columns of a wider tensor)."""
     rng = np.random.default_rng(latent + ntok)
     wide = latent + 64
     x = rng.standard_normal((ntok, wide)) * np.exp2(rng.uniform(-10, 10, size=(ntok, 1)))
     src_wide = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
-    nb, bs, stride = 50, 48, 100
+    nb, bs, stride = max(50, ntok // 40 + 10), 48, 100
     slots = rng.choice(nb * bs, ntok, replace=False).astype(np.int64)
     slots[rng.random(ntok) < 0.1] = -1
     pitch = latent // 2 + latent // 32
@@ -351,7 +353,7 @@ def test_cache_extent_checked(device):
 
 
 def test_large_batch_ragged_generic_paging(device):
-    """A batch past the 2^18-token switch (4 tokens per wave) with a ragged
+    """A batch past the 16,384-token switch (4 tokens per wave) with a ragged
     tail, a non-power-of-two block, interleaved blocks and scattered slots."""
     rng = np.random.default_rng(24)
     n, nb, bs, stride = 300_001, 3100, 100, 150
