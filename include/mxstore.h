@@ -144,6 +144,31 @@ int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t la
                         int64_t block_stride_rows, int32_t group, void* stream);
 
 /*
+ * Allocation-free slot-order store, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, checks and
+ * result as mxfp4_store (and as mxfp4_build_inverse + mxfp4_store_by_slot on
+ * the same mapping): it builds the inverse map in a static device array of
+ * MX_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends, then stores in slot order.  Three launches on
+ * `stream`, no allocation, no workspace argument.
+ *   - The array of the CURRENT device is used (looked up on the first call
+ *     there); `stream` must belong to that device.
+ *   - num_blocks * block_size slots need mxfp4_inverse_bytes(num_blocks,
+ *     block_size) <= MX_NOALLOC_SCRATCH_BYTES (8,388,608 slots), else
+ *     MX_E_RANGE with nothing launched.  latent 512, 1024 or 2048;
+ *     num_tokens < 2^31.
+ *   - Every call on a GPU shares that GPU's array, and the map is rebuilt by
+ *     each call: calls that overlap on one GPU (on different streams without
+ *     ordering between them) race and may write wrong rows.
+ */
+#define MX_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+int mxfp4_store_slot_order_noalloc(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                                   int64_t src_row_stride, const int64_t* slot_mapping,
+                                   uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                                   int64_t block_stride_rows, int32_t group, void* stream);
+
+/*
  * MXFP4 gather-dequant [P3 Details, read path: unpack to bf16; Claims: the
  * result equals the dequantized values stored as bf16].  For each i <
  * num_slots_in_list with slot s = slots[i] in range, writes

@@ -21,6 +21,7 @@ from .ops import (
     mxfp4_inverse_bytes,
     mxfp4_slot_order_advised,
     mxfp4_store_by_slot,
+    mxfp4_store_slot_order_noalloc,
     mxfp8_rope_store,
     nvfp4_rope_store,
     v4_rope_store,
@@ -48,6 +49,7 @@ __all__ = [
     "mxfp4_inverse_bytes",
     "mxfp4_slot_order_advised",
     "mxfp4_store_by_slot",
+    "mxfp4_store_slot_order_noalloc",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
     "v4_rope_store",

@@ -20,6 +20,7 @@ MX_E_ALIGN = -4
 MX_E_RANGE = -5
 MX_E_ARG = -6
 MX_E_LAUNCH = -7
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MX_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/mxstore.h declares.
 EXPORTED = (
@@ -29,6 +30,7 @@ EXPORTED = (
     "mxfp4_slot_order_advised",
     "mxfp4_build_inverse",
     "mxfp4_store_by_slot",
+    "mxfp4_store_slot_order_noalloc",
     "mxfp4_gather_dequant",
     "mxfp8_rope_store",
     "nvfp4_rope_store",
@@ -80,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_build_inverse.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
         L.mxfp4_store_by_slot.restype = ctypes.c_int
         L.mxfp4_store_by_slot.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp]
+        L.mxfp4_store_slot_order_noalloc.restype = ctypes.c_int
+        L.mxfp4_store_slot_order_noalloc.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64,
+                                                     _i32, _vp]
         L.mxfp4_gather_dequant.restype = ctypes.c_int
         L.mxfp4_gather_dequant.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp]
         for name in ("mxfp8_rope_store", "nvfp4_rope_store", "v4_rope_store"):

@@ -115,6 +115,12 @@ hipError_t launch_build_inverse(const int64_t* slots, int64_t num_tokens, uint32
                                 int32_t* inverse, hipStream_t stream);
 hipError_t launch_mxfp4_store_by_slot(const StoreArgs& a, int latent, const int32_t* inverse,
                                       hipStream_t stream);
+// The slot-order store with its inverse map in the library's static device
+// array (kNoAllocScratchBytes per GPU, looked up once per device): no
+// allocation, no workspace.  The caller has checked that the map fits.
+constexpr int64_t kNoAllocScratchBytes = int64_t(32) << 20;
+hipError_t launch_mxfp4_store_slot_order_noalloc(const StoreArgs& a, int latent,
+                                                 hipStream_t stream);
 hipError_t launch_mxfp4_dequant(const DequantArgs& a, int latent, hipStream_t stream);
 hipError_t launch_mxfp8_rope(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_nvfp4_rope(const RopeArgs& a, hipStream_t stream);

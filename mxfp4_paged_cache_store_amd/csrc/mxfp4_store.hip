@@ -40,9 +40,18 @@
 //     range check returns zeros or drops the access without touching
 //     memory).  Latents below 512 put several tokens in a pass and skip a
 //     pad token's load too.  All addressing is 64-bit.
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace mxs {
+
+// Inverse map of the allocation-free slot-order store, one int32 per slot.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code this name is only a stand-in for the symbol: the device
+// address comes from hipGetSymbolAddress (scratch_of_current_device).
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / 4];
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -446,6 +455,46 @@ hipError_t launch_mxfp4_store_by_slot(const StoreArgs& a, int latent, const int3
     case 2048: return launch_by_slot<2048>(a, inverse, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there and kept (each GPU holds the array at its own address).
+hipError_t scratch_of_current_device(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_mxfp4_store_slot_order_noalloc(const StoreArgs& a, int latent,
+                                                 hipStream_t stream) {
+  if ((int64_t)a.map.num_slots * 4 > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  int32_t* inv = nullptr;
+  hipError_t e = scratch_of_current_device(&inv);
+  if (e != hipSuccess) return e;
+  // The map is refilled on every call (fill kernel, then the tokens'
+  // entries), so nothing a previous call left in the array is read.
+  e = launch_build_inverse(a.slots, a.num_tokens, a.map.num_slots, inv, stream);
+  if (e != hipSuccess) return e;
+  return launch_mxfp4_store_by_slot(a, latent, inv, stream);
 }
 
 hipError_t launch_mxfp4_store(const StoreArgs& a, int latent, hipStream_t stream) {

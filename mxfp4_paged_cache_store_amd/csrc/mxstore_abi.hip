@@ -216,6 +216,32 @@ int mxfp4_store_by_slot(const uint16_t* src_bf16, int64_t num_tokens, int64_t la
                   "mxfp4_store_by_slot");
 }
 
+static_assert(MX_NOALLOC_SCRATCH_BYTES == mxs::kNoAllocScratchBytes,
+              "the header's scratch size is the array's");
+
+int mxfp4_store_slot_order_noalloc(const uint16_t* src_bf16, int64_t num_tokens, int64_t latent,
+                                   int64_t src_row_stride, const int64_t* slot_mapping,
+                                   uint8_t* cache, int64_t num_blocks, int64_t block_size,
+                                   int64_t block_stride_rows, int32_t group, void* stream) {
+  mxs::StoreArgs a{};
+  bool empty = false;
+  int rc = check_store(src_bf16, num_tokens, latent, src_row_stride, slot_mapping, cache,
+                       num_blocks, block_size, block_stride_rows, group, &a, &empty);
+  if (rc) return rc;
+  if (latent < 512)
+    return fail(MX_E_SHAPE, "the slot-order store needs latent >= 512, got %lld", (long long)latent);
+  const int64_t need = mxfp4_inverse_bytes(num_blocks, block_size);
+  if (need > MX_NOALLOC_SCRATCH_BYTES)
+    return fail(MX_E_RANGE, "%lld slots need a %lld-byte inverse map; the static one holds %lld",
+                (long long)(num_blocks * block_size), (long long)need,
+                (long long)MX_NOALLOC_SCRATCH_BYTES);
+  if (num_tokens > 0x7FFFFFFF) return fail(MX_E_RANGE, "num_tokens must be in [0, 2^31)");
+  if (empty) return ok();
+  a.slots = slot_mapping;
+  return launched(mxs::launch_mxfp4_store_slot_order_noalloc(a, (int)latent, (hipStream_t)stream),
+                  "mxfp4_store_slot_order_noalloc");
+}
+
 int mxfp4_gather_dequant(const uint8_t* cache, int64_t num_blocks, int64_t block_size,
                          int64_t block_stride_rows, int64_t latent, int32_t group,
                          const int64_t* slots, int64_t num_slots_in_list, uint16_t* out_bf16,

@@ -137,6 +137,29 @@ def mxfp4_store_by_slot(src: torch.Tensor, num_tokens: int, inverse: torch.Tenso
         _stream(stream)))
 
 
+def mxfp4_store_slot_order_noalloc(src: torch.Tensor, slot_mapping: torch.Tensor,
+                                   cache: torch.Tensor, num_blocks: int, block_size: int,
+                                   block_stride_rows: int, group: int = GROUP_SIZE,
+                                   stream=None) -> None:
+    """``mxfp4_store_slot_order_noalloc`` of the C ABI: the slot-order store
+    with its inverse map in the library's static per-GPU array (no
+    allocation, no workspace; calls that overlap on one GPU race)."""
+    _need_cuda(src, slot_mapping, cache)
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    if cache.dtype != torch.uint8:
+        raise ValueError(f"the cache is raw bytes (torch.uint8), not {cache.dtype}")
+    num_tokens = slot_mapping.numel()
+    if num_tokens > src.shape[0]:
+        raise ValueError("slot_mapping has more entries than src has rows")
+    _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
+    _abi.check(_abi.lib().mxfp4_store_slot_order_noalloc(
+        src.data_ptr(), num_tokens, src.shape[1], src.stride(0), slot_mapping.data_ptr(),
+        cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
+
+
 def mxfp4_gather_dequant(cache: torch.Tensor, num_blocks: int, block_size: int,
                          block_stride_rows: int, latent: int, slots: torch.Tensor,
                          out: torch.Tensor, group: int = GROUP_SIZE, stream=None) -> torch.Tensor:
