@@ -54,7 +54,16 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=4_500_000)
     p.add_argument("--scatter", action="store_true", help="time the scatter form as the step")
     p.add_argument("--counters", action="store_true",
-                   help="for rocprofv3 --pmc: a 1 GiB copy (calibration) then 3 steps, no JSON")
+                   help="for rocprofv3 --pmc: a 1 GiB copy (calibration) then 3 launches of each "
+                        "kernel of --counter-set, no JSON")
+    p.add_argument("--counter-set", choices=("store", "companions", "probes", "pads"), default="store",
+                   help="what --counters runs: the store step, the companions, or the probes")
+    p.add_argument("--only", default="",
+                   help="comma-separated companion names to run (default: all)")
+    p.add_argument("--probes", action="store_true",
+                   help="time the memory-system probes of libmxprobe.so (one JSON line each)")
+    p.add_argument("--pads", action="store_true",
+                   help="time the scatter store on pad-heavy batches (one JSON line each)")
     return p.parse_args()
 
 
@@ -234,136 +243,317 @@ def small_stores(torch, ops, workloads, steps, warmup):
     return out
 
 
-def companions(torch, ops, workloads, steps, warmup, cache, n_tokens):
+COMPANIONS = ("mxfp4_gather_dequant", "save_ring_rows", "fused_save_compress_norm_cr1",
+              "rope_store", "rope_store_large", "sparse_mla_attention",
+              "sparse_mla_attention_decode", "small_stores")
+
+
+def companions(torch, ops, workloads, steps, warmup, cache, n_tokens, only=(), counters=False):
+    """Each companion on its own workload.  `only`: names from COMPANIONS to
+    run (all when empty).  With `counters`, each kernel is launched three
+    times and nothing is timed (for rocprofv3 --pmc)."""
     out = {}
-    # gather-dequant of every slot of the large cache back to bf16
-    slots = torch.arange(n_tokens, dtype=torch.int64, device="cuda")
-    dq = torch.empty((n_tokens, 512), dtype=torch.bfloat16, device="cuda")
-    _, ev = time_launches(lambda: ops.mxfp4_gather_dequant(cache, 1, n_tokens, n_tokens, 512, slots, dq),
-                          max(3, steps // 3), warmup, torch)
-    per = ev / max(3, steps // 3)
-    out["mxfp4_gather_dequant"] = {
-        "workload": f"{n_tokens} slots of the flat cache -> bf16 [{n_tokens}, 512]",
-        "us_per_launch": round(per * 1e6, 2),
-        "slots_per_s": round(n_tokens / per, 1),
-        "GBps": round(n_tokens * 1304 / per / 1e9, 1),
-        "frac_hbm_peak": round(n_tokens * 1304 / per / 1e9 / HBM_PEAK_GBS, 4),
-    }
-    del dq, slots
-    # ring-state save: 262,144 fp32 [kv, score] rows (1024 wide) to scattered
-    # slots of an 8192-block x 32-row ring
-    rows, ring_slots, ring_shape = workloads.ring_large_device()
-    n_rows = rows.shape[0]
-    ring = torch.zeros(ring_shape, dtype=torch.float32, device="cuda")
-    _, ev = time_launches(lambda: ops.save_ring_rows(rows, ring_slots, ring), steps, warmup, torch)
-    per = ev / steps
-    out["save_ring_rows"] = {
-        "workload": f"{n_rows} fp32 rows x 1024 -> scattered slots of an 8192 x 32 ring",
-        "us_per_launch": round(per * 1e6, 2),
-        "GBps": round(n_rows * (4096 + 4096 + 8) / per / 1e9, 1),
-        "frac_hbm_peak": round(n_rows * (4096 + 4096 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
-    }
-    del rows, ring, ring_slots
-    # compress-ratio-1 RMSNorm: 2,097,152 fp32 [512] rows -> bf16, all valid
-    n_norm = 1 << 21
-    kv = torch.empty((n_norm, 512), dtype=torch.float32, device="cuda").normal_()
-    norm_slots = torch.arange(n_norm, dtype=torch.int64, device="cuda")
-    w = torch.empty(512, dtype=torch.float32, device="cuda").normal_(0.8, 0.5).to(torch.bfloat16)
-    latent_out = torch.empty((n_norm, 512), dtype=torch.bfloat16, device="cuda")
-    _, ev = time_launches(lambda: ops.fused_save_compress_norm_cr1(kv, norm_slots, w, 1e-6, latent_out),
-                          steps, warmup, torch)
-    per = ev / steps
-    out["fused_save_compress_norm_cr1"] = {
-        "workload": f"{n_norm} fp32 rows x 512 -> bf16 RMSNorm, all tokens valid",
-        "us_per_launch": round(per * 1e6, 2),
-        "tokens_per_s": round(n_norm / per, 1),
-        "GBps": round(n_norm * (2048 + 1024 + 8) / per / 1e9, 1),
-        "frac_hbm_peak": round(n_norm * (2048 + 1024 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
-    }
-    del kv, norm_slots, w, latent_out
-    # RoPE inserts on the 16384-token, compress-ratio-4 workload
-    case = workloads.rope_case()
-    lat = torch.from_numpy(case.latent.view("int16")).cuda().view(torch.bfloat16)
-    pos = torch.from_numpy(case.positions).cuda()
-    cs = torch.from_numpy(case.cos_sin).cuda()
-    sl = torch.from_numpy(case.slots).cuda()
-    written = int(((case.positions + 1) % case.compress_ratio == 0).sum())
-    for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
-                            ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
-                            ("v4_rope_store", ops.v4_rope_store, 584)):
-        kv = torch.zeros((case.num_blocks, case.block, width), dtype=torch.uint8, device="cuda")
-        insert = lambda: fn(lat, pos, cs, kv, sl, case.compress_ratio)  # noqa: E731
-        _, ev = time_launches(insert, steps, warmup, torch)
-        per = ev / steps
-        per_graph = time_graph(insert, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
-        nbytes = written * (1024 + 256 + 16 + width) + (case.latent.shape[0] - written) * 16
-        out[name] = {
-            "workload": f"{case.latent.shape[0]} tokens, CR {case.compress_ratio} ({written} written), "
-                        f"{width}-byte records",
-            "us_per_launch": round(per * 1e6, 2),
-            "GBps": round(nbytes / per / 1e9, 1),
-            "graph_us_per_launch": round(per_graph * 1e6, 2),
-        }
-    del lat, pos, sl, kv
-    # the same inserts at bandwidth scale: 1,048,576 tokens, compress ratio 1
-    # (every token written), random positions and a permutation of the slots
-    lat, pos, cs, sl = workloads.rope_large_device()
-    n_big = lat.shape[0]
-    for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
-                            ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
-                            ("v4_rope_store", ops.v4_rope_store, 584)):
-        kv = torch.zeros((n_big // 64, 64, width), dtype=torch.uint8, device="cuda")
-        _, ev = time_launches(lambda: fn(lat, pos, cs, kv, sl, 1), max(10, steps), warmup, torch)
-        per = ev / max(10, steps)
-        nbytes = n_big * (1024 + 256 + 16 + width)
-        out[name + "_large"] = {
-            "workload": f"{n_big} tokens, CR 1 (all written), {width}-byte records, scattered slots",
-            "us_per_launch": round(per * 1e6, 2),
-            "GBps": round(nbytes / per / 1e9, 1),
-            "frac_hbm_peak": round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4),
-        }
-        del kv
-    del lat, pos, cs, sl
-    # sparse MLA attention over the packed cache (last: its matrix-core load
-    # can lower the clock for the launches that follow): the last 4,096 queries of a
-    # 16,384-token prefill, 32 heads, top-2048 causal slots
-    q, acache, aidx, ascale = workloads.attention_workload_device()
-    aout = torch.empty_like(q)
-    _, ev = time_launches(lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout, splits=1),
-                          max(3, steps // 3), warmup, torch)
-    per = ev / max(3, steps // 3)
-    valid = int((aidx >= 0).sum())
-    flops = 4.0 * q.shape[1] * 512 * valid
-    out["sparse_mla_attention"] = {
-        "workload": f"{q.shape[0]} queries x {q.shape[1]} heads, top-{aidx.shape[1]} of a "
-                    f"{acache.shape[0]}-token MXFP4 cache ({valid} valid slot reads)",
-        "us_per_launch": round(per * 1e6, 2),
-        "TFLOPs": round(flops / per / 1e12, 1),
-        "frac_bf16_mfma_peak": round(flops / per / 1e12 / BF16_PEAK_TFLOPS, 4),
-    }
-    del q, acache, aidx, aout
-    # decode: the last 64 queries of the same context, in the advised split form
-    q, acache, aidx, ascale = workloads.attention_workload_device(tokens=64)
-    aout = torch.empty_like(q)
-    splits = ops.sparse_mla_attention_splits_advised(64, q.shape[1], aidx.shape[1])
-    ws = torch.empty(max(256, ops.sparse_mla_attention_workspace_bytes(64, q.shape[1], splits)),
-                     dtype=torch.uint8, device="cuda")
-    decode = lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout,  # noqa: E731
-                                              splits=splits, workspace=ws)
-    _, ev = time_launches(decode, max(10, steps), warmup, torch)
-    per = ev / max(10, steps)
-    per_graph = time_graph(decode, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
-    valid = int((aidx >= 0).sum())
-    flops = 4.0 * q.shape[1] * 512 * valid
-    out["sparse_mla_attention_decode"] = {
-        "workload": f"{q.shape[0]} decode queries x {q.shape[1]} heads, top-{aidx.shape[1]} of a "
-                    f"{acache.shape[0]}-token MXFP4 cache, {splits} key ranges + merge",
-        "us_per_call": round(per * 1e6, 2),
-        "TFLOPs": round(flops / per / 1e12, 1),
-        "graph_us_per_call": round(per_graph * 1e6, 2),
-    }
-    del q, acache, aidx, aout, ws
+    want = lambda name: not only or name in only  # noqa: E731
+
+    def timed(fn, reps):
+        if counters:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            return None
+        _, ev = time_launches(fn, reps, warmup, torch)
+        return ev / reps
+
+    if want("mxfp4_gather_dequant"):
+        # gather-dequant of every slot of the large cache back to bf16
+        slots = torch.arange(n_tokens, dtype=torch.int64, device="cuda")
+        dq = torch.empty((n_tokens, 512), dtype=torch.bfloat16, device="cuda")
+        per = timed(lambda: ops.mxfp4_gather_dequant(cache, 1, n_tokens, n_tokens, 512, slots, dq),
+                    max(3, steps // 3))
+        if per is not None:
+            out["mxfp4_gather_dequant"] = {
+                "workload": f"{n_tokens} slots of the flat cache -> bf16 [{n_tokens}, 512]",
+                "us_per_launch": round(per * 1e6, 2),
+                "slots_per_s": round(n_tokens / per, 1),
+                "GBps": round(n_tokens * 1304 / per / 1e9, 1),
+                "frac_hbm_peak": round(n_tokens * 1304 / per / 1e9 / HBM_PEAK_GBS, 4),
+            }
+        del dq, slots
+    if want("save_ring_rows"):
+        # ring-state save: 262,144 fp32 [kv, score] rows (1024 wide) to
+        # scattered slots of an 8192-block x 32-row ring
+        rows, ring_slots, ring_shape = workloads.ring_large_device()
+        n_rows = rows.shape[0]
+        ring = torch.zeros(ring_shape, dtype=torch.float32, device="cuda")
+        per = timed(lambda: ops.save_ring_rows(rows, ring_slots, ring), steps)
+        if per is not None:
+            out["save_ring_rows"] = {
+                "workload": f"{n_rows} fp32 rows x 1024 -> scattered slots of an 8192 x 32 ring",
+                "us_per_launch": round(per * 1e6, 2),
+                "GBps": round(n_rows * (4096 + 4096 + 8) / per / 1e9, 1),
+                "frac_hbm_peak": round(n_rows * (4096 + 4096 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
+            }
+        del rows, ring, ring_slots
+    if want("fused_save_compress_norm_cr1"):
+        # compress-ratio-1 RMSNorm: 2,097,152 fp32 [512] rows -> bf16, all valid
+        n_norm = 1 << 21
+        kv = torch.empty((n_norm, 512), dtype=torch.float32, device="cuda").normal_()
+        norm_slots = torch.arange(n_norm, dtype=torch.int64, device="cuda")
+        w = torch.empty(512, dtype=torch.float32, device="cuda").normal_(0.8, 0.5).to(torch.bfloat16)
+        latent_out = torch.empty((n_norm, 512), dtype=torch.bfloat16, device="cuda")
+        per = timed(lambda: ops.fused_save_compress_norm_cr1(kv, norm_slots, w, 1e-6, latent_out), steps)
+        if per is not None:
+            out["fused_save_compress_norm_cr1"] = {
+                "workload": f"{n_norm} fp32 rows x 512 -> bf16 RMSNorm, all tokens valid",
+                "us_per_launch": round(per * 1e6, 2),
+                "tokens_per_s": round(n_norm / per, 1),
+                "GBps": round(n_norm * (2048 + 1024 + 8) / per / 1e9, 1),
+                "frac_hbm_peak": round(n_norm * (2048 + 1024 + 8) / per / 1e9 / HBM_PEAK_GBS, 4),
+            }
+        del kv, norm_slots, w, latent_out
+    if want("rope_store"):
+        # RoPE inserts on the 16384-token, compress-ratio-4 workload
+        case = workloads.rope_case()
+        lat = torch.from_numpy(case.latent.view("int16")).cuda().view(torch.bfloat16)
+        pos = torch.from_numpy(case.positions).cuda()
+        cs = torch.from_numpy(case.cos_sin).cuda()
+        sl = torch.from_numpy(case.slots).cuda()
+        written = int(((case.positions + 1) % case.compress_ratio == 0).sum())
+        for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
+                                ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
+                                ("v4_rope_store", ops.v4_rope_store, 584)):
+            kv = torch.zeros((case.num_blocks, case.block, width), dtype=torch.uint8, device="cuda")
+            insert = lambda: fn(lat, pos, cs, kv, sl, case.compress_ratio)  # noqa: E731
+            per = timed(insert, steps)
+            if per is not None:
+                per_graph = time_graph(insert, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
+                nbytes = written * (1024 + 256 + 16 + width) + (case.latent.shape[0] - written) * 16
+                out[name] = {
+                    "workload": f"{case.latent.shape[0]} tokens, CR {case.compress_ratio} ({written} "
+                                f"written), {width}-byte records",
+                    "us_per_launch": round(per * 1e6, 2),
+                    "GBps": round(nbytes / per / 1e9, 1),
+                    "graph_us_per_launch": round(per_graph * 1e6, 2),
+                }
+        del lat, pos, sl, kv
+    if want("rope_store_large"):
+        # the same inserts at bandwidth scale: 1,048,576 tokens, compress
+        # ratio 1 (every token written), random positions and a permutation
+        # of the slots
+        lat, pos, cs, sl = workloads.rope_large_device()
+        n_big = lat.shape[0]
+        for name, fn, width in (("mxfp8_rope_store", ops.mxfp8_rope_store, 528),
+                                ("nvfp4_rope_store", ops.nvfp4_rope_store, 288),
+                                ("v4_rope_store", ops.v4_rope_store, 584)):
+            kv = torch.zeros((n_big // 64, 64, width), dtype=torch.uint8, device="cuda")
+            per = timed(lambda: fn(lat, pos, cs, kv, sl, 1), max(10, steps))
+            if per is not None:
+                nbytes = n_big * (1024 + 256 + 16 + width)
+                out[name + "_large"] = {
+                    "workload": f"{n_big} tokens, CR 1 (all written), {width}-byte records, "
+                                f"scattered slots",
+                    "us_per_launch": round(per * 1e6, 2),
+                    "GBps": round(nbytes / per / 1e9, 1),
+                    "frac_hbm_peak": round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4),
+                }
+            del kv
+        del lat, pos, cs, sl
+    if want("sparse_mla_attention"):
+        # sparse MLA attention over the packed cache (after the HBM-bound
+        # companions: its matrix-core load can lower the clock for the
+        # launches that follow): the last 4,096 queries of a 16,384-token
+        # prefill, 32 heads, top-2048 causal slots
+        q, acache, aidx, ascale = workloads.attention_workload_device()
+        aout = torch.empty_like(q)
+        per = timed(lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout, splits=1),
+                    max(3, steps // 3))
+        if per is not None:
+            valid = int((aidx >= 0).sum())
+            flops = 4.0 * q.shape[1] * 512 * valid
+            out["sparse_mla_attention"] = {
+                "workload": f"{q.shape[0]} queries x {q.shape[1]} heads, top-{aidx.shape[1]} of a "
+                            f"{acache.shape[0]}-token MXFP4 cache ({valid} valid slot reads)",
+                "us_per_launch": round(per * 1e6, 2),
+                "TFLOPs": round(flops / per / 1e12, 1),
+                "frac_bf16_mfma_peak": round(flops / per / 1e12 / BF16_PEAK_TFLOPS, 4),
+            }
+        del q, acache, aidx, aout
+    if want("sparse_mla_attention_decode"):
+        # decode: the last 64 queries of the same context, in the advised
+        # split form
+        q, acache, aidx, ascale = workloads.attention_workload_device(tokens=64)
+        aout = torch.empty_like(q)
+        splits = ops.sparse_mla_attention_splits_advised(64, q.shape[1], aidx.shape[1])
+        ws = torch.empty(max(256, ops.sparse_mla_attention_workspace_bytes(64, q.shape[1], splits)),
+                         dtype=torch.uint8, device="cuda")
+        decode = lambda: ops.sparse_mla_attention(q, acache, aidx, ascale, out=aout,  # noqa: E731
+                                                  splits=splits, workspace=ws)
+        per = timed(decode, max(10, steps))
+        if per is not None:
+            per_graph = time_graph(decode, GRAPH_LAUNCHES, GRAPH_REPLAYS, torch)
+            valid = int((aidx >= 0).sum())
+            flops = 4.0 * q.shape[1] * 512 * valid
+            out["sparse_mla_attention_decode"] = {
+                "workload": f"{q.shape[0]} decode queries x {q.shape[1]} heads, top-{aidx.shape[1]} "
+                            f"of a {acache.shape[0]}-token MXFP4 cache, {splits} key ranges + merge",
+                "us_per_call": round(per * 1e6, 2),
+                "TFLOPs": round(flops / per / 1e12, 1),
+                "graph_us_per_call": round(per_graph * 1e6, 2),
+            }
+        del q, acache, aidx, aout, ws
     return out
+
+
+PROBE_REPS = 20
+PAD_TOKENS = (16384, 262144)
+PAD_FRACTIONS = (0.0, 0.5, 0.9)
+
+
+def run_pads(torch, ops, counters: bool = False) -> None:
+    """The scatter store on batches where a share of the slots are pads (-1,
+    at random positions, as in a batch padded to a captured size): 16,384 and
+    262,144 tokens x 512 into a flat cache with four slots per token, valid
+    tokens on distinct random slots.  Bytes per launch count 1304 per valid
+    token and 8 per pad.  Median of PROBE_REPS HIP-event times of single
+    launches after a 1 GiB read (flushed) and back to back (warm); with
+    `counters`, three launches of each case, untimed."""
+    import statistics
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    for n in PAD_TOKENS:
+        src = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda").uniform_(-4, 4, generator=g)
+        num_slots = 4 * n
+        cache = torch.zeros(num_slots * 272, dtype=torch.uint8, device="cuda")
+        for frac in PAD_FRACTIONS:
+            slots = torch.randperm(num_slots, generator=g, device="cuda")[:n].contiguous()
+            pad = torch.rand(n, generator=g, device="cuda") < frac
+            slots[pad] = -1
+            valid = int((slots >= 0).sum())
+            fn = lambda: ops.mxfp4_store(src, slots, cache, 1, num_slots, num_slots)  # noqa: E731
+            if counters:
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                continue
+            nbytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
+            for state in ("flushed", "warm"):
+                times = []
+                for _ in range(PROBE_REPS + 2):
+                    if state == "flushed":
+                        flush.sum()
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1) / 1000.0)
+                t = statistics.median(times[2:])
+                print(json.dumps({"pads": "mxfp4_store", "tokens": n, "valid": valid,
+                                  "pad_fraction": frac, "cache": state, "reps": PROBE_REPS,
+                                  "us": round(t * 1e6, 2), "bytes": nbytes,
+                                  "GBps": round(nbytes / t / 1e9, 1)}), flush=True)
+            del slots, pad
+        del src, cache
+    del flush
+
+
+def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
+    """The memory-system probes of libmxprobe.so next to the store on the
+    same buffers (4.5M tokens: 4.608 GB of latent, a 1.224 GB cache, a random
+    permutation): read-only, write-only, the store's traffic as a plain copy
+    (1 KiB read + 272-byte row written per token) in sequential and in
+    slot order (gathered through the inverse map), and the store's slot-order
+    kernel and whole step; then the small-batch floors (an empty launch of
+    the store's grid, a plain read of the batch's latent) at 16,384 and
+    65,536 tokens.  One JSON line per probe: median of PROBE_REPS HIP-event
+    times of single launches, each after a 1 GiB read that flushes the
+    Infinity Cache.  With `counters`, three launches of each, untimed."""
+    import ctypes
+    import statistics
+
+    from mxfp4_paged_cache_store_amd import build, ops
+
+    if not os.path.exists(build.PROBE_LIB_PATH):
+        build.build_probes()
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.probe_read.argtypes = [vp, i64, vp, vp]
+    lib.probe_write.argtypes = [vp, i64, vp]
+    lib.probe_copy_rows.argtypes = [vp, i64, vp, vp, vp]
+    lib.probe_empty.argtypes = [i64, vp]
+    for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty):
+        f.restype = ctypes.c_int
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    st = lambda: int(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+    src, slots = workloads.large_case_device(n)
+    cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
+    inv = ops.mxfp4_inverse_workspace(1, n)
+    ops.mxfp4_build_inverse(slots, 1, n, inv)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    read_bytes = (n * 1024) // 16384 * 16384
+    write_bytes = (n * 272) // 16384 * 16384
+    rows = n // 16 * 16
+
+    def store_kernel():
+        ops.mxfp4_store_by_slot(src, n, inv, cache, 1, n, n)
+
+    def store_step():
+        ops.mxfp4_build_inverse(slots, 1, n, inv)
+        store_kernel()
+
+    cases = [
+        ("read_only", read_bytes, lambda: ok(lib.probe_read(src.data_ptr(), read_bytes, sink.data_ptr(), st()))),
+        ("write_only", write_bytes, lambda: ok(lib.probe_write(cache.data_ptr(), write_bytes, st()))),
+        ("copy_rows_sequential", rows * 1296,
+         lambda: ok(lib.probe_copy_rows(src.data_ptr(), rows, None, cache.data_ptr(), st()))),
+        ("copy_rows_slot_order", rows * 1300,
+         lambda: ok(lib.probe_copy_rows(src.data_ptr(), rows, inv.data_ptr(), cache.data_ptr(), st()))),
+        ("store_by_slot_kernel", n * 1300, store_kernel),
+        ("store_slot_order_step", n * BYTES_PER_TOKEN, store_step),
+    ]
+    for tokens in (16384, 65536):
+        tpw = 2 if tokens <= 16384 else 4
+        grid = tokens // (4 * tpw)  # the scatter store's workgroups at this size
+        nbytes = tokens * 1024
+        cases.append((f"empty_launch_{tokens}", 0, lambda g=grid: ok(lib.probe_empty(g, st()))))
+        cases.append((f"read_latent_{tokens}", nbytes,
+                      lambda b=nbytes: ok(lib.probe_read(src.data_ptr(), b, sink.data_ptr(), st()))))
+    for name, nbytes, fn in cases:
+        if counters:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            continue
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(PROBE_REPS):
+            flush.sum()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1000.0)
+        t = statistics.median(times)
+        line = {"probe": name, "bytes": nbytes, "reps": PROBE_REPS, "cache": "flushed",
+                "us": round(t * 1e6, 2)}
+        if nbytes:
+            line["GBps"] = round(nbytes / t / 1e9, 1)
+            line["frac_hbm_peak"] = round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)
+        print(json.dumps(line), flush=True)
+    del src, slots, cache, inv, flush
 
 
 SWEEP_TOKENS = (16384, 65536, 262144, 1048576, 4500000)
@@ -393,7 +583,7 @@ def run_sweep(torch, ops, workloads):
                 host, num_slots = workloads.request_runs_slots(n)
                 slots = torch.from_numpy(host).to("cuda")
             cache = torch.zeros(num_slots * 272, dtype=torch.uint8, device="cuda")
-            inv = torch.empty(num_slots, dtype=torch.int32, device="cuda")
+            inv = ops.mxfp4_inverse_workspace(1, num_slots)
             forms = {"scatter": lambda: ops.mxfp4_store(src, slots, cache, 1, num_slots, num_slots)}
             if ops.mxfp4_slot_order_advised(n, 512, 1, num_slots):
                 def slot_order():
@@ -423,6 +613,9 @@ def run_sweep(torch, ops, workloads):
             del src, slots, cache, inv
 
 
+LAYERS_SHARING_MAPPING = (1, 4, 16, 64)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -440,15 +633,48 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
+    only = tuple(x for x in args.only.split(",") if x)
+    unknown = [x for x in only if x not in COMPANIONS]
+    if unknown:
+        print(f"unknown companion(s) {unknown}; known: {', '.join(COMPANIONS)}", file=sys.stderr)
+        sys.exit(2)
 
     n = args.tokens
+    if args.counters:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)  # calibration: 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del a, b
+        if args.counter_set == "probes":
+            run_probes(torch, workloads, n, counters=True)
+            print("[bench] counters run done", file=sys.stderr, flush=True)
+            return
+        if args.counter_set == "pads":
+            run_pads(torch, ops, counters=True)
+            print("[bench] counters run done", file=sys.stderr, flush=True)
+            return
+        if args.counter_set == "companions":
+            cache = workloads.random_cache_device(n)
+            companions(torch, ops, workloads, args.steps, args.warmup, cache, n, only, counters=True)
+            print("[bench] counters run done", file=sys.stderr, flush=True)
+            return
+    if args.probes:
+        print(f"[bench] probes over {n} tokens", file=sys.stderr, flush=True)
+        run_probes(torch, workloads, n)
+        return
+    if args.pads:
+        print("[bench] pad-heavy batches", file=sys.stderr, flush=True)
+        run_pads(torch, ops)
+        return
+
     print(f"[bench] generating {n} tokens on the device", file=sys.stderr, flush=True)
     src, slots = workloads.large_case_device(n)
     cache = torch.zeros(n * 272, dtype=torch.uint8, device="cuda")
     valid = n  # a permutation: no pad slots
     num_slots = n
     slot_order = ops.mxfp4_slot_order_advised(n, 512, 1, num_slots) and not args.scatter
-    inv = torch.empty(num_slots, dtype=torch.int32, device="cuda")
+    inv = ops.mxfp4_inverse_workspace(1, num_slots)
 
     def scatter_step():
         ops.mxfp4_store(src, slots, cache, 1, num_slots, num_slots)
@@ -463,10 +689,6 @@ def main():
     step = slot_order_step if slot_order else scatter_step
 
     if args.counters:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)  # calibration: 1 GiB read + 1 GiB written
-        torch.cuda.synchronize()
         for _ in range(3):
             step()
         torch.cuda.synchronize()
@@ -505,14 +727,18 @@ def main():
     per_launch = sum(a.elapsed_time(b) for a, b in kev) / 1000.0 / args.steps
     if slot_order:
         kernel = "mxfp4_store_by_slot_kernel<512>"
-        algo_bytes = valid * BY_SLOT_BYTES_PER_TOKEN + num_slots * BY_SLOT_BYTES_PER_SLOT
+        kernel_bytes = valid * BY_SLOT_BYTES_PER_TOKEN + num_slots * BY_SLOT_BYTES_PER_SLOT
     else:
         kernel = "mxfp4_store_kernel<512>"
-        algo_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
+        kernel_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
+    # The metric's bytes: 1024 read + 272 written + 8 slot bytes per token.
+    algo_bytes = valid * BYTES_PER_TOKEN + (n - valid) * BYTES_PER_PAD
     _, sev = time_launches(scatter_step, args.steps, args.warmup, torch)
     scatter_s = sev / args.steps
     achieved = algo_bytes / per_launch / 1e9
+    step_gbs = algo_bytes / step_s / 1e9
     traffic = measured_traffic(n, kernel)
+    inverse_s = step_s - per_launch
 
     result = {
         "metric": "MXFP4 store tokens/s and effective HBM GB/s (% of MI355X peak), 1 GPU",
@@ -537,7 +763,7 @@ def main():
             "parallelism": "single GPU",
         },
         "effective_GBps": round(valid * BYTES_PER_TOKEN * args.steps / wall / 1e9, 1),
-        "frac_hbm_peak_whole_step": round(valid * BYTES_PER_TOKEN / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "frac_hbm_peak_whole_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
@@ -547,8 +773,13 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes,
+            "bytes_per_token": BYTES_PER_TOKEN,
             "kernel_us_per_launch": round(per_launch * 1e6, 2),
+            "kernel_own_bytes_per_launch": kernel_bytes,
             "traffic_bytes_per_token": None if traffic is None else round(traffic / valid, 1),
+            "whole_step_us": round(step_s * 1e6, 2),
+            "whole_step_achieved": round(step_gbs, 1),
+            "whole_step_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         },
         "scatter_form": {
             "kernel": "mxfp4_store_kernel<512>",
@@ -557,10 +788,19 @@ def main():
             "frac_hbm_peak": round(valid * BYTES_PER_TOKEN / scatter_s / 1e9 / HBM_PEAK_GBS, 4),
         },
     }
+    if slot_order:
+        # One inverse map serves every layer that stores with the same slot
+        # mapping in a step: per-layer cost with the map built once for L
+        # layers (L = 1 is the headline step above).
+        result["per_layer_shared_mapping"] = [
+            {"layers": L, "us_per_layer": round((per_launch + inverse_s / L) * 1e6, 2),
+             "frac_hbm_peak": round(algo_bytes / (per_launch + inverse_s / L) / 1e9 / HBM_PEAK_GBS, 4)}
+            for L in LAYERS_SHARING_MAPPING]
     if not args.no_companions:
         print("[bench] companions", file=sys.stderr, flush=True)
-        result["companions"] = companions(torch, ops, workloads, args.steps, args.warmup, cache, n)
-        result["companions"].update(small_stores(torch, ops, workloads, args.steps, args.warmup))
+        result["companions"] = companions(torch, ops, workloads, args.steps, args.warmup, cache, n, only)
+        if not only or "small_stores" in only:
+            result["companions"].update(small_stores(torch, ops, workloads, args.steps, args.warmup))
     del src, slots, inv
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

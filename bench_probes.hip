@@ -1,0 +1,148 @@
+// bench_probes.hip -- memory-system probes for the benchmark (libmxprobe.so).
+//
+// Plain kernels with the memory traffic of the MXFP4 store and none of its
+// arithmetic, used by bench.py --probes to measure what the HBM of one
+// MI355X delivers for each access pattern the store path makes:
+//   probe_read       sequential non-temporal reads (16 B per lane, 64 B per thread)
+//   probe_write      sequential plain writes
+//   probe_copy_rows  per row: read a 1 KiB row, write a 272-byte row derived
+//                    from it, four rows per wave assembled in LDS and written
+//                    as 16-byte chunks -- the store's traffic and write form.
+//                    With `order`, output row s comes from input row order[s]
+//                    (a gather in output order, as the slot-order store does);
+//                    without, row t goes to row t (both sides sequential).
+//   probe_empty      an empty kernel: the launch floor of a given grid.
+// The written bytes depend on the loaded ones so no load can be dropped; a
+// read-only probe writes one dword only when its checksum hits a constant.
+// Not part of the library's product path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBufNT = 2;
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// Consecutive logical blocks on one XCD (workgroups go round-robin over the 8).
+__device__ __forceinline__ uint32_t xcd_contiguous_block() {
+  const uint32_t nb = gridDim.x, full = nb & ~7u, b = blockIdx.x;
+  return b < full ? (b & 7u) * (full >> 3) + (b >> 3) : b;
+}
+
+// 256 threads, each reading four 16-byte vectors, 16 KiB per block.
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ src,
+                                                         uint32_t* __restrict__ sink) {
+  const int64_t base = (int64_t)xcd_contiguous_block() * 1024 + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + base + j * 256);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(256) void probe_write_kernel(u32x4* __restrict__ dst) {
+  const int64_t base = (int64_t)xcd_contiguous_block() * 1024 + threadIdx.x;
+  const uint32_t t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dst[base + j * 256] = u32x4{t, t ^ 1u, t ^ 2u, (uint32_t)j};
+}
+
+constexpr int kRowsPerWave = 4;
+constexpr int kWavesPerBlock = 4;
+constexpr int kOut = 272;                    // bytes per output row
+constexpr int kSpan = kRowsPerWave * kOut;   // 1088 bytes per wave
+
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void probe_copy_rows_kernel(
+    const uint8_t* __restrict__ src, int64_t rows, const int32_t* __restrict__ order,
+    uint8_t* __restrict__ dst) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = ((int64_t)xcd_contiguous_block() * kWavesPerBlock + wave) * kRowsPerWave;
+  if (r0 >= rows) return;
+  int32_t tok[kRowsPerWave];
+#pragma unroll
+  for (int p = 0; p < kRowsPerWave; ++p) tok[p] = order ? order[r0 + p] : (int32_t)(r0 + p);
+  u32x4 v[kRowsPerWave];
+#pragma unroll
+  for (int p = 0; p < kRowsPerWave; ++p) {
+    const bool ok = tok[p] >= 0;
+    const __amdgpu_buffer_rsrc_t rs = buffer_at(src + (ok ? (int64_t)tok[p] * 1024 : 0), ok ? 1024u : 0u);
+    v[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0, kBufNT));
+  }
+  __shared__ uint32_t stage[kWavesPerBlock][kSpan / 4];
+  uint32_t* st = stage[wave];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int p = 0; p < kRowsPerWave; ++p) {
+    valid |= (tok[p] >= 0 ? 1u : 0u) << p;
+    const uint32_t x = v[p].x ^ v[p].y ^ v[p].z ^ v[p].w;
+    st[p * (kOut / 4) + lane] = x;
+    if ((lane & 15) == 12) st[p * (kOut / 4) + 64 + (lane >> 4)] = x ^ 0x5A5A5A5Au;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const __amdgpu_buffer_rsrc_t rs = buffer_at(dst + r0 * kOut, (uint32_t)kSpan);
+#pragma unroll
+  for (int c0 = 0; c0 < kSpan / 16; c0 += kWave) {
+    const int c = c0 + lane;
+    if (c < kSpan / 16) {
+      const u32x4 d = *reinterpret_cast<const u32x4*>(&st[4 * c]);
+      const uint32_t off = (valid >> (c / (kOut / 16))) & 1u ? (uint32_t)(16 * c) : 0x7FFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void probe_empty_kernel() {}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : -7; }
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16 KiB) from src.  sink: one device dword.
+int probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16384 || bytes / 16384 > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)(bytes / 16384)), dim3(256), 0,
+                     (hipStream_t)stream, static_cast<const u32x4*>(src), sink);
+  return status(hipGetLastError());
+}
+
+// Writes `bytes` (a multiple of 16 KiB) to dst.
+int probe_write(void* dst, int64_t bytes, void* stream) {
+  if (!dst || bytes <= 0 || bytes % 16384 || bytes / 16384 > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(probe_write_kernel, dim3((unsigned)(bytes / 16384)), dim3(256), 0,
+                     (hipStream_t)stream, static_cast<u32x4*>(dst));
+  return status(hipGetLastError());
+}
+
+// rows (a multiple of 16) output rows of 272 bytes in dst, each from a
+// 1 KiB row of src: row order[s] (entries in [0, src rows) or -1: row not
+// written) or, with order NULL, row s.  src and dst 16-byte aligned.
+int probe_copy_rows(const void* src, int64_t rows, const int32_t* order, void* dst, void* stream) {
+  if (!src || !dst || rows <= 0 || rows % 16 || rows / 16 > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(probe_copy_rows_kernel, dim3((unsigned)(rows / 16)), dim3(kWave * kWavesPerBlock),
+                     0, (hipStream_t)stream, static_cast<const uint8_t*>(src), rows, order,
+                     static_cast<uint8_t*>(dst));
+  return status(hipGetLastError());
+}
+
+// An empty kernel over `blocks` workgroups of 256 threads.
+int probe_empty(int64_t blocks, void* stream) {
+  if (blocks <= 0 || blocks > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(probe_empty_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream);
+  return status(hipGetLastError());
+}
+
+}  // extern "C"

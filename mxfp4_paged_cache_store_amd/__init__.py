@@ -19,6 +19,7 @@ from .ops import (
     mxfp4_store,
     mxfp4_build_inverse,
     mxfp4_inverse_bytes,
+    mxfp4_inverse_workspace,
     mxfp4_slot_order_advised,
     mxfp4_store_by_slot,
     mxfp4_store_slot_order_noalloc,
@@ -47,6 +48,7 @@ __all__ = [
     "mxfp4_store",
     "mxfp4_build_inverse",
     "mxfp4_inverse_bytes",
+    "mxfp4_inverse_workspace",
     "mxfp4_slot_order_advised",
     "mxfp4_store_by_slot",
     "mxfp4_store_slot_order_noalloc",

@@ -19,6 +19,11 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libmxstore.so")
 INCLUDE_DIR = os.path.join(ROOT_DIR, "include")
 
+# The benchmark's memory-system probes (bench_probes.hip beside bench.py),
+# built into a library of their own: not part of libmxstore.
+PROBE_SRC = os.path.join(ROOT_DIR, "bench_probes.hip")
+PROBE_LIB_PATH = os.path.join(BUILD_DIR, "libmxprobe.so")
+
 SOURCES = ["mxstore_abi.hip", "mxfp4_store.hip", "mxfp4_dequant.hip", "rope_insert.hip",
            "ring_rows.hip", "compress_norm.hip", "sparse_attn.hip"]
 
@@ -43,10 +48,19 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None,
           out: str | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    out = out or LIB_PATH
+    """Compile libmxstore.so from the csrc/ sources (always recompiles)."""
+    return _compile([os.path.join(CSRC, s) for s in SOURCES], out or LIB_PATH, verbose,
+                    extra_flags)
+
+
+def build_probes(verbose: bool = False) -> str:
+    """Compile the benchmark's probe library, libmxprobe.so."""
+    return _compile([PROBE_SRC], PROBE_LIB_PATH, verbose, None)
+
+
+def _compile(srcs: list[str], out: str, verbose: bool, extra_flags: list[str] | None) -> str:
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp"
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE_DIR, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -65,3 +79,4 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None,
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probes(verbose="-v" in sys.argv))

@@ -89,11 +89,20 @@ def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tens
 
 
 def mxfp4_inverse_bytes(num_blocks: int, block_size: int) -> int:
-    """``mxfp4_inverse_bytes`` of the C ABI."""
+    """``mxfp4_inverse_bytes`` of the C ABI: bytes of the inverse map (one
+    int32 per slot, padded to 16)."""
     n = int(_abi.lib().mxfp4_inverse_bytes(num_blocks, block_size))
     if n < 0:
         raise ValueError("num_blocks and block_size must be >= 1 with fewer than 2^32 slots")
     return n
+
+
+def mxfp4_inverse_workspace(num_blocks: int, block_size: int, device="cuda") -> torch.Tensor:
+    """A device int32 tensor of ``mxfp4_inverse_bytes`` bytes: the inverse
+    map that ``mxfp4_build_inverse`` fills and ``mxfp4_store_by_slot`` reads
+    (its first num_blocks * block_size entries)."""
+    return torch.empty(mxfp4_inverse_bytes(num_blocks, block_size) // 4, dtype=torch.int32,
+                       device=device)
 
 
 def mxfp4_slot_order_advised(num_tokens: int, latent: int, num_blocks: int, block_size: int) -> bool:
@@ -104,7 +113,8 @@ def mxfp4_slot_order_advised(num_tokens: int, latent: int, num_blocks: int, bloc
 def mxfp4_build_inverse(slot_mapping: torch.Tensor, num_blocks: int, block_size: int,
                         inverse: torch.Tensor, stream=None) -> torch.Tensor:
     """``mxfp4_build_inverse`` of the C ABI; ``inverse`` is a device int32
-    tensor of at least num_blocks * block_size entries."""
+    tensor of at least ``mxfp4_inverse_bytes`` bytes (see
+    ``mxfp4_inverse_workspace``)."""
     _need_cuda(slot_mapping, inverse)
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int64 tensor")
@@ -358,9 +368,9 @@ def store_mxfp4_mla(kv_c_normed: torch.Tensor, slot_mapping: torch.Tensor,
     """Quantize the MLA latent to MXFP4 and write it into the paged cache
     [P1 `store_mxfp4_mla`]: same arguments and view resolution as the page's
     wrapper.  The work is one ``mxfp4_store`` launch; when an int32
-    ``inverse`` buffer is given and the library advises the slot-order form
-    for this shape, it is ``mxfp4_build_inverse`` + ``mxfp4_store_by_slot``
-    instead (same bytes)."""
+    ``inverse`` workspace (``mxfp4_inverse_workspace``) is given and the
+    library advises the slot-order form for this shape, it is
+    ``mxfp4_build_inverse`` + ``mxfp4_store_by_slot`` instead (same bytes)."""
     if kv_c_normed.dim() != 2:
         raise ValueError(f"kv_c_normed is a 2-D [tokens, latent] tensor; this one is {tuple(kv_c_normed.shape)}")
     num_blocks, block_size, stride_rows = resolve_paged_view(cache, kv_c_normed.shape[1], group)

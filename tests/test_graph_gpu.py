@@ -18,7 +18,7 @@ def test_graph_replays_match_eager(device):
     n = 1 << 17  # a dense scattered batch through the slot-order form
     g_src = torch.empty((n, 512), dtype=torch.bfloat16, device=device)
     g_slots = torch.randperm(n, device=device)
-    inv = torch.empty(n, dtype=torch.int32, device=device)
+    inv = ops.mxfp4_inverse_workspace(1, n, device)
     g_cache = torch.empty(n * 272, dtype=torch.uint8, device=device)
     p_src = torch.empty((4096, 512), dtype=torch.bfloat16, device=device)
     p_slots = torch.randperm(1 << 16, device=device)[:4096]

@@ -201,7 +201,7 @@ def test_large_int64_addressing(device):
     torch.cuda.synchronize()
     got_scatter = cache.cpu().numpy()
     assert ops.mxfp4_slot_order_advised(n, 512, 1, n)
-    inv = torch.empty(n, dtype=torch.int32, device=device)
+    inv = ops.mxfp4_inverse_workspace(1, n, device)
     cache.fill_(0xA5)
     log("store large: slot-order form")
     ops.mxfp4_build_inverse(slots, 1, n, inv)
@@ -240,7 +240,7 @@ def test_slot_order_form(device, latent, nb, bs, stride, ntok):
     slots[rng.random(ntok) < 0.03] = -1
     slots[:5] = [num_slots, num_slots + 7, 10**13, -2, -(2**40)]
     pitch = latent // 2 + latent // 32
-    inv = torch.empty(ops.mxfp4_inverse_bytes(nb, bs) // 4, dtype=torch.int32, device=device)
+    inv = ops.mxfp4_inverse_workspace(nb, bs, device)
     log(f"store slot order latent={latent} nb={nb} bs={bs} stride={stride} ntok={ntok}")
     ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
     for layer in range(2):
@@ -274,7 +274,7 @@ def test_slot_order_row_writes(device):
         host = np.full(nbytes, 0xA5, dtype=np.uint8)
         backing = u8_dev(np.full(nbytes + 16, 0xA5, dtype=np.uint8), device)
         dev_cache = backing[base: base + nbytes]
-        inv = torch.empty(ops.mxfp4_inverse_bytes(nb, bs) // 4, dtype=torch.int32, device=device)
+        inv = ops.mxfp4_inverse_workspace(nb, bs, device)
         log(f"store slot order rows: nb={nb} bs={bs} stride={stride} cache offset {base}")
         ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
         ops.mxfp4_store_by_slot(bf16_dev(src, device), ntok, inv, dev_cache, nb, bs, stride)
@@ -297,7 +297,7 @@ def test_page_api_with_inverse(device):
         src |= (rng.integers(0, 2, size=(ntok, 512), dtype=np.uint16) << 15)
         slots = rng.choice(nslots, ntok, replace=False).astype(np.int64)
         assert ops.mxfp4_slot_order_advised(ntok, 512, 1, nslots) == (ntok == 1 << 20)
-        inv = torch.empty(nslots, dtype=torch.int32, device=device)
+        inv = ops.mxfp4_inverse_workspace(1, nslots, device)
         cache = torch.full((nslots * 272,), 0xA5, dtype=torch.uint8, device=device)
         log(f"store page API with inverse: {ntok} tokens, {nslots} slots")
         ops.store_mxfp4_mla(bf16_dev(src, device), i64_dev(slots, device), cache, inverse=inv)
@@ -309,13 +309,15 @@ def test_page_api_with_inverse(device):
 
 def test_inverse_map_contents(device):
     """The inverse map itself: -1 everywhere except at the batch's valid
-    slots, which hold their token index."""
+    slots, which hold their token index; the map is the workspace's first
+    num_slots int32 entries and nothing past it is written."""
     rng = np.random.default_rng(23)
     nb, bs, n = 37, 33, 900
     slots = rng.choice(nb * bs, n, replace=False).astype(np.int64)
     slots[::17] = -1
     slots[5] = nb * bs
-    inv = torch.full((nb * bs + 4,), 12345, dtype=torch.int32, device=device)
+    words = ops.mxfp4_inverse_bytes(nb, bs) // 4
+    inv = torch.full((words + 4,), 12345, dtype=torch.int32, device=device)
     ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
     torch.cuda.synchronize()
     want = np.full(nb * bs, -1, dtype=np.int32)
@@ -323,7 +325,48 @@ def test_inverse_map_contents(device):
     want[slots[ok]] = np.flatnonzero(ok)
     got = inv.cpu().numpy()
     assert (got[: nb * bs] == want).all()
-    assert (got[nb * bs:] == 12345).all()  # nothing past the map
+    assert (got[words:] == 12345).all()  # nothing past the map
+
+
+def _check_map_with_duplicates(got, slots, num_slots):
+    """Each slot named by some tokens holds one of them; the others hold -1."""
+    ok = (slots >= 0) & (slots < num_slots)
+    owners = {}
+    for t in np.flatnonzero(ok):
+        owners.setdefault(int(slots[t]), set()).add(int(t))
+    named = np.zeros(num_slots, dtype=bool)
+    named[list(owners)] = True
+    assert (got[~named] == -1).all()
+    for s_, toks in owners.items():
+        assert int(got[s_]) in toks, (s_, int(got[s_]))
+
+
+@pytest.mark.parametrize("case", ["one_range_full", "crowded", "more_tokens_than_slots"])
+def test_inverse_map_ranges_and_duplicates(device, case):
+    """A batch that fills one contiguous range of slots exactly; one whose
+    700 tokens crowd onto 40 slots; and a batch with more tokens than slots
+    (pads, duplicates, slots past the end): every named slot holds one of
+    its tokens, every other slot -1."""
+    rng = np.random.default_rng(24)
+    nb, bs = 50, 40  # 2,000 slots
+    ns = nb * bs
+    if case == "one_range_full":
+        slots = rng.permutation(np.arange(500, 750)).astype(np.int64)
+    elif case == "crowded":
+        slots = rng.integers(750, 790, size=700).astype(np.int64)
+        slots[::50] = rng.integers(0, ns, size=14)
+    else:
+        slots = rng.integers(-2, ns + 3, size=5000).astype(np.int64)
+    inv = ops.mxfp4_inverse_workspace(nb, bs, device)
+    log(f"inverse map, {case}: {slots.size} tokens, {ns} slots")
+    ops.mxfp4_build_inverse(i64_dev(slots, device), nb, bs, inv)
+    torch.cuda.synchronize()
+    got = inv[:ns].cpu().numpy()
+    _check_map_with_duplicates(got, slots, ns)
+    if case == "one_range_full":
+        want = np.full(ns, -1, dtype=np.int32)
+        want[slots] = np.arange(slots.size)
+        assert (got == want).all()
 
 
 def test_cache_extent_checked(device):
@@ -333,7 +376,7 @@ def test_cache_extent_checked(device):
     need = ((nb - 1) * stride + bs) * 272
     src = torch.zeros((8, 512), dtype=torch.bfloat16, device=device)
     slots = torch.arange(8, dtype=torch.int64, device=device)
-    inv = torch.full((nb * bs,), -1, dtype=torch.int32, device=device)
+    inv = ops.mxfp4_inverse_workspace(nb, bs, device)
     out = torch.empty((8, 512), dtype=torch.bfloat16, device=device)
     short = torch.full((need - 1,), 0xA5, dtype=torch.uint8, device=device)
     with pytest.raises(ValueError, match="cache holds"):

@@ -43,7 +43,7 @@ def test_noalloc_matches_workspace_form_twice(device):
         runs.append((s_dev, sl_dev, noalloc, ntok, nb, bs, stride, nbytes))
     torch.cuda.synchronize()
     for s_dev, sl_dev, noalloc, ntok, nb, bs, stride, nbytes in runs:
-        inv = torch.empty(ops.mxfp4_inverse_bytes(nb, bs) // 4, dtype=torch.int32, device=device)
+        inv = ops.mxfp4_inverse_workspace(nb, bs, device)
         ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=device)
         scatter = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=device)
         log(f"workspace and scatter forms: {ntok} tokens")
