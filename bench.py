@@ -15,7 +15,10 @@ workload, and reported under "companions".
 
 Output: one JSON line (see the fields below).  `--sweep` prints further
 lines for the token-count / slot-pattern sweep with the Infinity Cache
-flushed between repetitions.
+flushed between repetitions, then the pad-heavy batches.  Other modes (no
+headline line): `--probes` (memory-system probes next to the store),
+`--pads` (pad-heavy batches), `--counters [--counter-set ...]` (launches
+only, for rocprofv3 --pmc).
 """
 
 from __future__ import annotations
@@ -810,6 +813,7 @@ def main():
         del cache
         torch.cuda.empty_cache()
         run_sweep(torch, ops, workloads)
+        run_pads(torch, ops)
 
 
 if __name__ == "__main__":

@@ -407,3 +407,21 @@ def test_large_batch_ragged_generic_paging(device):
     log(f"store {n} tokens, B={bs}, stride={stride}")
     got, want = run_both(device, src, slots, nb, bs, stride, ((nb - 1) * stride + bs) * 272)
     assert (got == want).all(), first_mismatch(got, want, 272)
+
+
+@pytest.mark.parametrize("pad", [0.5, 0.9, 1.0])
+def test_pad_heavy_large_batch(device, pad):
+    """Batches above 16,384 tokens request a token's row only once its slot
+    is known: 70,001 tokens with half, nine tenths or all of them pads
+    (negative, past the cache, -2^62), scattered into an interleaved paged
+    cache -- every cache byte as the oracle's."""
+    rng = np.random.default_rng(int(pad * 100) + 7)
+    n, nb, bs, stride = 70_001, 1200, 64, 80
+    x = rng.standard_normal((n, 512)) * np.exp2(rng.uniform(-20, 20, size=(n, 1)))
+    src = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    slots = rng.choice(nb * bs, n, replace=False).astype(np.int64)
+    bad = rng.random(n) < pad
+    slots[bad] = rng.choice(np.array([-1, -7, nb * bs, -(1 << 62)], dtype=np.int64), int(bad.sum()))
+    log(f"store {n} tokens, pad fraction {pad}")
+    got, want = run_both(device, src, slots, nb, bs, stride, ((nb - 1) * stride + bs) * 272)
+    assert (got == want).all(), first_mismatch(got, want, 272)
