@@ -626,6 +626,12 @@ def main():
               "no cross-GPU step, so run it with --gpus 1 on each GPU's share", file=sys.stderr)
         sys.exit(2)
 
+    only = tuple(x for x in args.only.split(",") if x)
+    unknown = [x for x in only if x not in COMPANIONS]
+    if unknown:
+        print(f"unknown companion(s) {unknown}; known: {', '.join(COMPANIONS)}", file=sys.stderr)
+        sys.exit(2)
+
     import torch
 
     import workloads
@@ -636,11 +642,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
-    only = tuple(x for x in args.only.split(",") if x)
-    unknown = [x for x in only if x not in COMPANIONS]
-    if unknown:
-        print(f"unknown companion(s) {unknown}; known: {', '.join(COMPANIONS)}", file=sys.stderr)
-        sys.exit(2)
 
     n = args.tokens
     if args.counters:

@@ -41,3 +41,24 @@ def test_cpu_threads_capped():
 
     threads, nproc = bench.cpu_threads()
     assert 1 <= threads <= min(16, nproc)
+
+
+def test_unknown_companion_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--only", "no_such_kernel"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "unknown companion" in r.stderr and not r.stdout
+
+
+def test_probe_library_exports():
+    """The benchmark's probe library builds for gfx950 and exports its four
+    launchers (no device work here)."""
+    import ctypes
+
+    from mxfp4_paged_cache_store_amd import build
+
+    if not os.path.exists(build.PROBE_LIB_PATH):
+        build.build_probes()
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    for name in ("probe_read", "probe_write", "probe_copy_rows", "probe_empty"):
+        assert hasattr(lib, name), name
