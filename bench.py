@@ -470,7 +470,9 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     permutation): read-only, write-only, the store's traffic as a plain copy
     (1 KiB read + 272-byte row written per token) in sequential and in
     slot order (gathered through the inverse map), and the store's slot-order
-    kernel and whole step; then the small-batch floors (an empty launch of
+    kernel and whole step; a copy of 262,144 rows of 4 KiB in order and to a
+    permutation of the rows, beside save_ring_rows on the same shapes; then
+    the small-batch floors (an empty launch of
     the store's grid, a plain read of the batch's latent) at 16,384 and
     65,536 tokens.  One JSON line per probe: median of PROBE_REPS HIP-event
     times of single launches, each after a 1 GiB read that flushes the
@@ -488,7 +490,8 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     lib.probe_write.argtypes = [vp, i64, vp]
     lib.probe_copy_rows.argtypes = [vp, i64, vp, vp, vp]
     lib.probe_empty.argtypes = [i64, vp]
-    for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty):
+    lib.probe_copy_wide.argtypes = [vp, i64, i64, vp, vp, vp]
+    for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty, lib.probe_copy_wide):
         f.restype = ctypes.c_int
 
     def ok(rc):
@@ -523,6 +526,21 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
         ("store_by_slot_kernel", n * 1300, store_kernel),
         ("store_slot_order_step", n * BYTES_PER_TOKEN, store_step),
     ]
+    # the ring-state save's traffic: 262,144 rows of 4 KiB, in order or to a
+    # permutation of the rows, next to save_ring_rows on the same shapes
+    ring_rows, ring_slots, ring_shape = workloads.ring_large_device()
+    n_ring = ring_rows.shape[0]
+    ring = torch.zeros(ring_shape, dtype=torch.float32, device="cuda")
+    ring_dst = torch.empty_like(ring_rows)
+    ring_perm = torch.randperm(n_ring, device="cuda")
+    cases += [
+        ("copy_wide_sequential", n_ring * 8192,
+         lambda: ok(lib.probe_copy_wide(ring_rows.data_ptr(), n_ring, 4096, None, ring_dst.data_ptr(), st()))),
+        ("copy_wide_scattered", n_ring * 8200,
+         lambda: ok(lib.probe_copy_wide(ring_rows.data_ptr(), n_ring, 4096, ring_perm.data_ptr(),
+                                        ring_dst.data_ptr(), st()))),
+        ("save_ring_rows", n_ring * 8200, lambda: ops.save_ring_rows(ring_rows, ring_slots, ring)),
+    ]
     for tokens in (16384, 65536):
         tpw = 2 if tokens <= 16384 else 4
         grid = tokens // (4 * tpw)  # the scatter store's workgroups at this size
@@ -556,7 +574,7 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
             line["GBps"] = round(nbytes / t / 1e9, 1)
             line["frac_hbm_peak"] = round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)
         print(json.dumps(line), flush=True)
-    del src, slots, cache, inv, flush
+    del src, slots, cache, inv, flush, ring_rows, ring_slots, ring, ring_dst, ring_perm
 
 
 SWEEP_TOKENS = (16384, 65536, 262144, 1048576, 4500000)

@@ -11,6 +11,9 @@
 //                    With `order`, output row s comes from input row order[s]
 //                    (a gather in output order, as the slot-order store does);
 //                    without, row t goes to row t (both sides sequential).
+//   probe_copy_wide  per row: copy a row of `width` bytes (a multiple of 1 KiB)
+//                    to output row order[t] (or t), one wave per row -- the
+//                    ring-state save's traffic.
 //   probe_empty      an empty kernel: the launch floor of a given grid.
 // The written bytes depend on the loaded ones so no load can be dropped; a
 // read-only probe writes one dword only when its checksum hits a constant.
@@ -103,6 +106,17 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void probe_copy_rows_kernel
   }
 }
 
+// One wave per row; lane l moves bytes 16l + 1024j of it.
+__global__ __launch_bounds__(256) void probe_copy_wide_kernel(const u32x4* __restrict__ src, int64_t rows,
+                                                              int64_t width16, const int64_t* __restrict__ order,
+                                                              u32x4* __restrict__ dst) {
+  const int64_t t = (int64_t)xcd_contiguous_block() * 4 + (threadIdx.x >> 6);
+  if (t >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t d = order ? order[t] : t;
+  for (int64_t j = lane; j < width16; j += 64) dst[d * width16 + j] = src[t * width16 + j];
+}
+
 __global__ __launch_bounds__(256) void probe_empty_kernel() {}
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -7; }
@@ -135,6 +149,18 @@ int probe_copy_rows(const void* src, int64_t rows, const int32_t* order, void* d
   hipLaunchKernelGGL(probe_copy_rows_kernel, dim3((unsigned)(rows / 16)), dim3(kWave * kWavesPerBlock),
                      0, (hipStream_t)stream, static_cast<const uint8_t*>(src), rows, order,
                      static_cast<uint8_t*>(dst));
+  return status(hipGetLastError());
+}
+
+// rows rows of `width` bytes (a multiple of 1024) from src to dst row
+// order[t] (entries in [0, rows), a permutation) or, with order NULL, row t.
+// src and dst 16-byte aligned.
+int probe_copy_wide(const void* src, int64_t rows, int64_t width, const int64_t* order, void* dst,
+                    void* stream) {
+  if (!src || !dst || rows <= 0 || width <= 0 || width % 1024 || (rows + 3) / 4 > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(probe_copy_wide_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     (hipStream_t)stream, static_cast<const u32x4*>(src), rows, width / 16, order,
+                     static_cast<u32x4*>(dst));
   return status(hipGetLastError());
 }
 

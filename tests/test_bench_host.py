@@ -51,7 +51,7 @@ def test_unknown_companion_is_refused():
 
 
 def test_probe_library_exports():
-    """The benchmark's probe library builds for gfx950 and exports its four
+    """The benchmark's probe library builds for gfx950 and exports its
     launchers (no device work here)."""
     import ctypes
 
@@ -60,5 +60,5 @@ def test_probe_library_exports():
     if not os.path.exists(build.PROBE_LIB_PATH):
         build.build_probes()
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
-    for name in ("probe_read", "probe_write", "probe_copy_rows", "probe_empty"):
+    for name in ("probe_read", "probe_write", "probe_copy_rows", "probe_copy_wide", "probe_empty"):
         assert hasattr(lib, name), name
