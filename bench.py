@@ -42,7 +42,9 @@ BYTES_PER_PAD = 8
 BY_SLOT_BYTES_PER_TOKEN = 1024 + 272
 BY_SLOT_BYTES_PER_SLOT = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mxfp4_store_large_traffic.txt")
-STORE_SRC = os.path.join(ROOT, "mxfp4_paged_cache_store_amd", "csrc", "mxfp4_store.hip")
+# the store kernel's source and the headers it includes
+STORE_SRCS = tuple(os.path.join(ROOT, "mxfp4_paged_cache_store_amd", "csrc", f)
+                   for f in ("mxfp4_store.hip", "device_common.hpp", "kernels.hpp"))
 
 
 def parse():
@@ -70,13 +72,13 @@ def parse():
     return p.parse_args()
 
 
-def source_digest(path: str) -> str:
-    """Digest of a kernel source's code: comments and blank space removed, so
-    that counters taken on a kernel stay attached to it across comment-only
-    edits."""
+def source_digest(paths) -> str:
+    """Digest of kernel sources' code (in the order given): comments and blank
+    space removed, so that counters taken on a kernel stay attached to it
+    across comment-only edits."""
     import re
 
-    text = open(path, encoding="utf-8").read()
+    text = "\n".join(open(p, encoding="utf-8").read() for p in paths)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     code = " ".join(text.split())
@@ -94,7 +96,7 @@ def measured_traffic(tokens: int, kernel: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != source_digest(STORE_SRC):
+    if kv.get("kernel_source_sha256_16") != source_digest(STORE_SRCS):
         return None
     if int(kv.get("tokens", -1)) != tokens or kv.get("kernel") != kernel:
         return None
@@ -487,8 +489,8 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.probe_read.argtypes = [vp, i64, vp, vp]
-    lib.probe_write.argtypes = [vp, i64, vp]
-    lib.probe_copy_rows.argtypes = [vp, i64, vp, vp, vp]
+    lib.probe_write.argtypes = [vp, i64, ctypes.c_int, vp]
+    lib.probe_copy_rows.argtypes = [vp, i64, vp, vp, ctypes.c_int, vp]
     lib.probe_empty.argtypes = [i64, vp]
     lib.probe_copy_wide.argtypes = [vp, i64, i64, vp, vp, vp]
     for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty, lib.probe_copy_wide):
@@ -518,11 +520,20 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
 
     cases = [
         ("read_only", read_bytes, lambda: ok(lib.probe_read(src.data_ptr(), read_bytes, sink.data_ptr(), st()))),
-        ("write_only", write_bytes, lambda: ok(lib.probe_write(cache.data_ptr(), write_bytes, st()))),
-        ("copy_rows_sequential", rows * 1296,
-         lambda: ok(lib.probe_copy_rows(src.data_ptr(), rows, None, cache.data_ptr(), st()))),
-        ("copy_rows_slot_order", rows * 1300,
-         lambda: ok(lib.probe_copy_rows(src.data_ptr(), rows, inv.data_ptr(), cache.data_ptr(), st()))),
+    ]
+    # each write probe with plain stores and written through (NT + SC1), as
+    # the slot-order store writes
+    for through, tag in ((0, ""), (1, "_through")):
+        cases += [
+            ("write_only" + tag, write_bytes,
+             lambda w=through: ok(lib.probe_write(cache.data_ptr(), write_bytes, w, st()))),
+            ("copy_rows_sequential" + tag, rows * 1296,
+             lambda w=through: ok(lib.probe_copy_rows(src.data_ptr(), rows, None, cache.data_ptr(), w, st()))),
+            ("copy_rows_slot_order" + tag, rows * 1300,
+             lambda w=through: ok(lib.probe_copy_rows(src.data_ptr(), rows, inv.data_ptr(), cache.data_ptr(), w,
+                                                      st()))),
+        ]
+    cases += [
         ("store_by_slot_kernel", n * 1300, store_kernel),
         ("store_slot_order_step", n * BYTES_PER_TOKEN, store_step),
     ]

@@ -4,13 +4,14 @@
 // arithmetic, used by bench.py --probes to measure what the HBM of one
 // MI355X delivers for each access pattern the store path makes:
 //   probe_read       sequential non-temporal reads (16 B per lane, 64 B per thread)
-//   probe_write      sequential plain writes
+//   probe_write      sequential writes: plain, or written through (NT + SC1)
 //   probe_copy_rows  per row: read a 1 KiB row, write a 272-byte row derived
 //                    from it, four rows per wave assembled in LDS and written
 //                    as 16-byte chunks -- the store's traffic and write form.
 //                    With `order`, output row s comes from input row order[s]
 //                    (a gather in output order, as the slot-order store does);
 //                    without, row t goes to row t (both sides sequential).
+//                    Its 16-byte stores are plain or written through (NT + SC1).
 //   probe_copy_wide  per row: copy a row of `width` bytes (a multiple of 1 KiB)
 //                    to output row order[t] (or t), one wave per row -- the
 //                    ring-state save's traffic.
@@ -27,6 +28,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kBufNT = 2;
+constexpr int kBufNTDevice = kBufNT | 16;  // NT + SC1: written through to memory
 constexpr int kBufWord3 = 0x00020000;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base, uint32_t bytes) {
@@ -52,11 +54,18 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+template <int kPol>
 __global__ __launch_bounds__(256) void probe_write_kernel(u32x4* __restrict__ dst) {
-  const int64_t base = (int64_t)xcd_contiguous_block() * 1024 + threadIdx.x;
+  const int64_t block = xcd_contiguous_block();
   const uint32_t t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dst[base + j * 256] = u32x4{t, t ^ 1u, t ^ 2u, (uint32_t)j};
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 v = u32x4{t, t ^ 1u, t ^ 2u, (uint32_t)j};
+    if constexpr (kPol == 0)
+      dst[block * 1024 + t + j * 256] = v;
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(v, buffer_at(dst + block * 1024, 16384), (t + j * 256) * 16, 0, kPol);
+  }
 }
 
 constexpr int kRowsPerWave = 4;
@@ -64,6 +73,7 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kOut = 272;                    // bytes per output row
 constexpr int kSpan = kRowsPerWave * kOut;   // 1088 bytes per wave
 
+template <int kPol>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void probe_copy_rows_kernel(
     const uint8_t* __restrict__ src, int64_t rows, const int32_t* __restrict__ order,
     uint8_t* __restrict__ dst) {
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void probe_copy_rows_kernel
     if (c < kSpan / 16) {
       const u32x4 d = *reinterpret_cast<const u32x4*>(&st[4 * c]);
       const uint32_t off = (valid >> (c / (kOut / 16))) & 1u ? (uint32_t)(16 * c) : 0x7FFFFFF0u;
-      __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, kPol);
     }
   }
 }
@@ -133,21 +143,24 @@ int probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
   return status(hipGetLastError());
 }
 
-// Writes `bytes` (a multiple of 16 KiB) to dst.
-int probe_write(void* dst, int64_t bytes, void* stream) {
+// Writes `bytes` (a multiple of 16 KiB) to dst; through != 0: NT + SC1 stores.
+int probe_write(void* dst, int64_t bytes, int through, void* stream) {
   if (!dst || bytes <= 0 || bytes % 16384 || bytes / 16384 > 0x7FFFFFFF) return -1;
-  hipLaunchKernelGGL(probe_write_kernel, dim3((unsigned)(bytes / 16384)), dim3(256), 0,
-                     (hipStream_t)stream, static_cast<u32x4*>(dst));
+  hipLaunchKernelGGL(through ? probe_write_kernel<kBufNTDevice> : probe_write_kernel<0>,
+                     dim3((unsigned)(bytes / 16384)), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<u32x4*>(dst));
   return status(hipGetLastError());
 }
 
 // rows (a multiple of 16) output rows of 272 bytes in dst, each from a
 // 1 KiB row of src: row order[s] (entries in [0, src rows) or -1: row not
 // written) or, with order NULL, row s.  src and dst 16-byte aligned.
-int probe_copy_rows(const void* src, int64_t rows, const int32_t* order, void* dst, void* stream) {
+// through != 0: NT + SC1 stores.
+int probe_copy_rows(const void* src, int64_t rows, const int32_t* order, void* dst, int through,
+                    void* stream) {
   if (!src || !dst || rows <= 0 || rows % 16 || rows / 16 > 0x7FFFFFFF) return -1;
-  hipLaunchKernelGGL(probe_copy_rows_kernel, dim3((unsigned)(rows / 16)), dim3(kWave * kWavesPerBlock),
-                     0, (hipStream_t)stream, static_cast<const uint8_t*>(src), rows, order,
+  hipLaunchKernelGGL(through ? probe_copy_rows_kernel<kBufNTDevice> : probe_copy_rows_kernel<0>,
+                     dim3((unsigned)(rows / 16)), dim3(kWave * kWavesPerBlock), 0, (hipStream_t)stream, static_cast<const uint8_t*>(src), rows, order,
                      static_cast<uint8_t*>(dst));
   return status(hipGetLastError());
 }

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_norm_cr1_kern
         h[k] = bf16_rn((as_f32(x[p][c][k]) * r) * as_f32(wb));
       }
       const u32x2 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      __builtin_amdgcn_raw_buffer_store_b64(o, dst[p], (c * 64 + lane) * 8, 0, 0);
+      // Whole output rows: streamed to memory (NT + SC1).
+      __builtin_amdgcn_raw_buffer_store_b64(o, dst[p], (c * 64 + lane) * 8, 0, kBufNTDevice);
     }
   }
 }

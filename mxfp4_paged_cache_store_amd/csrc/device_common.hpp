@@ -24,8 +24,14 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, true);
 }
 
-// Cache-policy bits of buffer instructions on gfx94x/gfx950: bit 1 = NT.
+// Cache-policy bits of buffer instructions on gfx94x/gfx950: bit 1 = NT,
+// bit 4 = SC1 (device scope).
 constexpr int kBufNT = 2;
+// NT + SC1: a store that goes through L2 to memory without staying dirty in
+// L2 or the Infinity Cache.  For streams of whole-line writes this avoids
+// the write-back of one launch's dirty lines during the next.  Scattered
+// sub-line stores need the caches to merge them and must not use it.
+constexpr int kBufNTDevice = kBufNT | 16;
 // Buffer descriptor word 3 for GFX9 raw (untyped) buffers.
 constexpr int kBufWord3 = 0x00020000;
 

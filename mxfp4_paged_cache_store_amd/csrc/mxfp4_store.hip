@@ -367,7 +367,11 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_ke
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // Rows go out in slot order, so plain stores let L2 merge neighbours.
+    // Rows go out in slot order as whole 16-byte chunks of a contiguous span,
+    // streamed through to memory (NT + SC1): measured on the 4.5M-token
+    // batch, 1136 -> 1074 us per step back to back (the previous step's
+    // dirty lines no longer drain during this one), 1121 -> 1082 us after a
+    // cache flush, and 1062 -> 958 us for prefill-style runs of slots.
     const __amdgpu_buffer_rsrc_t rs =
         buffer_at(a.cache + a.map.row<kPow2>((uint32_t)s0) * kPitch, (uint32_t)kSpan);
 #pragma unroll
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_by_slot_ke
       if (c0 + kWave <= kSpan / 16 || c < kSpan / 16) {
         const u32x4 d = *reinterpret_cast<const u32x4*>(&st[4 * c]);
         const uint32_t off = (valid >> (c / ((int)kPitch / 16))) & 1u ? (uint32_t)(16 * c) : kDrop;
-        __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, kBufNTDevice);
       }
     }
   } else {

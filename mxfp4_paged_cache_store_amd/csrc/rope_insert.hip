@@ -188,7 +188,9 @@ struct Mxfp8 {
     uint8_t* page = a.cache + page_off;
     uint8_t* values = page + (int64_t)in_page * 512;
     uint8_t* scales = page + (int64_t)a.block * 512 + (int64_t)in_page * 16;
-    *reinterpret_cast<u32x2*>(values + lane * 8) = u32x2{lo, hi};
+    // Value areas of a page are contiguous whole lines: streamed to memory
+    // (NT + SC1); the scattered 4-byte scale words go through the caches.
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, buffer_at(values, 512), lane * 8, 0, kBufNTDevice);
     if ((lane & 15) == 12) reinterpret_cast<uint32_t*>(scales)[lane >> 4] = sdw;
   }
 };
@@ -253,7 +255,7 @@ struct Nvfp4 {
     uint8_t* page = a.cache + page_off;
     uint8_t* values = page + (int64_t)in_page * 256;
     uint8_t* scales = page + (int64_t)a.block * 256 + (int64_t)in_page * 32;
-    reinterpret_cast<uint32_t*>(values)[lane] = codes;
+    __builtin_amdgcn_raw_buffer_store_b32(codes, buffer_at(values, 256), lane * 4, 0, kBufNTDevice);
     if ((lane & 7) == 6) reinterpret_cast<uint32_t*>(scales)[lane >> 3] = sdw;
   }
 };
@@ -319,7 +321,7 @@ struct V4 {
       for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(r[i] * mul, -448.0f), 448.0f);
       const uint32_t lo = e4m3x4(y[0], y[1], y[2], y[3]);
       const uint32_t hi = e4m3x4(y[4], y[5], y[6], y[7]);
-      *reinterpret_cast<u32x2*>(values + lane * 8) = u32x2{lo, hi};
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, buffer_at(values, 576), lane * 8, 0, kBufNTDevice);
     } else {
       u32x4 h;
       if (kNoNaN) {
@@ -328,7 +330,7 @@ struct V4 {
         h = u32x4{bf16_rn(r[0]) | (bf16_rn(r[1]) << 16), bf16_rn(r[2]) | (bf16_rn(r[3]) << 16),
                   bf16_rn(r[4]) | (bf16_rn(r[5]) << 16), bf16_rn(r[6]) | (bf16_rn(r[7]) << 16)};
       }
-      *reinterpret_cast<u32x4*>(values + 448 + (lane - 56) * 16) = h;
+      __builtin_amdgcn_raw_buffer_store_b128(h, buffer_at(values, 576), 448 + (lane - 56) * 16, 0, kBufNTDevice);
     }
     uint32_t s[7];
 #pragma unroll
