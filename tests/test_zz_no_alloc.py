@@ -76,3 +76,46 @@ def test_noalloc_refuses_maps_past_the_array(device):
     assert (head[: 4 * 272].reshape(4, 272)[:, 256:] == 127).all()  # zero rows: scale byte 127
     assert (head[4 * 272:] == 0xA5).all()
     del cache
+
+
+def test_noalloc_graph_replays(device):
+    """Captured in a HIP graph (the use the entry point is for: nothing to
+    allocate, no memset recorded), every replay writes the bytes of the
+    workspace form, also when an eager call with another slot mapping has
+    left its own map in the shared array just before."""
+    rng = np.random.default_rng(78)
+    ntok, nb, bs, stride = 50_000, 900, 64, 72
+    src, slots, nbytes = _case(rng, ntok, nb, bs, stride, 0.05)
+    s_dev, sl_dev = bf16_dev(src, device), i64_dev(slots, device)
+    inv = ops.mxfp4_inverse_workspace(nb, bs, device)
+    want = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=device)
+    ops.mxfp4_build_inverse(sl_dev, nb, bs, inv)
+    ops.mxfp4_store_by_slot(s_dev, ntok, inv, want, nb, bs, stride)
+    # another batch, stored eagerly between replays
+    o_src, o_slots, o_nbytes = _case(rng, 3_000, 60, 64, 64, 0.0)
+    o_src_dev, o_slots_dev = bf16_dev(o_src, device), i64_dev(o_slots, device)
+    o_cache = torch.empty((o_nbytes,), dtype=torch.uint8, device=device)
+
+    cache = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        cache.fill_(0xA5)
+        ops.mxfp4_store_slot_order_noalloc(s_dev, sl_dev, cache, nb, bs, stride)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, want), "eager call"
+
+    graph = torch.cuda.CUDAGraph()
+    log(f"capturing the noalloc store: {ntok} tokens, {nb} x {bs} slots")
+    with torch.cuda.graph(graph):
+        ops.mxfp4_store_slot_order_noalloc(s_dev, sl_dev, cache, nb, bs, stride)
+    for rep in range(3):
+        log(f"noalloc graph replay {rep}")
+        cache.fill_(0xA5)
+        ops.mxfp4_store_slot_order_noalloc(o_src_dev, o_slots_dev, o_cache, 60, 64, 64)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got, exp = cache.cpu().numpy(), want.cpu().numpy()
+        assert (got == exp).all(), (rep, first_mismatch(got, exp, 272))
