@@ -325,3 +325,27 @@ def test_attention_strided_query(device):
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
         assert (np.abs(got - want) <= tol).all()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_attention_random_geometry(device, seed):
+    """Seeded random geometries: heads (16-80), tokens, top-k (0-700, ragged
+    last tiles), block size and interleaved blocks, share of invalid slots,
+    sinks, score sharpness, and the one-pass or split-key form (1-8 ranges,
+    some of them empty)."""
+    rng = np.random.default_rng(3000 + seed)
+    heads = int(rng.choice([16, 32, 48, 64, 80]))
+    tokens = int(rng.integers(1, 7))
+    topk = int(rng.choice([0, 1, 17, 64, 100, 256, 333, 700]))
+    bs = int(rng.choice([16, 48, 64, 100]))
+    nb = int(rng.integers(2, 60))
+    bsr = bs + int(rng.choice([0, 0, 8, bs]))
+    invalid = float(rng.choice([0.0, 0.1, 0.5, 0.95]))
+    sink = bool(rng.random() < 0.5)
+    std = float(rng.choice([0.5, 2.0, 8.0]))
+    splits = int(rng.choice([1, 1, 2, 3, 8]))
+    log(f"random attention seed={seed}: T={tokens} H={heads} topk={topk} blocks={nb}x{bs} stride={bsr} "
+        f"invalid={invalid} sink={sink} std={std} splits={splits}")
+    case = workloads.attention_case(tokens, heads, topk, 4000 + seed, num_blocks=nb, block_size=bs,
+                                    block_stride_rows=bsr, invalid_frac=invalid, sink=sink, score_std=std)
+    check_case(device, case, splits=splits)

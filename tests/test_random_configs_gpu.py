@@ -29,7 +29,7 @@ def _latent_rows(rng, n, width):
     return bits
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_store_and_dequant_random_geometry(device, seed):
     rng = np.random.default_rng(1000 + seed)
     latent = int(rng.choice([128, 256, 512, 512, 1024, 2048]))
@@ -97,7 +97,7 @@ VARIANTS = {
 }
 
 
-@pytest.mark.parametrize("seed", range(18))
+@pytest.mark.parametrize("seed", range(60))
 def test_rope_inserts_random_geometry(device, seed):
     rng = np.random.default_rng(2000 + seed)
     variant = ["mxfp8", "nvfp4", "v4"][seed % 3]
