@@ -35,6 +35,23 @@ def _need_cuda(*tensors: torch.Tensor) -> None:
             raise ValueError("libmxstore works on device tensors only")
 
 
+def _unit_inner(t: torch.Tensor) -> bool:
+    """Unit stride along the last dimension.  An empty tensor's strides say
+    nothing about a layout (torch may give it zero strides), so it passes."""
+    return t.numel() == 0 or t.stride(-1) == 1
+
+
+def _strides(t: torch.Tensor) -> tuple:
+    """Element strides to hand to the C ABI; an empty tensor goes as dense."""
+    if t.numel() == 0:
+        out, acc = [], 1
+        for n in reversed(t.shape):
+            out.append(acc)
+            acc *= max(n, 1)
+        return tuple(reversed(out))
+    return t.stride()
+
+
 def _extent_bytes(t: torch.Tensor) -> int:
     """Bytes from t's data pointer to the end of its last element (what a
     kernel given only the pointer may touch without leaving the tensor)."""
@@ -73,7 +90,7 @@ def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tens
     stride; ``slot_mapping``: int64 [T] contiguous; ``cache``: uint8 storage
     of the paged view (its data pointer is the cache base)."""
     _need_cuda(src, slot_mapping, cache)
-    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or not _unit_inner(src):
         raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int64 tensor")
@@ -84,7 +101,7 @@ def mxfp4_store(src: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tens
         raise ValueError("slot_mapping has more entries than src has rows")
     _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
     _abi.check(_abi.lib().mxfp4_store(
-        src.data_ptr(), num_tokens, src.shape[1], src.stride(0), slot_mapping.data_ptr(),
+        src.data_ptr(), num_tokens, src.shape[1], _strides(src)[0], slot_mapping.data_ptr(),
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
 
 
@@ -132,7 +149,7 @@ def mxfp4_store_by_slot(src: torch.Tensor, num_tokens: int, inverse: torch.Tenso
     """``mxfp4_store_by_slot`` of the C ABI: the store in slot order, from the
     inverse map of the batch's slot mapping."""
     _need_cuda(src, inverse, cache)
-    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or not _unit_inner(src):
         raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
     if inverse.dtype != torch.int32 or not inverse.is_contiguous():
         raise ValueError("inverse must be a contiguous int32 tensor")
@@ -142,7 +159,7 @@ def mxfp4_store_by_slot(src: torch.Tensor, num_tokens: int, inverse: torch.Tenso
         raise ValueError("num_tokens exceeds the rows of src")
     _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
     _abi.check(_abi.lib().mxfp4_store_by_slot(
-        src.data_ptr(), num_tokens, src.shape[1], src.stride(0), inverse.data_ptr(),
+        src.data_ptr(), num_tokens, src.shape[1], _strides(src)[0], inverse.data_ptr(),
         inverse.numel() * 4, cache.data_ptr(), num_blocks, block_size, block_stride_rows, group,
         _stream(stream)))
 
@@ -155,7 +172,7 @@ def mxfp4_store_slot_order_noalloc(src: torch.Tensor, slot_mapping: torch.Tensor
     with its inverse map in the library's static per-GPU array (no
     allocation, no workspace; calls that overlap on one GPU race)."""
     _need_cuda(src, slot_mapping, cache)
-    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or not _unit_inner(src):
         raise ValueError("src must be a bf16 [tokens, latent] tensor with unit inner stride")
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int64 tensor")
@@ -166,7 +183,7 @@ def mxfp4_store_slot_order_noalloc(src: torch.Tensor, slot_mapping: torch.Tensor
         raise ValueError("slot_mapping has more entries than src has rows")
     _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, src.shape[1], group)
     _abi.check(_abi.lib().mxfp4_store_slot_order_noalloc(
-        src.data_ptr(), num_tokens, src.shape[1], src.stride(0), slot_mapping.data_ptr(),
+        src.data_ptr(), num_tokens, src.shape[1], _strides(src)[0], slot_mapping.data_ptr(),
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, group, _stream(stream)))
 
 
@@ -177,14 +194,14 @@ def mxfp4_gather_dequant(cache: torch.Tensor, num_blocks: int, block_size: int,
     _need_cuda(cache, slots, out)
     if slots.dtype != torch.int64 or not slots.is_contiguous():
         raise ValueError("slots must be a contiguous int64 tensor")
-    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or not _unit_inner(out):
         raise ValueError("out must be a bf16 [n, latent] tensor with unit inner stride")
     if out.shape[0] < slots.numel() or out.shape[1] != latent:
         raise ValueError("out must have at least len(slots) rows of `latent` values")
     _need_cache_extent(cache, num_blocks, block_size, block_stride_rows, latent, group)
     _abi.check(_abi.lib().mxfp4_gather_dequant(
         cache.data_ptr(), num_blocks, block_size, block_stride_rows, latent, group,
-        slots.data_ptr(), slots.numel(), out.data_ptr(), out.stride(0), _stream(stream)))
+        slots.data_ptr(), slots.numel(), out.data_ptr(), _strides(out)[0], _stream(stream)))
     return out
 
 
@@ -240,7 +257,7 @@ def save_ring_rows(rows: torch.Tensor, slot_mapping: torch.Tensor, state_cache: 
     [P2 `save_ring_rows`]: same arguments and checks as the page's wrapper;
     ``state_cache`` is the fp32 ring [blocks, capacity, width]."""
     _need_cuda(rows, slot_mapping, state_cache)
-    if rows.dtype != torch.float32 or rows.dim() != 2 or rows.stride(1) != 1:
+    if rows.dtype != torch.float32 or rows.dim() != 2 or not _unit_inner(rows):
         raise ValueError("rows must be fp32 [n, width] with unit inner stride")
     if state_cache.dtype != torch.float32 or state_cache.dim() != 3 or state_cache.stride(2) != 1 \
             or state_cache.shape[2] != rows.shape[1]:
@@ -249,7 +266,7 @@ def save_ring_rows(rows: torch.Tensor, slot_mapping: torch.Tensor, state_cache: 
             or slot_mapping.numel() != rows.shape[0]:
         raise ValueError("slot_mapping must be contiguous int64 with one entry per row")
     _abi.check(_abi.lib().save_ring_rows(
-        rows.data_ptr(), rows.shape[0], rows.shape[1], rows.stride(0), slot_mapping.data_ptr(),
+        rows.data_ptr(), rows.shape[0], rows.shape[1], _strides(rows)[0], slot_mapping.data_ptr(),
         state_cache.data_ptr(), state_cache.shape[0], state_cache.shape[1], state_cache.stride(0),
         state_cache.stride(1), _stream(stream)))
 
@@ -261,13 +278,13 @@ def fused_save_compress_norm_cr1(kv_score: torch.Tensor, slot_mapping: torch.Ten
     valid token's fp32 [512] row with the bf16 weight, into bf16
     ``latent_out`` (rows of tokens with slot < 0 are not written)."""
     _need_cuda(kv_score, slot_mapping, rms_norm_weight, latent_out)
-    if kv_score.dtype != torch.float32 or kv_score.dim() != 2 or kv_score.stride(1) != 1 \
+    if kv_score.dtype != torch.float32 or kv_score.dim() != 2 or not _unit_inner(kv_score) \
             or kv_score.shape[1] != 512:
         raise ValueError("kv_score must be fp32 [tokens, 512] with unit inner stride")
     if rms_norm_weight.dtype != torch.bfloat16 or rms_norm_weight.numel() != 512 \
             or not rms_norm_weight.is_contiguous():
         raise ValueError("rms_norm_weight must be contiguous bf16 [512]")
-    if latent_out.dtype != torch.bfloat16 or latent_out.dim() != 2 or latent_out.stride(1) != 1 \
+    if latent_out.dtype != torch.bfloat16 or latent_out.dim() != 2 or not _unit_inner(latent_out) \
             or latent_out.shape[1] != 512:
         raise ValueError("latent_out must be bf16 [tokens, 512] with unit inner stride")
     n = slot_mapping.numel()
@@ -275,8 +292,8 @@ def fused_save_compress_norm_cr1(kv_score: torch.Tensor, slot_mapping: torch.Ten
             or n > kv_score.shape[0] or n > latent_out.shape[0]:
         raise ValueError("slot_mapping must be contiguous int64 with at most one entry per row")
     _abi.check(_abi.lib().fused_save_compress_norm_cr1(
-        kv_score.data_ptr(), n, 512, kv_score.stride(0), slot_mapping.data_ptr(),
-        rms_norm_weight.data_ptr(), float(rms_norm_eps), latent_out.data_ptr(), latent_out.stride(0),
+        kv_score.data_ptr(), n, 512, _strides(kv_score)[0], slot_mapping.data_ptr(),
+        rms_norm_weight.data_ptr(), float(rms_norm_eps), latent_out.data_ptr(), _strides(latent_out)[0],
         _stream(stream)))
 
 
@@ -305,10 +322,10 @@ def sparse_mla_attention(q: torch.Tensor, cache: torch.Tensor, indices: torch.Te
     advice.  The split form needs a device ``workspace`` (uint8, at least
     ``sparse_mla_attention_workspace_bytes``); one is allocated when None."""
     _need_cuda(q, cache, indices)
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 512 or q.stride(2) != 1:
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 512 or not _unit_inner(q):
         raise ValueError("q must be bf16 [tokens, heads, 512] with unit inner stride")
     if indices.dtype != torch.int32 or indices.dim() != 2 or indices.shape[0] != q.shape[0] \
-            or (indices.shape[1] > 1 and indices.stride(1) != 1):
+            or (indices.shape[1] > 1 and not _unit_inner(indices)):
         raise ValueError("indices must be int32 [tokens, topk] with unit inner stride")
     num_blocks, block_size, stride_rows = resolve_paged_view(cache, 512)
     if sink is not None and (sink.dtype != torch.float32 or sink.numel() != q.shape[1]
@@ -316,15 +333,16 @@ def sparse_mla_attention(q: torch.Tensor, cache: torch.Tensor, indices: torch.Te
         raise ValueError("sink must be contiguous fp32 [heads]")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    if out.dtype != torch.bfloat16 or out.shape != q.shape or out.stride(2) != 1:
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not _unit_inner(out):
         raise ValueError("out must be bf16 shaped like q with unit inner stride")
     tokens, heads, topk = q.shape[0], q.shape[1], indices.shape[1]
     if splits is None:
         splits = sparse_mla_attention_splits_advised(tokens, heads, topk)
-    args = (q.data_ptr(), tokens, heads, 512, q.stride(0), q.stride(1), cache.data_ptr(),
+    qs, os_ = _strides(q), _strides(out)
+    args = (q.data_ptr(), tokens, heads, 512, qs[0], qs[1], cache.data_ptr(),
             num_blocks, block_size, stride_rows, indices.data_ptr(), topk,
-            max(indices.stride(0), topk), float(scale), None if sink is None else sink.data_ptr(),
-            out.data_ptr(), out.stride(0), out.stride(1))
+            max(_strides(indices)[0], topk), float(scale), None if sink is None else sink.data_ptr(),
+            out.data_ptr(), os_[0], os_[1])
     if splits == 1:
         _abi.check(_abi.lib().sparse_mla_attention(*args, _stream(stream)))
         return out

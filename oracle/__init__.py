@@ -291,10 +291,13 @@ class Oracle:
                        state: np.ndarray) -> None:
         """Copy fp32 ``rows`` [n, width] (row-strided allowed) into the ring
         ``state`` [blocks, capacity, width] (strided views allowed) in place."""
-        assert rows.dtype == np.float32 and rows.ndim == 2 and rows.strides[1] == 4
+        assert rows.dtype == np.float32 and rows.ndim == 2
         assert state.dtype == np.float32 and state.ndim == 3 and state.strides[2] == 4
         assert slot_mapping.dtype == np.int64 and slot_mapping.flags.c_contiguous
         assert slot_mapping.size == rows.shape[0] and state.shape[2] == rows.shape[1]
+        if rows.shape[0] == 0:  # nothing to copy (an empty array's strides mean nothing)
+            return
+        assert rows.strides[1] == 4
         rc = self.lib.orc_save_ring_rows(
             rows.ctypes.data, rows.shape[0], rows.shape[1], rows.strides[0] // 4,
             _ptr(slot_mapping), state.ctypes.data, state.shape[0], state.shape[1],
