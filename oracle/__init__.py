@@ -160,10 +160,13 @@ class Oracle:
         place.  ``threads > 1`` splits the tokens into contiguous ranges run
         concurrently (distinct slots never share bytes).
         """
-        assert src.dtype == np.uint16 and src.ndim == 2 and src.strides[1] == 2
+        assert src.dtype == np.uint16 and src.ndim == 2
         assert slot_mapping.dtype == np.int64 and cache.dtype == np.uint8
         assert cache.flags.c_contiguous and slot_mapping.flags.c_contiguous
         num_tokens = slot_mapping.size
+        if num_tokens == 0:  # nothing stored (an empty array's strides mean nothing)
+            return
+        assert src.strides[1] == 2
         latent = src.shape[1]
         src_row_stride = src.strides[0] // 2
         need = ((num_blocks - 1) * block_stride_rows + block_size) * self.row_bytes(latent)
@@ -311,7 +314,7 @@ class Oracle:
         allowed) with a bf16-bits weight, in double; rows of invalid tokens of
         ``out`` (float64 [n, width]) are left as they are (NaN if allocated
         here)."""
-        assert kv.dtype == np.float32 and kv.ndim == 2 and kv.strides[1] == 4
+        assert kv.dtype == np.float32 and kv.ndim == 2
         assert slot_mapping.dtype == np.int64 and slot_mapping.flags.c_contiguous
         w = np.ascontiguousarray(weight_bf16, dtype=np.uint16)
         n, width = slot_mapping.size, kv.shape[1]
@@ -319,6 +322,9 @@ class Oracle:
         if out is None:
             out = np.full((n, width), np.nan, dtype=np.float64)
         assert out.dtype == np.float64 and out.flags.c_contiguous
+        if n == 0:  # no rows (an empty array's strides mean nothing)
+            return out
+        assert kv.strides[1] == 4
         rc = self.lib.orc_rmsnorm_cr1(kv.ctypes.data, n, width, kv.strides[0] // 4,
                                       _ptr(slot_mapping), _ptr(w), eps, _ptr(out), out.shape[1])
         _check(rc, "rmsnorm_cr1")

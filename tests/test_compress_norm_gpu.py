@@ -141,3 +141,28 @@ def test_compress_norm_large_sampled(device):
     valid = slots_s >= 0
     check_bf16_rounding(got[valid], want[valid])
     assert (got[~valid] == CANARY).all()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_compress_norm_random_geometry(device, seed):
+    """Seeded random batches: token counts (0-20,000, ragged), row padding of
+    the fp32 input and the bf16 output, epsilon, the share of invalid tokens
+    (negative slots), row magnitudes over 2^+-50, and rows that are all
+    zeros.  (Rows whose fp32 sum of squares overflows, from magnitudes of
+    about 2^59 up, are outside the fp32 arithmetic this kernel shares with the
+    pages' and outside the derived tolerance.)"""
+    rng = np.random.default_rng(6000 + seed)
+    n = int(rng.choice([0, 1, 7, 8, 9, 513, 4096, 20_000]))
+    kv_pad, out_pad = int(rng.choice([0, 4, 12])), int(rng.choice([0, 8]))
+    eps = float(rng.choice([0.0, 1e-6, 1e-5, 1e-2]))
+    backing = (rng.standard_normal((n, 512 + kv_pad)) *
+               np.exp2(rng.uniform(-50, 50, (n, 1)))).astype(np.float32)
+    if n:
+        backing[rng.random(n) < 0.05] = 0.0
+    slots = np.arange(n, dtype=np.int64)
+    slots[rng.random(n) < float(rng.choice([0.0, 0.1, 0.9]))] = -1
+    w = weight_bits(rng)
+    log(f"random norm seed={seed}: n={n} kv_pad={kv_pad} out_pad={out_pad} eps={eps}")
+    got = run_case(device, backing, slots, w, eps, out_pad)
+    near = check(got, backing[:, :512], slots, w, eps, out_pad)
+    assert near <= max(16, got.size // 100)
