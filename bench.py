@@ -42,6 +42,8 @@ BYTES_PER_PAD = 8
 BY_SLOT_BYTES_PER_TOKEN = 1024 + 272
 BY_SLOT_BYTES_PER_SLOT = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mxfp4_store_large_traffic.txt")
+# tokens of the compress-ratio-1 norm's benchmark batch (2M fp32 rows of 512)
+NORM_TOKENS = 1 << 21
 # the store kernel's source and the headers it includes
 STORE_SRCS = tuple(os.path.join(ROOT, "mxfp4_paged_cache_store_amd", "csrc", f)
                    for f in ("mxfp4_store.hip", "device_common.hpp", "kernels.hpp"))
@@ -301,7 +303,7 @@ def companions(torch, ops, workloads, steps, warmup, cache, n_tokens, only=(), c
         del rows, ring, ring_slots
     if want("fused_save_compress_norm_cr1"):
         # compress-ratio-1 RMSNorm: 2,097,152 fp32 [512] rows -> bf16, all valid
-        n_norm = 1 << 21
+        n_norm = NORM_TOKENS
         kv = torch.empty((n_norm, 512), dtype=torch.float32, device="cuda").normal_()
         norm_slots = torch.arange(n_norm, dtype=torch.int64, device="cuda")
         w = torch.empty(512, dtype=torch.float32, device="cuda").normal_(0.8, 0.5).to(torch.bfloat16)
@@ -473,8 +475,10 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     (1 KiB read + 272-byte row written per token) in sequential and in
     slot order (gathered through the inverse map), and the store's slot-order
     kernel and whole step; a copy of 262,144 rows of 4 KiB in order and to a
-    permutation of the rows, beside save_ring_rows on the same shapes; then
-    the small-batch floors (an empty launch of
+    permutation of the rows, beside save_ring_rows on the same shapes; the
+    gather-dequant's traffic (272-byte rows to 1 KiB rows, in order) and the
+    CR1 norm's (2 KiB rows to 1 KiB rows) as plain copies beside those
+    kernels; then the small-batch floors (an empty launch of
     the store's grid, a plain read of the batch's latent) at 16,384 and
     65,536 tokens.  One JSON line per probe: median of PROBE_REPS HIP-event
     times of single launches, each after a 1 GiB read that flushes the
@@ -493,7 +497,9 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     lib.probe_copy_rows.argtypes = [vp, i64, vp, vp, ctypes.c_int, vp]
     lib.probe_empty.argtypes = [i64, vp]
     lib.probe_copy_wide.argtypes = [vp, i64, i64, vp, vp, vp]
-    for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty, lib.probe_copy_wide):
+    lib.probe_copy_expand.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty, lib.probe_copy_wide,
+              lib.probe_copy_expand):
         f.restype = ctypes.c_int
 
     def ok(rc):
@@ -552,6 +558,30 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
                                         ring_dst.data_ptr(), st()))),
         ("save_ring_rows", n_ring * 8200, lambda: ops.save_ring_rows(ring_rows, ring_slots, ring)),
     ]
+    # the gather-dequant's traffic (272-byte rows in order -> 1 KiB bf16 rows,
+    # non-temporal stores) and the CR1 norm's (2 KiB fp32 rows -> 1 KiB bf16
+    # rows, written through), each next to its kernel on the same shapes
+    dq_out = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda")
+    dq_slots = torch.arange(n, dtype=torch.int64, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    kv = torch.randn((NORM_TOKENS, 512), generator=gen, dtype=torch.float32, device="cuda")
+    kv_out = torch.empty((NORM_TOKENS, 512), dtype=torch.bfloat16, device="cuda")
+    kv_slots = torch.arange(NORM_TOKENS, dtype=torch.int64, device="cuda")
+    weight = torch.ones(512, dtype=torch.bfloat16, device="cuda")
+    # (the copies with 1, 2, 4 and 8 rows per wave: the fastest is the ceiling)
+    for rpw in (1, 2, 4, 8):
+        cases.append((f"copy_272_to_1024_nt_{rpw}_rows_per_wave", n * 1296,
+                      lambda r=rpw: ok(lib.probe_copy_expand(cache.data_ptr(), n, 272, 1024, 2, r,
+                                                             dq_out.data_ptr(), st()))))
+    cases.append(("gather_dequant_in_order", n * 1304,
+                  lambda: ops.mxfp4_gather_dequant(cache, 1, n, n, 512, dq_slots, dq_out)))
+    for rpw in (1, 2, 4, 8):
+        cases.append((f"copy_2048_to_1024_through_{rpw}_rows_per_wave", NORM_TOKENS * 3072,
+                      lambda r=rpw: ok(lib.probe_copy_expand(kv.data_ptr(), NORM_TOKENS, 2048, 1024, 18, r,
+                                                             kv_out.data_ptr(), st()))))
+    cases.append(("compress_norm_cr1", NORM_TOKENS * 3080,
+                  lambda: ops.fused_save_compress_norm_cr1(kv, kv_slots, weight, 1e-6, kv_out)))
     for tokens in (16384, 65536):
         tpw = 2 if tokens <= 16384 else 4
         grid = tokens // (4 * tpw)  # the scatter store's workgroups at this size
@@ -586,6 +616,7 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
             line["frac_hbm_peak"] = round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)
         print(json.dumps(line), flush=True)
     del src, slots, cache, inv, flush, ring_rows, ring_slots, ring, ring_dst, ring_perm
+    del dq_out, dq_slots, kv, kv_out, kv_slots
 
 
 SWEEP_TOKENS = (16384, 65536, 262144, 1048576, 4500000)

@@ -15,6 +15,10 @@
 //   probe_copy_wide  per row: copy a row of `width` bytes (a multiple of 1 KiB)
 //                    to output row order[t] (or t), one wave per row -- the
 //                    ring-state save's traffic.
+//   probe_copy_expand  rows in order: read `in_bytes`, write `out_bytes` derived
+//                    from them, one wave per row, 16 B per lane -- the traffic of
+//                    the gather-dequant (272 -> 1024, non-temporal stores) and of
+//                    the compress-ratio-1 norm (2048 -> 1024, written through).
 //   probe_empty      an empty kernel: the launch floor of a given grid.
 // The written bytes depend on the loaded ones so no load can be dropped; a
 // read-only probe writes one dword only when its checksum hits a constant.
@@ -127,9 +131,51 @@ __global__ __launch_bounds__(256) void probe_copy_wide_kernel(const u32x4* __res
   for (int64_t j = lane; j < width16; j += 64) dst[d * width16 + j] = src[t * width16 + j];
 }
 
+// A wave moves kRows consecutive rows (one span of kRows * kIn bytes in, one
+// of kRows * kOut bytes out), four waves per block.  Lanes load 16-byte
+// chunks of the input span (lanes past its chunks reload one, which the
+// caches serve) and write 16-byte chunks of the output span that depend on
+// them.  A last, partial span is cut by the buffer ranges.
+template <int kIn, int kOut, int kPol, int kRows>
+__global__ __launch_bounds__(256) void probe_copy_expand_kernel(const uint8_t* __restrict__ src, int64_t rows,
+                                                                uint8_t* __restrict__ dst) {
+  static_assert(kIn % 16 == 0 && (kRows * kOut) % 1024 == 0, "16-byte chunks, 1 KiB output steps");
+  constexpr int kInChunks = kRows * kIn / 16;
+  const int64_t r0 = ((int64_t)xcd_contiguous_block() * 4 + (threadIdx.x >> 6)) * kRows;
+  if (r0 >= rows) return;
+  const int64_t nr = rows - r0 < kRows ? rows - r0 : kRows;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t in = buffer_at(src + r0 * kIn, (uint32_t)(nr * kIn));
+  u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < (kInChunks + 63) / 64; ++i) {
+    const int c = (i * 64 + lane) % kInChunks;
+    v ^= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in, c * 16, 0, 0));
+  }
+  const __amdgpu_buffer_rsrc_t out = buffer_at(dst + r0 * kOut, (uint32_t)(nr * kOut));
+#pragma unroll
+  for (int j = 0; j < kRows * kOut / 1024; ++j)
+    __builtin_amdgcn_raw_buffer_store_b128(v ^ u32x4{(uint32_t)j, 0u, 0u, 0u}, out, (j * 64 + lane) * 16, 0, kPol);
+}
+
 __global__ __launch_bounds__(256) void probe_empty_kernel() {}
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -7; }
+
+template <int kIn, int kOut, int kPol>
+int launch_expand(const uint8_t* s, int64_t rows, int rows_per_wave, uint8_t* d, hipStream_t stream) {
+  const int64_t per_block = 4 * (int64_t)rows_per_wave;
+  if ((rows + per_block - 1) / per_block > 0x7FFFFFFF) return -1;
+  const dim3 grid((unsigned)((rows + per_block - 1) / per_block)), block(256);
+  switch (rows_per_wave) {
+    case 1: hipLaunchKernelGGL((probe_copy_expand_kernel<kIn, kOut, kPol, 1>), grid, block, 0, stream, s, rows, d); break;
+    case 2: hipLaunchKernelGGL((probe_copy_expand_kernel<kIn, kOut, kPol, 2>), grid, block, 0, stream, s, rows, d); break;
+    case 4: hipLaunchKernelGGL((probe_copy_expand_kernel<kIn, kOut, kPol, 4>), grid, block, 0, stream, s, rows, d); break;
+    case 8: hipLaunchKernelGGL((probe_copy_expand_kernel<kIn, kOut, kPol, 8>), grid, block, 0, stream, s, rows, d); break;
+    default: return -1;
+  }
+  return status(hipGetLastError());
+}
 
 }  // namespace
 
@@ -175,6 +221,22 @@ int probe_copy_wide(const void* src, int64_t rows, int64_t width, const int64_t*
                      (hipStream_t)stream, static_cast<const u32x4*>(src), rows, width / 16, order,
                      static_cast<u32x4*>(dst));
   return status(hipGetLastError());
+}
+
+// rows rows of in_bytes in src, in order, to rows of out_bytes in dst, with
+// rows_per_wave in {1, 2, 4, 8}: (in_bytes, out_bytes, policy) = (272, 1024,
+// 2) (non-temporal stores) or (2048, 1024, 18) (stores written through);
+// anything else is refused.
+int probe_copy_expand(const void* src, int64_t rows, int in_bytes, int out_bytes, int policy, int rows_per_wave,
+                      void* dst, void* stream) {
+  if (!src || !dst || rows <= 0) return -1;
+  const auto s = static_cast<const uint8_t*>(src);
+  const auto d = static_cast<uint8_t*>(dst);
+  if (in_bytes == 272 && out_bytes == 1024 && policy == kBufNT)
+    return launch_expand<272, 1024, kBufNT>(s, rows, rows_per_wave, d, (hipStream_t)stream);
+  if (in_bytes == 2048 && out_bytes == 1024 && policy == kBufNTDevice)
+    return launch_expand<2048, 1024, kBufNTDevice>(s, rows, rows_per_wave, d, (hipStream_t)stream);
+  return -1;
 }
 
 // An empty kernel over `blocks` workgroups of 256 threads.

@@ -60,5 +60,6 @@ def test_probe_library_exports():
     if not os.path.exists(build.PROBE_LIB_PATH):
         build.build_probes()
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
-    for name in ("probe_read", "probe_write", "probe_copy_rows", "probe_copy_wide", "probe_empty"):
+    for name in ("probe_read", "probe_write", "probe_copy_rows", "probe_copy_wide", "probe_copy_expand",
+                 "probe_empty"):
         assert hasattr(lib, name), name
