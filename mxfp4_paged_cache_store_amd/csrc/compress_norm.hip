@@ -16,7 +16,8 @@
 // the wave), so loads and the 8-byte bf16 stores are fully coalesced.  The
 // sum of squares is reduced with DPP within rows of 16 lanes, then across
 // rows with two lane shuffles; every step adds a value to its exact mirror,
-// so all 64 lanes end with the same bits.  HBM-bound: 2048 B in, 1024 B out.
+// so all 64 lanes end with the same bits.  HBM-bound: 2048 B in, 1024 B out;
+// the output rows are written through to memory (NT + SC1).
 #include "kernels.hpp"
 
 namespace mxs {

@@ -42,6 +42,12 @@
 //     range check returns zeros or drops the access without touching
 //     memory).  Latents below 512 put several tokens in a pass and skip a
 //     pad token's load too.  All addressing is 64-bit.
+//   * The slot-order form, for dense scattered batches larger than the
+//     Infinity Cache, turns the scatter into a gather: an inverse map
+//     (slot -> token, built by a fill and one scattered int32 write per
+//     token) lets each wave walk 4 consecutive slots, load their tokens' rows,
+//     quantize them, assemble the 4 rows in LDS and write them as 16-byte
+//     chunks of one contiguous span, written through to memory (NT + SC1).
 #include <mutex>
 
 #include "kernels.hpp"

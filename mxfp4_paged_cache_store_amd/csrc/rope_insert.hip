@@ -33,7 +33,10 @@
 // lanes and an NVFP4 tile a lane pair.  E4M3 and E2M1 conversions use
 // gfx950's v_cvt_scalef32_pk_fp8_f32 / v_cvt_scalef32_pk_fp4_f32 with scale
 // 1.0; the NVFP4 quotient r / S is a product with an fp64 reciprocal that
-// leads to the same E2M1 code as the correctly rounded fp32 quotient.
+// leads to the same E2M1 code as the correctly rounded fp32 quotient.  A
+// token's value bytes are written through to memory (NT + SC1 buffer
+// stores: a page's value area is whole contiguous lines); its scale words go
+// through the caches, which merge them.
 #include "kernels.hpp"
 
 namespace mxs {
