@@ -40,6 +40,16 @@ def test_graph_replays_match_eager(device):
     a_out = torch.empty_like(a_q)
     a_out1 = torch.empty_like(a_q)
     a_ws = torch.empty(ops.sparse_mla_attention_workspace_bytes(8, 32, 4), dtype=torch.uint8, device=device)
+    # the V4 insert, the ring-state save and the compress-ratio-1 norm
+    v4_kv = torch.empty((16, 64, 584), dtype=torch.uint8, device=device)
+    ring_rows = torch.empty((3000, 1024), dtype=torch.float32, device=device)
+    ring_slots = torch.randperm(200 * 32, device=device)[:3000].contiguous()
+    ring = torch.empty((200, 32, 1024), dtype=torch.float32, device=device)
+    n_kv = torch.empty((5000, 512), dtype=torch.float32, device=device)
+    n_slots = torch.arange(5000, device=device)
+    n_slots[::7] = -1
+    n_w = torch.empty(512, dtype=torch.bfloat16, device=device)
+    n_out = torch.empty((5000, 512), dtype=torch.bfloat16, device=device)
 
     def work():
         ops.mxfp4_build_inverse(g_slots, 1, n, inv)
@@ -50,6 +60,9 @@ def test_graph_replays_match_eager(device):
         ops.nvfp4_rope_store(r1_lat, r1_pos, r_cs, r1_kv, r1_slots, 1)
         ops.sparse_mla_attention(a_q, p_cache, a_idx, 0.04, out=a_out, splits=4, workspace=a_ws)
         ops.sparse_mla_attention(a_q, p_cache, a_idx, 0.04, out=a_out1, splits=1)
+        ops.v4_rope_store(r_lat, r_pos, r_cs, v4_kv, r_slots, rc.compress_ratio)
+        ops.save_ring_rows(ring_rows, ring_slots, ring)
+        ops.fused_save_compress_norm_cr1(n_kv, n_slots, n_w, 1e-6, n_out)
 
     def reset(seed):
         gen = torch.Generator(device=device)
@@ -65,6 +78,12 @@ def test_graph_replays_match_eager(device):
         a_q.normal_(generator=gen)
         a_out.fill_(0)
         a_out1.fill_(0)
+        v4_kv.fill_(0xA5)
+        ring_rows.uniform_(-2, 2, generator=gen)
+        ring.fill_(1.5)
+        n_kv.normal_(generator=gen)
+        n_w.uniform_(0.5, 1.5, generator=gen)
+        n_out.fill_(0)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -85,12 +104,12 @@ def test_graph_replays_match_eager(device):
         graph.replay()
         torch.cuda.synchronize()
         got = [g_cache.clone(), p_cache.clone(), dq_out.clone(), r_kv.clone(), r1_kv.clone(), a_out.clone(),
-               a_out1.clone()]
+               a_out1.clone(), v4_kv.clone(), ring.clone(), n_out.clone()]
         reset(100 + rep)
         work()  # eager
         torch.cuda.synchronize()
-        want = [g_cache, p_cache, dq_out, r_kv, r1_kv, a_out, a_out1]
+        want = [g_cache, p_cache, dq_out, r_kv, r1_kv, a_out, a_out1, v4_kv, ring, n_out]
         names = ("slot-order store", "scatter store", "dequant", "mxfp8 insert", "nvfp4 insert, ratio 1",
-                 "attention split", "attention one pass")
+                 "attention split", "attention one pass", "v4 insert", "ring save", "cr1 norm")
         for name, a, b in zip(names, got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rep, name)
