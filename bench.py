@@ -474,7 +474,8 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     permutation): read-only, write-only, the store's traffic as a plain copy
     (1 KiB read + 272-byte row written per token) in sequential and in
     slot order (gathered through the inverse map), and the store's slot-order
-    kernel and whole step; a copy of 262,144 rows of 4 KiB in order and to a
+    kernel and whole step; the inverse map's traffic (a sequential write of
+    its size, scattered 4-byte writes) beside its build; a copy of 262,144 rows of 4 KiB in order and to a
     permutation of the rows, beside save_ring_rows on the same shapes; the
     gather-dequant's traffic (272-byte rows to 1 KiB rows, in order) and the
     CR1 norm's (2 KiB rows to 1 KiB rows) as plain copies beside those
@@ -498,8 +499,9 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     lib.probe_empty.argtypes = [i64, vp]
     lib.probe_copy_wide.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.probe_copy_expand.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.probe_scatter_dwords.argtypes = [vp, i64, ctypes.c_int, vp, vp]
     for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty, lib.probe_copy_wide,
-              lib.probe_copy_expand):
+              lib.probe_copy_expand, lib.probe_scatter_dwords):
         f.restype = ctypes.c_int
 
     def ok(rc):
@@ -543,6 +545,18 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
         ("store_by_slot_kernel", n * 1300, store_kernel),
         ("store_slot_order_step", n * BYTES_PER_TOKEN, store_step),
     ]
+    # the inverse map's traffic: a sequential write of its size (the fill) and
+    # n scattered 4-byte writes to the positions the permutation names (an
+    # 8-byte index read + 4 bytes written each), 1-8 per thread, next to the
+    # library's build of the same map (fill + inversion)
+    scat = torch.empty(n, dtype=torch.int32, device="cuda")
+    map_bytes = (n * 4) // 16384 * 16384
+    cases.append(("write_map_sequential", map_bytes,
+                  lambda: ok(lib.probe_write(scat.data_ptr(), map_bytes, 0, st()))))
+    for per in (1, 2, 4, 8):
+        cases.append((f"scatter_dwords_{per}_per_thread", n * 12,
+                      lambda p=per: ok(lib.probe_scatter_dwords(slots.data_ptr(), n, p, scat.data_ptr(), st()))))
+    cases.append(("inverse_map_build", n * 16, lambda: ops.mxfp4_build_inverse(slots, 1, n, inv)))
     # the ring-state save's traffic: 262,144 rows of 4 KiB, in order or to a
     # permutation of the rows, next to save_ring_rows on the same shapes
     ring_rows, ring_slots, ring_shape = workloads.ring_large_device()
@@ -616,7 +630,7 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
             line["frac_hbm_peak"] = round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)
         print(json.dumps(line), flush=True)
     del src, slots, cache, inv, flush, ring_rows, ring_slots, ring, ring_dst, ring_perm
-    del dq_out, dq_slots, kv, kv_out, kv_slots
+    del dq_out, dq_slots, kv, kv_out, kv_slots, scat
 
 
 SWEEP_TOKENS = (16384, 65536, 262144, 1048576, 4500000)

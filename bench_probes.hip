@@ -19,6 +19,9 @@
 //                    from them, one wave per row, 16 B per lane -- the traffic of
 //                    the gather-dequant (272 -> 1024, non-temporal stores) and of
 //                    the compress-ratio-1 norm (2048 -> 1024, written through).
+//   probe_scatter_dwords  dst[idx[t]] = t for t < n (idx int64, in range):
+//                    scattered 4-byte writes, 1-8 per thread -- the inverse
+//                    map's traffic.
 //   probe_empty      an empty kernel: the launch floor of a given grid.
 // The written bytes depend on the loaded ones so no load can be dropped; a
 // read-only probe writes one dword only when its checksum hits a constant.
@@ -158,6 +161,20 @@ __global__ __launch_bounds__(256) void probe_copy_expand_kernel(const uint8_t* _
     __builtin_amdgcn_raw_buffer_store_b128(v ^ u32x4{(uint32_t)j, 0u, 0u, 0u}, out, (j * 64 + lane) * 16, 0, kPol);
 }
 
+// Each thread writes kPer entries: its indices are loaded first, then the
+// scattered dwords are stored.
+template <int kPer>
+__global__ __launch_bounds__(256) void probe_scatter_dwords_kernel(const int64_t* __restrict__ idx, int64_t n,
+                                                                   int32_t* __restrict__ dst) {
+  const int64_t t0 = ((int64_t)blockIdx.x * 256) * kPer + threadIdx.x;
+  int64_t s[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) s[j] = t0 + j * 256 < n ? idx[t0 + j * 256] : -1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (s[j] >= 0) dst[s[j]] = (int32_t)(t0 + j * 256);
+}
+
 __global__ __launch_bounds__(256) void probe_empty_kernel() {}
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -7; }
@@ -237,6 +254,25 @@ int probe_copy_expand(const void* src, int64_t rows, int in_bytes, int out_bytes
   if (in_bytes == 2048 && out_bytes == 1024 && policy == kBufNTDevice)
     return launch_expand<2048, 1024, kBufNTDevice>(s, rows, rows_per_wave, d, (hipStream_t)stream);
   return -1;
+}
+
+// dst[idx[t]] = t for t < n, per_thread in {1, 2, 4, 8}.  Every idx[t] must
+// lie in [0, dst_len) or be negative (skipped); checked by the caller, as the
+// kernel writes where the entries say.
+int probe_scatter_dwords(const int64_t* idx, int64_t n, int per_thread, int32_t* dst, void* stream) {
+  if (!idx || !dst || n <= 0) return -1;
+  const int64_t per_block = 256 * (int64_t)per_thread;
+  const int64_t blocks = (n + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return -1;
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (per_thread) {
+    case 1: hipLaunchKernelGGL(probe_scatter_dwords_kernel<1>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
+    case 2: hipLaunchKernelGGL(probe_scatter_dwords_kernel<2>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
+    case 4: hipLaunchKernelGGL(probe_scatter_dwords_kernel<4>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
+    case 8: hipLaunchKernelGGL(probe_scatter_dwords_kernel<8>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
+    default: return -1;
+  }
+  return status(hipGetLastError());
 }
 
 // An empty kernel over `blocks` workgroups of 256 threads.
