@@ -481,9 +481,12 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     CR1 norm's (2 KiB rows to 1 KiB rows) as plain copies beside those
     kernels; then the small-batch floors (an empty launch of
     the store's grid, a plain read of the batch's latent) at 16,384 and
-    65,536 tokens.  One JSON line per probe: median of PROBE_REPS HIP-event
-    times of single launches, each after a 1 GiB read that flushes the
-    Infinity Cache.  With `counters`, three launches of each, untimed."""
+    65,536 tokens; last, the LDS and matrix-core rates of a CU (contiguous
+    LDS reads, transposing reads and writes; bf16 MFMAs alone).  One JSON
+    line per probe: median of PROBE_REPS HIP-event times of single launches,
+    each after a 1 GiB read that flushes the Infinity Cache (the LDS and MFMA
+    probes: median of 5, no flush).  With `counters`, three launches of each
+    HBM probe, untimed."""
     import ctypes
     import statistics
 
@@ -500,8 +503,9 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     lib.probe_copy_wide.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.probe_copy_expand.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     lib.probe_scatter_dwords.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+    lib.probe_lds.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp]
     for f in (lib.probe_read, lib.probe_write, lib.probe_copy_rows, lib.probe_empty, lib.probe_copy_wide,
-              lib.probe_copy_expand, lib.probe_scatter_dwords):
+              lib.probe_copy_expand, lib.probe_scatter_dwords, lib.probe_lds):
         f.restype = ctypes.c_int
 
     def ok(rc):
@@ -631,7 +635,41 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
         print(json.dumps(line), flush=True)
     del src, slots, cache, inv, flush, ring_rows, ring_slots, ring, ring_dst, ring_perm
     del dq_out, dq_slots, kv, kv_out, kv_slots, scat
+    # LDS and matrix-core rates of a CU (no HBM traffic): 1,024 workgroups of
+    # 1,024 threads (one per CU at a time), LDS_ITERS x 8 accesses per wave
+    # (or x 16 MFMAs); median of 5 launches
+    lds_out = torch.empty(1024 * 1024, dtype=torch.int32, device="cuda")
+    waves = 1024 * 16
+    for kind, name, per_instr in ((0, "lds_read_b128", 1024), (1, "lds_read_b64_tr_b16", 512),
+                                  (2, "lds_write_b128", 1024), (3, "lds_write_b64", 512),
+                                  (4, "mfma_bf16_16x16x32", 0)):
+        fn = lambda k=kind: ok(lib.probe_lds(k, 1024, LDS_ITERS, lds_out.data_ptr(), st()))  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        if counters:
+            continue
+        times = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1000.0)
+        t = statistics.median(times)
+        line = {"probe": name, "reps": 5, "us": round(t * 1e6, 2)}
+        if per_instr:
+            line["lds_GBps_per_CU"] = round(waves * LDS_ITERS * 8 * per_instr / t / 1e9 / 256, 1)
+        else:
+            flops = waves * LDS_ITERS * 16 * (16 * 16 * 32 * 2)
+            line["TFLOPs"] = round(flops / t / 1e12, 1)
+            line["frac_bf16_mfma_peak"] = round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)
+        print(json.dumps(line), flush=True)
+    del lds_out
 
+
+LDS_ITERS = 1024
 
 SWEEP_TOKENS = (16384, 65536, 262144, 1048576, 4500000)
 SWEEP_REPS = 20

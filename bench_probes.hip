@@ -22,6 +22,11 @@
 //   probe_scatter_dwords  dst[idx[t]] = t for t < n (idx int64, in range):
 //                    scattered 4-byte writes, 1-8 per thread -- the inverse
 //                    map's traffic.
+//   probe_lds        LDS and matrix-core rates of one CU (1024-thread
+//                    workgroups holding 96 KB of LDS, one per CU): contiguous
+//                    ds_read_b128, ds_read_b64_tr_b16, ds_write_b128,
+//                    ds_write_b64, or 16x16x32 bf16 MFMAs alone -- the
+//                    budget a kernel that stages operands in LDS works with.
 //   probe_empty      an empty kernel: the launch floor of a given grid.
 // The written bytes depend on the loaded ones so no load can be dropped; a
 // read-only probe writes one dword only when its checksum hits a constant.
@@ -175,6 +180,60 @@ __global__ __launch_bounds__(256) void probe_scatter_dwords_kernel(const int64_t
     if (s[j] >= 0) dst[s[j]] = (int32_t)(t0 + j * 256);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// kind 0: ds_read_b128, 1: ds_read_b64_tr_b16, 2: ds_write_b128,
+// 3: ds_write_b64 (each wave instruction on 1 KB / 512 B of contiguous
+// LDS), 4: two independent 16x16x32 bf16 MFMAs per step.  The base offset
+// passes through an empty asm each iteration, so no access is hoisted or
+// merged.
+template <int kKind>
+__global__ __launch_bounds__(1024) void probe_lds_kernel(uint32_t* __restrict__ out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[24576];  // 96 KB: one workgroup per CU
+  for (int i = threadIdx.x; i < 24576; i += 1024) lds[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  char* base = reinterpret_cast<char*>(lds);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  f32x4 m[8];
+  for (int j = 0; j < 8; ++j) m[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8 qa = __builtin_bit_cast(bf16x8, u32x4{lane, 3u, 5u, 7u});
+  for (int it = 0; it < iters; ++it) {
+    uint32_t o = (uint32_t)it * 8192u;
+    asm volatile("" : "+v"(o));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (kKind == 0) {
+        acc ^= *reinterpret_cast<const u32x4*>(base + ((w * 4096u + lane * 16u + o + u * 1024u) & 0xFFF0u));
+      } else if constexpr (kKind == 1) {
+        const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(base + ((w * 4096u + lane * 8u + o + u * 512u) & 0xFFF8u)));
+        acc[u & 3] ^= (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[3] << 16);
+      } else if constexpr (kKind == 2) {
+        *reinterpret_cast<u32x4*>(base + ((w * 4096u + lane * 16u + o + u * 1024u) & 0xFFF0u)) =
+            u32x4{o, lane, w, (uint32_t)u};
+      } else if constexpr (kKind == 3) {
+        *reinterpret_cast<u32x2*>(base + ((w * 4096u + lane * 8u + o + u * 512u) & 0xFFF8u)) = u32x2{o, lane};
+      } else {
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, u32x4{o ^ (uint32_t)u, lane, w, 1u});
+        m[(2 * u) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa, m[(2 * u) & 7], 0, 0, 0);
+        m[(2 * u + 1) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, m[(2 * u + 1) & 7], 0, 0, 0);
+      }
+    }
+  }
+  if constexpr (kKind == 2 || kKind == 3) {
+    __syncthreads();
+    acc[0] = lds[threadIdx.x * 16];
+  }
+  float s = 0.0f;
+  for (int j = 0; j < 8; ++j) s += m[j][0] + m[j][1] + m[j][2] + m[j][3];
+  out[(size_t)blockIdx.x * 1024 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ __float_as_uint(s);
+}
+
 __global__ __launch_bounds__(256) void probe_empty_kernel() {}
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -7; }
@@ -270,6 +329,23 @@ int probe_scatter_dwords(const int64_t* idx, int64_t n, int per_thread, int32_t*
     case 2: hipLaunchKernelGGL(probe_scatter_dwords_kernel<2>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
     case 4: hipLaunchKernelGGL(probe_scatter_dwords_kernel<4>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
     case 8: hipLaunchKernelGGL(probe_scatter_dwords_kernel<8>, grid, block, 0, (hipStream_t)stream, idx, n, dst); break;
+    default: return -1;
+  }
+  return status(hipGetLastError());
+}
+
+// LDS / MFMA rate probe: `blocks` workgroups of 1024 threads, `iters`
+// iterations of 8 accesses (kinds 0-3) or 16 MFMAs (kind 4) per wave;
+// `out` holds blocks * 1024 dwords.
+int probe_lds(int kind, int64_t blocks, int iters, uint32_t* out, void* stream) {
+  if (!out || blocks <= 0 || blocks > 0x7FFFFFFF || iters <= 0) return -1;
+  const dim3 grid((unsigned)blocks), block(1024);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(probe_lds_kernel<0>, grid, block, 0, (hipStream_t)stream, out, iters); break;
+    case 1: hipLaunchKernelGGL(probe_lds_kernel<1>, grid, block, 0, (hipStream_t)stream, out, iters); break;
+    case 2: hipLaunchKernelGGL(probe_lds_kernel<2>, grid, block, 0, (hipStream_t)stream, out, iters); break;
+    case 3: hipLaunchKernelGGL(probe_lds_kernel<3>, grid, block, 0, (hipStream_t)stream, out, iters); break;
+    case 4: hipLaunchKernelGGL(probe_lds_kernel<4>, grid, block, 0, (hipStream_t)stream, out, iters); break;
     default: return -1;
   }
   return status(hipGetLastError());
