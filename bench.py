@@ -480,7 +480,8 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
     gather-dequant's traffic (272-byte rows to 1 KiB rows, in order) and the
     CR1 norm's (2 KiB rows to 1 KiB rows) as plain copies beside those
     kernels; then the small-batch floors (an empty launch of
-    the store's grid, a plain read of the batch's latent) at 16,384 and
+    the store's grid, a plain read of the batch's latent, a copy with the
+    store's traffic) beside the store with in-order slots at 16,384 and
     65,536 tokens; last, the LDS and matrix-core rates of a CU (contiguous
     LDS reads, transposing reads and writes; bf16 MFMAs alone).  One JSON
     line per probe: median of PROBE_REPS HIP-event times of single launches,
@@ -600,6 +601,7 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
                                                              kv_out.data_ptr(), st()))))
     cases.append(("compress_norm_cr1", NORM_TOKENS * 3080,
                   lambda: ops.fused_save_compress_norm_cr1(kv, kv_slots, weight, 1e-6, kv_out)))
+    seq_slots = torch.arange(65536, dtype=torch.int64, device="cuda")
     for tokens in (16384, 65536):
         tpw = 2 if tokens <= 16384 else 4
         grid = tokens // (4 * tpw)  # the scatter store's workgroups at this size
@@ -607,6 +609,14 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
         cases.append((f"empty_launch_{tokens}", 0, lambda g=grid: ok(lib.probe_empty(g, st()))))
         cases.append((f"read_latent_{tokens}", nbytes,
                       lambda b=nbytes: ok(lib.probe_read(src.data_ptr(), b, sink.data_ptr(), st()))))
+        # the store's own traffic and write form at this size (1 KiB read,
+        # 272-byte row written per token, in order) beside the scatter store
+        # on the same batch with slot t = t
+        cases.append((f"copy_rows_sequential_{tokens}", tokens * 1296,
+                      lambda k=tokens: ok(lib.probe_copy_rows(src.data_ptr(), k, None, cache.data_ptr(), 0,
+                                                              st()))))
+        cases.append((f"store_in_order_{tokens}", tokens * BYTES_PER_TOKEN,
+                      lambda k=tokens: ops.mxfp4_store(src[:k], seq_slots[:k], cache, 1, n, n)))
     for name, nbytes, fn in cases:
         if counters:
             for _ in range(3):
@@ -634,7 +644,7 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
             line["frac_hbm_peak"] = round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)
         print(json.dumps(line), flush=True)
     del src, slots, cache, inv, flush, ring_rows, ring_slots, ring, ring_dst, ring_perm
-    del dq_out, dq_slots, kv, kv_out, kv_slots, scat
+    del dq_out, dq_slots, kv, kv_out, kv_slots, scat, seq_slots
     # LDS and matrix-core rates of a CU (no HBM traffic): 1,024 workgroups of
     # 1,024 threads (one per CU at a time), LDS_ITERS x 8 accesses per wave
     # (or x 16 MFMAs); median of 5 launches
