@@ -64,13 +64,20 @@ __device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// max(a, b) for scores (never NaN) as the median of (a, b, +inf): one
+// v_med3_f32, without the NaN-quieting moves fmaxf needs on values the
+// compiler cannot see were computed (loaded, or moved between lanes).
+// `pinf` is +inf passed through an empty asm, so the median is not folded
+// back into a maximum.
+__device__ __forceinline__ float max2(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+
 // Maximum over lanes l, l^16, l^32, l^48 (gfx950 permlane swaps: the pair
 // returned for lane l is (x[l & ~16], x[l | 16]), resp. with 32).
-__device__ __forceinline__ float max_over_quarters(float v) {
+__device__ __forceinline__ float max_over_quarters(float v, float pinf) {
   const auto a = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
-  v = fmaxf(as_f32(a[0]), as_f32(a[1]));
+  v = max2(as_f32(a[0]), as_f32(a[1]), pinf);
   const auto b = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
-  return fmaxf(as_f32(b[0]), as_f32(b[1]));
+  return max2(as_f32(b[0]), as_f32(b[1]), pinf);
 }
 
 __device__ __forceinline__ float sum_over_quarters(float v) {
@@ -177,6 +184,8 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // scores over its 128 dims for all 64 keys; the four partials meet in
       // LDS, where producer w sums those of key tile w (keys 16w .. +15).
       constexpr int pd = decltype(pdc)::value;
+      float pinf = INFINITY;
+      asm volatile("" : "+v"(pinf));
       bf16x8 qf[HT][4];
       float m_qk[HT], lsum[HT];
 #pragma unroll
@@ -197,9 +206,25 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         const int32_t v = idx_row[j < a.topk ? j : a.topk - 1];
         return j < a.topk ? v : -1;
       };
+      // Below 4 GiB a view has fewer than 2^24 rows, so a listed slot's row
+      // and its byte offset come from 24-bit products (full-rate multiplies):
+      // block index and stride are both below 2^24 unless there is a single
+      // block, whose index is 0.
       auto row_index = [&](int32_t s) -> int32_t {
         const bool ok = s >= 0 && (uint32_t)s < a.map.num_slots;
-        return ok ? (int32_t)a.map.template row<kPow2>((uint32_t)s) : -1;
+        if constexpr (kBuf) {
+          uint32_t q, r;
+          if constexpr (kPow2) {
+            q = (uint32_t)((uint64_t)(uint32_t)s >> a.map.block_shift);
+            r = (uint32_t)s & a.map.block_mask;
+          } else {
+            q = (uint32_t)s / a.map.block_size;
+            r = (uint32_t)s - q * a.map.block_size;
+          }
+          return ok ? (int32_t)(__umul24(q, (uint32_t)a.map.block_stride_rows) + r) : -1;
+        } else {
+          return ok ? (int32_t)a.map.template row<kPow2>((uint32_t)s) : -1;
+        }
       };
       // Rows of keys 16kt + li, kt = 0..3, from the lanes (li, kt) that hold
       // them (permlane swaps: lane (li, lq) ends with the value of lane (li, kt)).
@@ -221,7 +246,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           if constexpr (kBuf) {
-            const uint32_t base = rows[kt] < 0 ? kAttnBufBytes : (uint32_t)rows[kt] * kRowBytes;
+            const uint32_t base = rows[kt] < 0 ? kAttnBufBytes : __umul24((uint32_t)rows[kt], kRowBytes);
             c[kt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, base + 64 * pd + 16 * lq, 0, 0));
             sd[kt] = __builtin_amdgcn_raw_buffer_load_b32(crs, base + 256 + 4 * pd, 0, 0);
           } else {
@@ -302,6 +327,10 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         if (step < ntile) {
           // ---- full scores of keys 16pd + 4lq + r (sum over the producers in
           // a fixed order), tile maxima (base 2); invalid keys become -inf
+          // through an additive bias (their partial sums are exact zeros)
+          float kbias[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) kbias[r] = ((vbits >> r) & 1u) ? 0.0f : -INFINITY;
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) {
             f32x4 part[4];
@@ -311,9 +340,9 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float sc = (part[0][r] + part[1][r]) + (part[2][r] + part[3][r]);
-              x[ht][r] = ((vbits >> r) & 1u) ? sc * a.c : -INFINITY;
+              x[ht][r] = __builtin_fmaf(sc, a.c, kbias[r]);
             }
-            const float mx = max_over_quarters(fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])));
+            const float mx = max_over_quarters(fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])), pinf);
             if (lq == 0) sm.loop.red[pb][16 * ht + li][pd] = mx;
           }
         }
@@ -325,14 +354,16 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) {
             const float* red = sm.loop.red[pb][16 * ht + li];
-            const float mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            const float mt = max2(max2(red[0], red[1], pinf), max2(red[2], red[3], pinf), pinf);
             const float mnew = mt > m_qk[ht] + kMaxSlack ? mt : m_qk[ht];
             const float alpha = mnew != m_qk[ht] ? __builtin_amdgcn_exp2f(m_qk[ht] - mnew) : 1.0f;
             moved |= mnew != m_qk[ht];
             m_qk[ht] = mnew;
+            // mnew is -inf only while every key so far was skipped (x = -inf)
+            const float mref = mnew == -INFINITY ? 0.0f : mnew;
             float p[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = mnew == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[ht][r] - mnew);
+            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[ht][r] - mref);
             lsum[ht] = lsum[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
             *reinterpret_cast<uint64_t*>(&sm.loop.p[pb][(16 * ht + li) * kPitch + 16 * pd + 4 * lq]) =
                 (uint64_t)bf16x2_rn(p[0], p[1]) | ((uint64_t)bf16x2_rn(p[2], p[3]) << 32);
