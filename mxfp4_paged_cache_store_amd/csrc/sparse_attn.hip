@@ -21,12 +21,13 @@
 //            against query fragments of the same dims (B operand, all HB
 //            heads, in registers), so every key is unpacked once.  Each
 //            producer copies its slice of the packed rows to LDS for the
-//            consumer of that slice, keeps its partials of key tile pd and
-//            passes the other three through LDS; after a barrier producer pd
-//            adds the four partials of keys 16pd .. +15 in a fixed order.
-//            Softmax in base 2: tile maxima of the 4 producers meet in LDS;
-//            the running maximum moves only past a slack, and when it moves
-//            the new maxima are published with a flag; weights go to LDS as
+//            consumer of that slice and writes its partial scores to LDS.
+//            After a barrier producer pd owns heads HB/4*pd .. +HB/4-1 over
+//            all 64 keys: it adds the four partials of its (head, key)
+//            pairs in a fixed order and runs the softmax in base 2 -- the
+//            tile maximum of a head is reduced among the head's lanes, the
+//            running maximum moves only past a slack, and when it moves the
+//            new maxima are published with a flag; weights go to LDS as
 //            bf16.
 //   consumers (waves 4..7) own output dims 128*(w-4) .. +127 of all HB
 //            heads and compute O += P V for tile s - 1.  The B operand needs
@@ -37,9 +38,9 @@
 //            pairs along dims) and re-pairs the halves along keys with
 //            v_perm_b32: 8 B operands for 8 MFMAs whose output column j is
 //            dim 8j + n of the slab.
-// LDS buffers alternate between tiles; a step costs three barriers (partials,
-// maxima, weights), and the consumers do all their work before the first.
-// At the end the sink is folded in, the producers' partial sums are added,
+// The packed-row buffers alternate between tiles; a step costs two barriers
+// (partial scores, weights), and the consumers do all their work before the
+// first.  At the end each owner folds the sink into its heads' weight sums,
 // and O / l is rounded to bf16.
 #include <type_traits>
 #include "kernels.hpp"
@@ -111,7 +112,10 @@ __device__ __forceinline__ uint32_t cvt_byte(uint32_t codes, float scale, int se
 // which owns 128 output dims.
 constexpr int kTile = 64;
 constexpr int kProducers = 4;
-constexpr int kPitch = kTile + 8;  // bf16 per LDS weight row (rows stay 16-B aligned)
+// bf16 per LDS weight row: 160 bytes, 8 dwords past a multiple of 32, at
+// which rows read or written 16 bytes each at one column meet no bank
+// conflict (measured).
+constexpr int kPitch = kTile + 16;
 // A key's row in LDS: its 256 code bytes, then the 16 group scales as fp32
 // (E8M0 byte in the exponent field, the form the converter takes), 8 bytes
 // of padding: rows 328 bytes apart, so rows 8 apart start 16 banks apart and
@@ -129,17 +133,26 @@ struct AttnSmem {
   union {
     struct {
       uint8_t kv[2][kTile][kKvPitch];        // packed rows of a tile
-      uint16_t p[2][HB * kPitch];            // a tile's weights (bf16): [head][key]
-      f32x4 sp[kProducers][kProducers - 1][HT][kWave];  // partial scores of the key tiles other producers own
-      float red[2][HB][kProducers];          // per-producer tile maxima
-      float mpub[2][HB];                     // running maxima after a tile
-      uint32_t moved[2];                     // some head's running maximum moved
+      uint16_t p[HB * kPitch];               // the latest tile's weights (bf16): [head][key]
+      // partial scores [producer][key tile][head tile][slot]: lane (li, lq)
+      // at slot 16lq + (li ^ 4lq), so an owner's 16-lane reads, which span
+      // several quarter-waves, fall in distinct banks
+      f32x4 sp[kProducers][kProducers][HT][kWave];
+      float mpub[HB];                        // running maxima after the latest tile
+      uint32_t moved[2];                     // some head's running maximum moved at that tile
     } loop;
     struct {
-      float l[kProducers][HB];               // partial sums
+      float l[HB];                           // weight sums (the sink folded in)
     } fin;
   };
 };
+
+__device__ __forceinline__ float dpp_ror4(float v) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), 0x128, 0xF, 0xF, false));
+}
 
 // Two workgroups per CU: at most 128 registers per lane (4 waves per SIMD).
 template <int HB, bool kPow2, bool kBuf, bool kSplit>
@@ -187,11 +200,17 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       float pinf = INFINITY;
       asm volatile("" : "+v"(pinf));
       bf16x8 qf[HT][4];
-      float m_qk[HT], lsum[HT];
+      // After the first barrier of a step producer pd owns heads HPO*pd ..
+      // +HPO-1 over all 64 keys: lane (hh, kk) holds head HPO*pd + hh and
+      // keys KPL*kk .. +KPL-1, whose scores it reads from NQ slots of each
+      // producer's partial-score tiles.
+      constexpr int HPO = HB / kProducers, KPL = kTile * HPO / kWave, NQ = KPL / 4;
+      const int hh = lane % HPO, kk = lane / HPO;
+      const int oh = HPO * pd + hh, oht = oh >> 4, oli = oh & 15;
+      const int okt = (KPL * kk) >> 4, olq0 = ((KPL * kk) & 15) >> 2;
+      float m_own = -INFINITY, lsum = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        m_qk[ht] = -INFINITY;
-        lsum[ht] = 0.0f;
         const uint16_t* qh = a.q + t * a.q_token_stride + (int64_t)(h0 + 16 * ht + li) * a.q_head_stride +
                              128 * pd + 32 * lq;
 #pragma unroll
@@ -271,12 +290,10 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 
       for (int64_t step = 0; step <= ntile; ++step) {
         const int pb = (int)(step & 1), cb = pb ^ 1;
-        float x[HT][4];
-        uint32_t vbits = 0;
+        uint64_t valid = 0;  // bit k: key k of the tile is listed
         if (step < ntile) {
           // ---- the packed slice to LDS for consumer pd; partial scores
-          const uint64_t valid = __ballot(g_own >= 0);  // bit k: key k of the tile
-          vbits = (uint32_t)(valid >> (16 * pd + 4 * lq)) & 0xFu;  // keys 16pd + 4lq + r
+          valid = __ballot(g_own >= 0);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             if (!kBuf && !((valid >> (16 * kt + li)) & 1u)) {
@@ -288,9 +305,8 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
             *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq + 8) = (uint64_t)g_cw[kt][2] | ((uint64_t)g_cw[kt][3] << 32);
             *reinterpret_cast<float*>(dst + kKvScales + 4 * (4 * pd + lq)) = as_f32(((g_sd[kt] >> (8 * lq)) & 0xFFu) << 23);
           }
-          // Key tile by key tile: partial scores over the 128 dims; those of
-          // the other producers' tiles go to LDS, the own tile's stay in x
-          // (summed in producer order after the barrier).
+          // Key tile by key tile: partial scores over the 128 dims, to LDS
+          // for the owners of their heads.
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             f32x4 s[HT];
@@ -305,14 +321,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
                 s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ht][ks], s[ht], 0, 0, 0);
             }
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-              if (kt != pd) {
-                sm.loop.sp[pd][(kt - pd - 1) & 3][ht][lane] = s[ht];
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x[ht][r] = s[ht][r];
-              }
-            }
+            for (int ht = 0; ht < HT; ++ht) sm.loop.sp[pd][kt][ht][16 * lq + (li ^ (4 * lq))] = s[ht];
           }
           // ---- next tile's gather (the index load goes first: waiting for it
           // later must not wait for the gather, as loads complete in order)
@@ -325,71 +334,71 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         }
         __syncthreads();
         if (step < ntile) {
-          // ---- full scores of keys 16pd + 4lq + r (sum over the producers in
-          // a fixed order), tile maxima (base 2); invalid keys become -inf
-          // through an additive bias (their partial sums are exact zeros)
-          float kbias[4];
+          // ---- owned heads: full scores (the four producers' partials in a
+          // fixed order; skipped keys -inf through an additive bias, their
+          // partial sums being exact zeros), the tile maximum over the head's
+          // lanes, running maximum, weights, partial sum; publish
+          if (threadIdx.x == 0) sm.loop.moved[cb] = 0u;  // read as tile step - 1's flag before the first barrier
+          const uint32_t vb = (uint32_t)(valid >> (KPL * kk));
+          float x[KPL];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) kbias[r] = ((vbits >> r) & 1u) ? 0.0f : -INFINITY;
+          for (int q = 0; q < NQ; ++q) {
+            f32x4 part[kProducers];
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            f32x4 part[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              part[v] = v == pd ? f32x4{x[ht][0], x[ht][1], x[ht][2], x[ht][3]} : sm.loop.sp[v][(pd - v - 1) & 3][ht][lane];
+            for (int v = 0; v < kProducers; ++v)
+              part[v] = sm.loop.sp[v][okt][oht][16 * (olq0 + q) + (oli ^ (4 * (olq0 + q)))];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float sc = (part[0][r] + part[1][r]) + (part[2][r] + part[3][r]);
-              x[ht][r] = __builtin_fmaf(sc, a.c, kbias[r]);
+              x[4 * q + r] = __builtin_fmaf(sc, a.c, ((vb >> (4 * q + r)) & 1u) ? 0.0f : -INFINITY);
             }
-            const float mx = max_over_quarters(fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])), pinf);
-            if (lq == 0) sm.loop.red[pb][16 * ht + li][pd] = mx;
           }
-        }
-        __syncthreads();
-        if (step < ntile) {
-          // ---- running maxima, weights, partial sums; publish
-          if (threadIdx.x == 0) sm.loop.moved[cb] = 0u;  // the consumers read it before the first barrier
-          bool moved = false;
+          float mt = x[0];
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            const float* red = sm.loop.red[pb][16 * ht + li];
-            const float mt = max2(max2(red[0], red[1], pinf), max2(red[2], red[3], pinf), pinf);
-            const float mnew = mt > m_qk[ht] + kMaxSlack ? mt : m_qk[ht];
-            const float alpha = mnew != m_qk[ht] ? __builtin_amdgcn_exp2f(m_qk[ht] - mnew) : 1.0f;
-            moved |= mnew != m_qk[ht];
-            m_qk[ht] = mnew;
-            // mnew is -inf only while every key so far was skipped (x = -inf)
-            const float mref = mnew == -INFINITY ? 0.0f : mnew;
-            float p[4];
+          for (int j = 1; j < KPL; ++j) mt = fmaxf(mt, x[j]);
+          // lanes of one head differ in lane bits log2(HPO) .. 5
+          if constexpr (HPO == 4) mt = max2(mt, dpp_ror4(mt), pinf);
+          mt = max2(mt, dpp_ror8(mt), pinf);
+          mt = max_over_quarters(mt, pinf);
+          const float mnew = mt > m_own + kMaxSlack ? mt : m_own;
+          const bool mv = mnew != m_own;
+          const float alpha = mv ? __builtin_amdgcn_exp2f(m_own - mnew) : 1.0f;
+          // mnew is -inf only while every key so far was skipped (x = -inf)
+          const float mref = mnew == -INFINITY ? 0.0f : mnew;
+          float pw[KPL];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[ht][r] - mref);
-            lsum[ht] = lsum[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            *reinterpret_cast<uint64_t*>(&sm.loop.p[pb][(16 * ht + li) * kPitch + 16 * pd + 4 * lq]) =
-                (uint64_t)bf16x2_rn(p[0], p[1]) | ((uint64_t)bf16x2_rn(p[2], p[3]) << 32);
-            if (pd == 0 && lq == 0) sm.loop.mpub[pb][16 * ht + li] = mnew;
+          for (int j = 0; j < KPL; ++j) pw[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+          float ps = 0.0f;
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) ps += (pw[4 * q] + pw[4 * q + 1]) + (pw[4 * q + 2] + pw[4 * q + 3]);
+          lsum = lsum * alpha + ps;
+          m_own = mnew;
+          uint16_t* prow = &sm.loop.p[oh * kPitch + KPL * kk];
+          if constexpr (KPL == 8) {
+            *reinterpret_cast<u32x4*>(prow) = u32x4{bf16x2_rn(pw[0], pw[1]), bf16x2_rn(pw[2], pw[3]),
+                                                    bf16x2_rn(pw[4], pw[5]), bf16x2_rn(pw[6], pw[7])};
+          } else {
+            *reinterpret_cast<uint64_t*>(prow) =
+                (uint64_t)bf16x2_rn(pw[0], pw[1]) | ((uint64_t)bf16x2_rn(pw[2], pw[3]) << 32);
           }
-          if (__any(moved) && lane == 0) sm.loop.moved[pb] = 1u;
+          if (kk == 0) sm.loop.mpub[oh] = mnew;
+          if (__any(mv) && lane == 0) sm.loop.moved[pb] = 1u;
         }
         __syncthreads();
       }
 
-      // ---- sink and partial sums
-      float l[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        l[ht] = sum_over_quarters(lsum[ht]);
-        if (a.sink && !kSplit) {  // the split form folds the sink in when merging
-          const float s2 = a.sink[h0 + 16 * ht + li] * kLog2e;
-          const float mf = fmaxf(m_qk[ht], s2);
-          l[ht] = m_qk[ht] == -INFINITY ? 0.0f : l[ht] * __builtin_amdgcn_exp2f(m_qk[ht] - mf);
-          if (pd == 0) l[ht] += __builtin_amdgcn_exp2f(s2 - mf);
-        }
+      // ---- weight sum of the owned head over its lanes (fixed order), sink
+      float l = lsum;
+      if constexpr (HPO == 4) l += dpp_ror4(l);
+      l += dpp_ror8(l);
+      l = sum_over_quarters(l);
+      if (a.sink && !kSplit) {  // the split form folds the sink in when merging
+        const float s2 = a.sink[h0 + oh] * kLog2e;
+        const float mf = fmaxf(m_own, s2);
+        l = (m_own == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m_own - mf)) + __builtin_amdgcn_exp2f(s2 - mf);
       }
       __syncthreads();  // the loop's LDS is reused
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        if (lq == 0) sm.fin.l[pd][16 * ht + li] = l[ht];
+      if (kk == 0) sm.fin.l[oh] = l;
       __syncthreads();
     };
     switch (w) {
@@ -417,7 +426,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
         pf[ht] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&sm.loop.p[cb][(16 * ht + li) * kPitch + kb + 8 * lq]));
+            bf16x8, *reinterpret_cast<const u32x4*>(&sm.loop.p[(16 * ht + li) * kPitch + kb + 8 * lq]));
       uint32_t vc[8];
       float vs[8];
 #pragma unroll
@@ -456,7 +465,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float mnew = sm.loop.mpub[cb][16 * ht + 4 * lq + r];
+              const float mnew = sm.loop.mpub[16 * ht + 4 * lq + r];
               const float alpha = mnew == m_pv[ht][r] ? 1.0f : __builtin_amdgcn_exp2f(m_pv[ht][r] - mnew);
               m_pv[ht][r] = mnew;
 #pragma unroll
@@ -466,7 +475,6 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         pv_step(cb, 0);
         pv_step(cb, 1);
       }
-      __syncthreads();
       __syncthreads();
       __syncthreads();
     }
@@ -479,7 +487,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 16 * ht + 4 * lq + r;
-        const float lt = (sm.fin.l[0][h] + sm.fin.l[1][h]) + (sm.fin.l[2][h] + sm.fin.l[3][h]);
+        const float lt = sm.fin.l[h];
         if constexpr (kSplit) {
           // Unnormalised partial output and (running maximum, weight sum)
           // of this key range, merged by attn_merge_kernel.
