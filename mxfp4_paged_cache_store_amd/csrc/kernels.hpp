@@ -87,7 +87,10 @@ struct AttnArgs {
   const int32_t* indices;     // [num_tokens, topk], row stride idx_stride
   int64_t topk;
   int64_t idx_stride;
-  float c;                    // softmax scale * log2(e)
+  float c;                    // |softmax scale| * log2(e) (> 0), or 1 when that is 0
+  uint32_t q_xor, q_and;      // applied to each bf16 pair of q: 0x80008000 / ~0 for a
+                              // negative scale (scores from -q times |scale|, exactly the
+                              // same), 0 / 0 for a zero one (all scores 0), else 0 / ~0
   const float* sink;          // [num_heads] natural-log logits, or null
   uint16_t* out;              // bf16 [num_tokens, num_heads, 512]
   int64_t out_token_stride;

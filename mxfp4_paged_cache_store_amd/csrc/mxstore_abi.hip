@@ -3,6 +3,7 @@
 // alignment and range rules the gfx950 kernels rely on) and the launch on the
 // caller's stream.  No allocation, no synchronisation.  Declarations and the
 // full contract are in include/mxstore.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -421,7 +422,14 @@ static int attention(const uint16_t* q_bf16, int64_t num_tokens, int64_t num_hea
   a.indices = indices;
   a.topk = topk;
   a.idx_stride = indices_stride;
-  a.c = (float)((double)scale * 1.4426950408889634);
+  {
+    // The kernel scales scores by a positive c: a negative scale negates q
+    // instead (exact), and a zero one (or one that rounds to 0) zeroes it.
+    const float c = (float)((double)scale * 1.4426950408889634);
+    a.c = c == 0.0f ? 1.0f : fabsf(c);
+    a.q_xor = c < 0.0f ? 0x80008000u : 0u;
+    a.q_and = c == 0.0f ? 0u : ~0u;
+  }
   a.sink = sink;
   a.out = out_bf16;
   a.out_token_stride = out_token_stride;

@@ -126,6 +126,15 @@ constexpr int kKvScales = 256;
 // than this (base-2 units): weights stay below 2^8, far from fp32 / bf16
 // overflow, and most tiles need no rescaling of O.
 constexpr float kMaxSlack = 8.0f;
+// Row index standing for a skipped key in views gathered through a raw
+// buffer: every byte of its row lies at an offset at or past the largest
+// such view and below 2^32, so its loads read zeros with no test, and no row
+// of such a view (fewer than kAttnBufBytes / 272 rows) has this index.
+constexpr uint32_t kRowSkip = 0xF0F0EFu;
+static_assert((uint64_t)kRowSkip * kRowBytes >= kAttnBufBytes &&
+              (uint64_t)kRowSkip * kRowBytes + kRowBytes <= 0x100000000ull &&
+              kRowSkip < (1u << 24) && kAttnBufBytes / kRowBytes < kRowSkip,
+              "skip row must read past every buffered view");
 
 template <int HB>
 struct AttnSmem {
@@ -147,11 +156,13 @@ struct AttnSmem {
   };
 };
 
+// Rotations within rows of 16 lanes (every lane has a source, so no old
+// value is needed).
 __device__ __forceinline__ float dpp_ror4(float v) {
-  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), 0x124, 0xF, 0xF, false));
+  return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x124, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float dpp_ror8(float v) {
-  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), 0x128, 0xF, 0xF, false));
+  return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x128, 0xF, 0xF, true));
 }
 
 // Two workgroups per CU: at most 128 registers per lane (4 waves per SIMD).
@@ -217,6 +228,13 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         for (int ks = 0; ks < 4; ++ks)
           qf[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 8 * ks));
       }
+      if (a.q_xor != 0u || a.q_and != ~0u) {  // a negative or zero scale
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            qf[ht][ks] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, qf[ht][ks]) ^ a.q_xor) & a.q_and);
+      }
       // Slot index of key 16lq + li (one load per lane covers the tile);
       // unconditional (address clamped, result masked) so the compiler's wait
       // counts stay exact.  Loads run only when topk >= 1.
@@ -228,7 +246,8 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // Below 4 GiB a view has fewer than 2^24 rows, so a listed slot's row
       // and its byte offset come from 24-bit products (full-rate multiplies):
       // block index and stride are both below 2^24 unless there is a single
-      // block, whose index is 0.
+      // block, whose index is 0.  A skipped key's row is kRowSkip there, -1
+      // otherwise.
       auto row_index = [&](int32_t s) -> int32_t {
         const bool ok = s >= 0 && (uint32_t)s < a.map.num_slots;
         if constexpr (kBuf) {
@@ -240,7 +259,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
             q = (uint32_t)s / a.map.block_size;
             r = (uint32_t)s - q * a.map.block_size;
           }
-          return ok ? (int32_t)(__umul24(q, (uint32_t)a.map.block_stride_rows) + r) : -1;
+          return ok ? (int32_t)(__umul24(q, (uint32_t)a.map.block_stride_rows) + r) : (int32_t)kRowSkip;
         } else {
           return ok ? (int32_t)a.map.template row<kPow2>((uint32_t)s) : -1;
         }
@@ -257,21 +276,22 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         rows[3] = (int32_t)c1[1];
       };
       // Through a raw buffer over the cache view when it spans less than
-      // kAttnBufBytes: a skipped key's offset lies past the view, so its
-      // codes and scales read as zeros (zero values); otherwise global loads
-      // of row 0, masked where they are used.
+      // kAttnBufBytes: a skipped key's row kRowSkip lies past the view, so its
+      // codes and scale read as zeros (zero values); otherwise global loads
+      // of row 0, masked where they are used.  Lane (li, lq) loads the scale
+      // byte of its own 32 dims.
       const __amdgpu_buffer_rsrc_t crs = buffer_at(a.cache, kBuf ? a.cache_bytes : 0u);
-      auto gather = [&](const int32_t (&rows)[4], u32x4 (&c)[4], uint32_t (&sd)[4]) {
+      auto gather = [&](const int32_t (&rows)[4], u32x4 (&c)[4], uint32_t (&sb)[4]) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           if constexpr (kBuf) {
-            const uint32_t base = rows[kt] < 0 ? kAttnBufBytes : __umul24((uint32_t)rows[kt], kRowBytes);
+            const uint32_t base = __umul24((uint32_t)rows[kt], kRowBytes);
             c[kt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, base + 64 * pd + 16 * lq, 0, 0));
-            sd[kt] = __builtin_amdgcn_raw_buffer_load_b32(crs, base + 256 + 4 * pd, 0, 0);
+            sb[kt] = __builtin_amdgcn_raw_buffer_load_b8(crs, base + 256 + 4 * pd + lq, 0, 0);
           } else {
             const uint8_t* rp = a.cache + (int64_t)(rows[kt] < 0 ? 0 : rows[kt]) * kRowBytes;
             c[kt] = *reinterpret_cast<const u32x4*>(rp + 64 * pd + 16 * lq);
-            sd[kt] = *reinterpret_cast<const uint32_t*>(rp + 256 + 4 * pd);
+            sb[kt] = rp[256 + 4 * pd + lq];
           }
         }
       };
@@ -279,12 +299,12 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // (one tile ahead); slot indices are loaded one tile earlier still.
       int32_t g_own = -1, g_idx = -1;  // row of key 16lq + li; next tile's index
       u32x4 g_cw[4];
-      uint32_t g_sd[4];
+      uint32_t g_sb[4];  // scale byte of the lane's 32 dims, per key tile
       if (ntile > 0) {
         g_own = row_index(load_index(0));
         int32_t rows[4];
         spread_rows(g_own, rows);
-        gather(rows, g_cw, g_sd);
+        gather(rows, g_cw, g_sb);
         g_idx = load_index(1);
       }
 
@@ -293,26 +313,35 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         uint64_t valid = 0;  // bit k: key k of the tile is listed
         if (step < ntile) {
           // ---- the packed slice to LDS for consumer pd; partial scores
-          valid = __ballot(g_own >= 0);
+          valid = __ballot(kBuf ? g_own != (int32_t)kRowSkip : g_own >= 0);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             if (!kBuf && !((valid >> (16 * kt + li)) & 1u)) {
               g_cw[kt] = u32x4{0u, 0u, 0u, 0u};
-              g_sd[kt] = 0u;
+              g_sb[kt] = 0u;
             }
             uint8_t* dst = sm.loop.kv[pb][16 * kt + li];
             *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq) = (uint64_t)g_cw[kt][0] | ((uint64_t)g_cw[kt][1] << 32);
             *reinterpret_cast<uint64_t*>(dst + 64 * pd + 16 * lq + 8) = (uint64_t)g_cw[kt][2] | ((uint64_t)g_cw[kt][3] << 32);
-            *reinterpret_cast<float*>(dst + kKvScales + 4 * (4 * pd + lq)) = as_f32(((g_sd[kt] >> (8 * lq)) & 0xFFu) << 23);
+            *reinterpret_cast<float*>(dst + kKvScales + 4 * (4 * pd + lq)) = as_f32(g_sb[kt] << 23);
           }
           // Key tile by key tile: partial scores over the 128 dims, to LDS
-          // for the owners of their heads.
+          // for the owners of their heads.  The accumulators start at 0,
+          // except that in key tile pd those of skipped keys (rows 4lq + r)
+          // start at -inf: a skipped key's codes are zeros, so its partials
+          // are exact zeros but for this one, and its score sum is -inf.
+          f32x4 bias;
+          {
+            const uint32_t skip = (uint32_t)(~valid >> (16 * pd)) >> (4 * lq);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bias[r] = as_f32((0u - ((skip >> r) & 1u)) & 0xFF800000u);
+          }
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             f32x4 s[HT];
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) s[ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint32_t sbyte = (g_sd[kt] >> (8 * lq)) & 0xFFu;
+            for (int ht = 0; ht < HT; ++ht) s[ht] = kt == pd ? bias : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t sbyte = g_sb[kt];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
               const bf16x8 kf = __builtin_bit_cast(bf16x8, unpack8(g_cw[kt][ks], sbyte));
@@ -330,16 +359,16 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           g_own = row_index(nxt);
           int32_t rows[4];
           spread_rows(g_own, rows);
-          gather(rows, g_cw, g_sd);
+          gather(rows, g_cw, g_sb);
         }
         __syncthreads();
         if (step < ntile) {
-          // ---- owned heads: full scores (the four producers' partials in a
-          // fixed order; skipped keys -inf through an additive bias, their
-          // partial sums being exact zeros), the tile maximum over the head's
-          // lanes, running maximum, weights, partial sum; publish
+          // ---- owned heads: score sums (the four producers' partials in a
+          // fixed order; -inf for skipped keys), the tile maximum over the
+          // head's lanes, running maximum, weights, partial sum; publish.
+          // The sums are scaled by c > 0 only in the weights' exponent (one
+          // fma): max_j fl(c x_j) = fl(c max_j x_j), as rounding is monotonic.
           if (threadIdx.x == 0) sm.loop.moved[cb] = 0u;  // read as tile step - 1's flag before the first barrier
-          const uint32_t vb = (uint32_t)(valid >> (KPL * kk));
           float x[KPL];
 #pragma unroll
           for (int q = 0; q < NQ; ++q) {
@@ -348,10 +377,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
             for (int v = 0; v < kProducers; ++v)
               part[v] = sm.loop.sp[v][okt][oht][16 * (olq0 + q) + (oli ^ (4 * (olq0 + q)))];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float sc = (part[0][r] + part[1][r]) + (part[2][r] + part[3][r]);
-              x[4 * q + r] = __builtin_fmaf(sc, a.c, ((vb >> (4 * q + r)) & 1u) ? 0.0f : -INFINITY);
-            }
+            for (int r = 0; r < 4; ++r) x[4 * q + r] = (part[0][r] + part[1][r]) + (part[2][r] + part[3][r]);
           }
           float mt = x[0];
 #pragma unroll
@@ -359,18 +385,20 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           // lanes of one head differ in lane bits log2(HPO) .. 5
           if constexpr (HPO == 4) mt = max2(mt, dpp_ror4(mt), pinf);
           mt = max2(mt, dpp_ror8(mt), pinf);
-          mt = max_over_quarters(mt, pinf);
+          mt = max_over_quarters(mt, pinf) * a.c;
           const float mnew = mt > m_own + kMaxSlack ? mt : m_own;
           const bool mv = mnew != m_own;
-          const float alpha = mv ? __builtin_amdgcn_exp2f(m_own - mnew) : 1.0f;
-          // mnew is -inf only while every key so far was skipped (x = -inf)
+          // mnew is -inf only while every key so far was skipped (x = -inf);
+          // alpha is exactly 1 when the maximum did not move, and 0 while
+          // m_own is -inf
           const float mref = mnew == -INFINITY ? 0.0f : mnew;
+          const float alpha = __builtin_amdgcn_exp2f(m_own - mref);
           float pw[KPL];
 #pragma unroll
-          for (int j = 0; j < KPL; ++j) pw[j] = __builtin_amdgcn_exp2f(x[j] - mref);
-          float ps = 0.0f;
+          for (int j = 0; j < KPL; ++j) pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.c, -mref));
+          float ps = (pw[0] + pw[1]) + (pw[2] + pw[3]);
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) ps += (pw[4 * q] + pw[4 * q + 1]) + (pw[4 * q + 2] + pw[4 * q + 3]);
+          for (int q = 1; q < NQ; ++q) ps += (pw[4 * q] + pw[4 * q + 1]) + (pw[4 * q + 2] + pw[4 * q + 3]);
           lsum = lsum * alpha + ps;
           m_own = mnew;
           uint16_t* prow = &sm.loop.p[oh * kPitch + KPL * kk];

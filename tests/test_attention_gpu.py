@@ -3,10 +3,10 @@ attention over the bf16 dequantized cache.
 
 Tolerance, derived from the kernel's arithmetic.  Scores: bf16 x bf16
 products are exact in fp32 and the MFMAs accumulate 512 of them in fp32, so
-|dS_j| <= g * scale * sum_d |q_d v_jd| with g = 2^-18 (a generous bound on
+|dS_j| <= g * |scale| * sum_d |q_d v_jd| with g = 2^-18 (a generous bound on
 32 chained fp32 accumulations); a score error e moves each softmax weight by
 a relative e - e_max, so the output moves by at most 4 g * SQ * A, with
-SQ = max_j scale * sum_d |q_d v_jd| and A_d = sum_j p_j |v_jd| / Z (p the
+SQ = max_j |scale| * sum_d |q_d v_jd| and A_d = sum_j p_j |v_jd| / Z (p the
 exact weights, Z their sum with the sink term).  The base-2 exponent
 (scale * log2 e rounded to fp32, exp2 in fp32) adds at most
 2^-19 * (1 + max|s|) relative per weight.  The weights are rounded to bf16
@@ -52,7 +52,7 @@ def tolerance(q_bits, cache, nb, bs, bsr, idx, scale, sink, exact):
             continue
         v = dequant_rows(cache, nb, bs, bsr, idx[t][good])                      # [J, D]
         s = scale * (qd[t] @ v.T)                                                # [H, J]
-        sq = scale * (np.abs(qd[t]) @ np.abs(v).T).max(axis=1)                   # [H]
+        sq = abs(scale) * (np.abs(qd[t]) @ np.abs(v).T).max(axis=1)              # [H]
         m = s.max(axis=1)
         if sink is not None:
             m = np.maximum(m, sink.astype(np.float64))
@@ -106,6 +106,18 @@ def test_attention_parity(device, tokens, heads, topk, sink, seed):
     case = workloads.attention_case(tokens, heads, topk, seed, sink=sink)
     worst = check_case(device, case)
     log(f"worst error / tolerance = {worst:.3f}")
+
+
+@pytest.mark.parametrize("sign", [-1.0, 0.0])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_attention_negative_and_zero_scale(device, sign, splits):
+    """A negative softmax scale (the kernel scores -q against |scale|,
+    which gives exactly the same scores) and a zero one (every score 0: the
+    weights are uniform over the valid slots, beside the sink), with skipped
+    slots and a ragged tile, in the one-pass and split forms."""
+    case = workloads.attention_case(5, 32, 200, 21, sink=True)
+    case.scale = sign * case.scale
+    check_case(device, case, splits=splits)
 
 
 def test_attention_sharp_scores_and_paged_cache(device):
