@@ -65,29 +65,6 @@ __device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// max(a, b) for scores (never NaN) as the median of (a, b, +inf): one
-// v_med3_f32, without the NaN-quieting moves fmaxf needs on values the
-// compiler cannot see were computed (loaded, or moved between lanes).
-// `pinf` is +inf passed through an empty asm, so the median is not folded
-// back into a maximum.
-__device__ __forceinline__ float max2(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
-
-// Maximum over lanes l, l^16, l^32, l^48 (gfx950 permlane swaps: the pair
-// returned for lane l is (x[l & ~16], x[l | 16]), resp. with 32).
-__device__ __forceinline__ float max_over_quarters(float v, float pinf) {
-  const auto a = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
-  v = max2(as_f32(a[0]), as_f32(a[1]), pinf);
-  const auto b = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
-  return max2(as_f32(b[0]), as_f32(b[1]), pinf);
-}
-
-__device__ __forceinline__ float sum_over_quarters(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
-  v = as_f32(a[0]) + as_f32(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
-  return as_f32(b[0]) + as_f32(b[1]);
-}
-
 __device__ __forceinline__ u32x4 unpack8(uint32_t codes, uint32_t scale_byte) {
   const float scale = as_f32(scale_byte << 23);
   return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0)),
@@ -143,10 +120,11 @@ struct AttnSmem {
     struct {
       uint8_t kv[2][kTile][kKvPitch];        // packed rows of a tile
       uint16_t p[HB * kPitch];               // the latest tile's weights (bf16): [head][key]
-      // partial scores [producer][key tile][head tile][slot]: lane (li, lq)
-      // at slot 16lq + (li ^ 4lq), so an owner's 16-lane reads, which span
-      // several quarter-waves, fall in distinct banks
-      f32x4 sp[kProducers][kProducers][HT][kWave];
+      // partial scores, 16 bytes (4 keys of one head) each: row (producer,
+      // head tile, sub-block q, head li) holds the head's key blocks kk, at
+      // column kk ^ li (see the producer); an owner's 8 lanes of one head
+      // read one 128-byte row, and 8 writing lanes hit 8 distinct columns
+      f32x4 sp[kProducers * kProducers * HT * kWave];
       float mpub[HB];                        // running maxima after the latest tile
       uint32_t moved[2];                     // some head's running maximum moved at that tile
     } loop;
@@ -156,13 +134,29 @@ struct AttnSmem {
   };
 };
 
-// Rotations within rows of 16 lanes (every lane has a source, so no old
-// value is needed).
-__device__ __forceinline__ float dpp_ror4(float v) {
-  return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x124, 0xF, 0xF, true));
+// Reductions over aligned groups of 8 or 16 consecutive lanes, in DPP
+// steps: swap neighbours, swap pairs, mirror within 8 lanes, mirror within
+// 16.  Every lane ends with the same value (each step combines two values
+// the same way in both lanes).  The maximum is written as v_max_f32 with a
+// DPP operand directly: through fmaxf the compiler would add NaN-quieting
+// moves on the moved value (scores are never NaN).  A DPP read of a VGPR
+// written by the previous VALU instruction needs two wait states.
+template <int N>
+__device__ __forceinline__ float max_lanes(float v) {
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "=v"(v) : "v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(v) : "v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf" : "=v"(v) : "v"(v));
+  if constexpr (N == 16)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf" : "=v"(v) : "v"(v));
+  return v;
 }
-__device__ __forceinline__ float dpp_ror8(float v) {
-  return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x128, 0xF, 0xF, true));
+template <int N>
+__device__ __forceinline__ float sum_lanes(float v) {
+  v += as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v += as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v += as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if constexpr (N == 16) v += as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x140, 0xF, 0xF, true));  // row_mirror
+  return v;
 }
 
 // Two workgroups per CU: at most 128 registers per lane (4 waves per SIMD).
@@ -208,17 +202,20 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // scores over its 128 dims for all 64 keys; the four partials meet in
       // LDS, where producer w sums those of key tile w (keys 16w .. +15).
       constexpr int pd = decltype(pdc)::value;
-      float pinf = INFINITY;
-      asm volatile("" : "+v"(pinf));
       bf16x8 qf[HT][4];
       // After the first barrier of a step producer pd owns heads HPO*pd ..
-      // +HPO-1 over all 64 keys: lane (hh, kk) holds head HPO*pd + hh and
-      // keys KPL*kk .. +KPL-1, whose scores it reads from NQ slots of each
+      // +HPO-1 over all 64 keys: lane (hh, kk) = hh*LPH + kk holds head
+      // HPO*pd + hh and keys KPL*kk .. +KPL-1 (a head's lanes are LPH
+      // consecutive ones), whose scores it reads from NQ slots of each
       // producer's partial-score tiles.
-      constexpr int HPO = HB / kProducers, KPL = kTile * HPO / kWave, NQ = KPL / 4;
-      const int hh = lane % HPO, kk = lane / HPO;
+      constexpr int HPO = HB / kProducers, KPL = kTile * HPO / kWave, NQ = KPL / 4, LPH = kWave / HPO;
+      const int kk = lane % LPH, hh = lane / LPH;
       const int oh = HPO * pd + hh, oht = oh >> 4, oli = oh & 15;
-      const int okt = (KPL * kk) >> 4, olq0 = ((KPL * kk) & 15) >> 2;
+      // Partial-score slot of (producer v, head tile ht, sub-block q, head
+      // li, key block kk): keys KPL*kk + 4q .. +3 of head 16ht + li.
+      auto sp_at = [](int v, int ht, int q, int li, int kk) {
+        return (((v * HT + ht) * NQ + q) * 16 + li) * LPH + (kk ^ (li & (LPH - 1)));
+      };
       float m_own = -INFINITY, lsum = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
@@ -235,13 +232,15 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           for (int ks = 0; ks < 4; ++ks)
             qf[ht][ks] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, qf[ht][ks]) ^ a.q_xor) & a.q_and);
       }
-      // Slot index of key 16lq + li (one load per lane covers the tile);
-      // unconditional (address clamped, result masked) so the compiler's wait
-      // counts stay exact.  Loads run only when topk >= 1.
+      // Slot index of key 16lq + li (one load per lane covers the tile),
+      // through a raw buffer over the tile's listed entries (topk <= 2^24):
+      // unconditional (lanes past the list read 0 and return -1) so the
+      // compiler's wait counts stay exact.  Loads run only when topk >= 1.
       auto load_index = [&](int64_t tile) -> int32_t {
-        const int64_t j = (tile0 + tile) * kTile + 16 * lq + li;
-        const int32_t v = idx_row[j < a.topk ? j : a.topk - 1];
-        return j < a.topk ? v : -1;
+        const int64_t j0 = (tile0 + tile) * kTile, rem = a.topk - j0;
+        const uint32_t n = rem <= 0 ? 0u : rem >= kTile ? (uint32_t)kTile : (uint32_t)rem;
+        const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_at(idx_row + j0, 4u * n), 4 * lane, 0, 0);
+        return (uint32_t)lane < n ? v : -1;
       };
       // Below 4 GiB a view has fewer than 2^24 rows, so a listed slot's row
       // and its byte offset come from 24-bit products (full-rate multiplies):
@@ -249,7 +248,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // block, whose index is 0.  A skipped key's row is kRowSkip there, -1
       // otherwise.
       auto row_index = [&](int32_t s) -> int32_t {
-        const bool ok = s >= 0 && (uint32_t)s < a.map.num_slots;
+        const bool ok = (uint32_t)s < a.map.num_slots;  // fewer than 2^31 slots
         if constexpr (kBuf) {
           uint32_t q, r;
           if constexpr (kPow2) {
@@ -350,7 +349,8 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
                 s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ht][ks], s[ht], 0, 0, 0);
             }
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) sm.loop.sp[pd][kt][ht][16 * lq + (li ^ (4 * lq))] = s[ht];
+            for (int ht = 0; ht < HT; ++ht)
+              sm.loop.sp[sp_at(pd, ht, ((16 * kt + 4 * lq) % KPL) / 4, li, (16 * kt + 4 * lq) / KPL)] = s[ht];
           }
           // ---- next tile's gather (the index load goes first: waiting for it
           // later must not wait for the gather, as loads complete in order)
@@ -375,17 +375,14 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
             f32x4 part[kProducers];
 #pragma unroll
             for (int v = 0; v < kProducers; ++v)
-              part[v] = sm.loop.sp[v][okt][oht][16 * (olq0 + q) + (oli ^ (4 * (olq0 + q)))];
+              part[v] = sm.loop.sp[sp_at(v, oht, q, oli, kk)];
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[4 * q + r] = (part[0][r] + part[1][r]) + (part[2][r] + part[3][r]);
           }
           float mt = x[0];
 #pragma unroll
           for (int j = 1; j < KPL; ++j) mt = fmaxf(mt, x[j]);
-          // lanes of one head differ in lane bits log2(HPO) .. 5
-          if constexpr (HPO == 4) mt = max2(mt, dpp_ror4(mt), pinf);
-          mt = max2(mt, dpp_ror8(mt), pinf);
-          mt = max_over_quarters(mt, pinf) * a.c;
+          mt = max_lanes<LPH>(mt) * a.c;
           const float mnew = mt > m_own + kMaxSlack ? mt : m_own;
           const bool mv = mnew != m_own;
           // mnew is -inf only while every key so far was skipped (x = -inf);
@@ -399,7 +396,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
           float ps = (pw[0] + pw[1]) + (pw[2] + pw[3]);
 #pragma unroll
           for (int q = 1; q < NQ; ++q) ps += (pw[4 * q] + pw[4 * q + 1]) + (pw[4 * q + 2] + pw[4 * q + 3]);
-          lsum = lsum * alpha + ps;
+          lsum = __builtin_fmaf(lsum, alpha, ps);
           m_own = mnew;
           uint16_t* prow = &sm.loop.p[oh * kPitch + KPL * kk];
           if constexpr (KPL == 8) {
@@ -416,10 +413,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       }
 
       // ---- weight sum of the owned head over its lanes (fixed order), sink
-      float l = lsum;
-      if constexpr (HPO == 4) l += dpp_ror4(l);
-      l += dpp_ror8(l);
-      l = sum_over_quarters(l);
+      float l = sum_lanes<LPH>(lsum);
       if (a.sink && !kSplit) {  // the split form folds the sink in when merging
         const float s2 = a.sink[h0 + oh] * kLog2e;
         const float mf = fmaxf(m_own, s2);
