@@ -64,6 +64,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWavesPerBlock = 4;
 
@@ -101,6 +102,33 @@ __device__ __forceinline__ uint32_t encode8(const u32x4 w, float mul) {
   return c;
 }
 
+// The same codes for groups with e <= kBf16MaxE, from the packed bf16
+// values: gfx950's v_cvt_scalef32_pk_fp4_bf16 with scale 2^e rounds the
+// exact quotient x / 2^e to E2M1.  For those e the fp32 quotient x * 2^-e
+// is exact too (|x| >= 2^-133, a multiple of 2^-133, so x * 2^-e is a
+// multiple of 2^-149 and never underflows), so the two round the same value;
+// a device sweep of every bf16 value against encode8 for every e in [-126,
+// 126] found no difference up to 16 and, from 17 on, only negatives whose
+// fp32 quotient underflows to -0.0 (code 0 there, 8 from the converter).  A
+// zero's sign is cleared first (-0.0 encodes as code 0): for each half,
+// (|h| + 0x7FFF) has bit 15 set exactly when |h| is not 0.
+constexpr int kBf16MaxE = 16;
+__device__ __forceinline__ uint32_t encode8_bf16(const u32x4 w, float scale) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t m = w[k] & 0x7FFF7FFFu;
+    const uint32_t z = ((m + 0x7FFF7FFFu) & w[k]) | m;
+    switch (k) {
+      case 0: c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, z), scale, 0); break;
+      case 1: c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, z), scale, 1); break;
+      case 2: c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, z), scale, 2); break;
+      default: c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, z), scale, 3); break;
+    }
+  }
+  return c;
+}
+
 // Quantizes the 512-value slice held by the wave (16 bytes per lane):
 // returns the lane's code dword (codes of its 8 values) and, in `sdw`, the
 // scale dword that the lanes 12 mod 16 store (scale bytes of groups
@@ -112,9 +140,12 @@ __device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw)
   e = max(e, -126);
   if (amax == 0u || nonfinite) e = 0;
   const uint32_t scale_byte = nonfinite ? 0xFFu : (uint32_t)(e + 127);
-  const float mul = as_f32((uint32_t)(127 - e) << 23);  // 2^-e, e in [-126, 126]
-
-  uint32_t codes = encode8(w, mul);
+  uint32_t codes;
+  if (e <= kBf16MaxE) {
+    codes = encode8_bf16(w, as_f32((uint32_t)(127 + e) << 23));  // 2^e
+  } else {
+    codes = encode8(w, as_f32((uint32_t)(127 - e) << 23));  // 2^-e, e in [17, 126]
+  }
   if (nonfinite) codes = 0u;
 
   // Scale dword k = groups 4k..4k+3 = lanes 16k, 16k+4, 16k+8, 16k+12.

@@ -58,7 +58,52 @@ def test_solo_sweep_exhaustive(device):
     assert (got == want).all(), first_mismatch(got, want, 272)
 
 
-@pytest.mark.parametrize("k", [0, 125, -126, 17, -100, 60])
+def anchored_groups(k):
+    """Groups of 32 bf16 patterns [6*2^k, x...] over every finite bf16 x with
+    |x| <= 6*2^k (scale exponent k), the anchor at a varying lane position."""
+    f = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    anchor = np.float32(6.0 * 2.0 ** k)  # exact
+    cands = np.flatnonzero(np.isfinite(f) & (np.abs(f.astype(np.float64)) <= 6.0 * 2.0 ** k)).astype(np.uint16)
+    abits = np.uint16(np.array([anchor], dtype=np.float32).view(np.uint32)[0] >> 16)
+    per = 31
+    ngroups = -(-cands.size // per)
+    groups = np.zeros((ngroups, 32), dtype=np.uint16)
+    body = np.zeros(ngroups * per, dtype=np.uint16)
+    body[: cands.size] = cands
+    body = body.reshape(ngroups, per)
+    for gi in range(ngroups):
+        groups[gi] = np.insert(body[gi], gi % 32, abits)
+    return groups
+
+
+@pytest.mark.parametrize("k", [16, 17])
+def test_mixed_scale_exponents_in_a_wave(device, k):
+    """Tokens whose groups alternate between scale exponents k - 16 .. k and
+    k + 1 (every finite bf16 below each anchor): a wave's groups take both
+    encodings (up to e = 16 from the packed bf16 values, above from fp32
+    quotients), including the boundary e = 16 / 17."""
+    lo, hi = anchored_groups(k - 16), anchored_groups(k + 1)
+    mid = anchored_groups(k)
+    n = min(lo.shape[0], hi.shape[0], mid.shape[0]) // 8 * 8
+    groups = np.empty((3 * n, 32), dtype=np.uint16)
+    groups[0::3], groups[1::3], groups[2::3] = lo[:n], hi[:n], mid[:n]
+    ntok = groups.shape[0] // 16
+    src = groups[: ntok * 16].reshape(ntok, 512)
+    slots = np.random.default_rng(k).permutation(ntok).astype(np.int64)
+    log(f"store mixed exponents k={k}: {ntok} tokens")
+    got, want = run_both(device, src, slots, 1, ntok, ntok, ntok * 272)
+    assert (got == want).all(), first_mismatch(got, want, 272)
+    # the slot-order form quantizes the same way
+    inv = ops.mxfp4_inverse_workspace(1, ntok, device)
+    ops.mxfp4_build_inverse(i64_dev(slots, device), 1, ntok, inv)
+    dev_cache = u8_dev(np.full(ntok * 272, 0xA5, dtype=np.uint8), device)
+    ops.mxfp4_store_by_slot(bf16_dev(src, device), ntok, inv, dev_cache, 1, ntok, ntok)
+    torch.cuda.synchronize()
+    got = dev_cache.cpu().numpy()
+    assert (got == want).all(), first_mismatch(got, want, 272)
+
+
+@pytest.mark.parametrize("k", [0, 125, -126, 16, 17, -100, 60])
 def test_anchored_sweep(device, k):
     """Groups [6*2^k, x...] over every finite bf16 x with |x| <= 6*2^k, with
     the anchor at a varying lane position."""
