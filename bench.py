@@ -63,8 +63,9 @@ def parse():
     p.add_argument("--counters", action="store_true",
                    help="for rocprofv3 --pmc: a 1 GiB copy (calibration) then 3 launches of each "
                         "kernel of --counter-set, no JSON")
-    p.add_argument("--counter-set", choices=("store", "companions", "probes", "pads"), default="store",
-                   help="what --counters runs: the store step, the companions, or the probes")
+    p.add_argument("--counter-set", choices=("store", "companions", "probes", "pads", "lds"), default="store",
+                   help="what --counters runs: the store step, the companions, the probes, the "
+                        "pad-heavy batches, or the LDS access patterns")
     p.add_argument("--only", default="",
                    help="comma-separated companion names to run (default: all)")
     p.add_argument("--probes", action="store_true",
@@ -687,6 +688,68 @@ def run_probes(torch, workloads, n: int, counters: bool = False) -> None:
 
 
 LDS_ITERS = 1024
+
+
+def lds_patterns():
+    """Lane -> 16-byte LDS unit maps of the attention kernel's accesses (32
+    heads per workgroup), its earlier layouts, and plain strides.  Partial
+    scores: 4 producers x 4 key tiles x 2 head tiles x 64 lanes of f32x4.
+    Weights: bf16 rows 160 bytes apart, [head][key]."""
+    def cur_slot(v, ht, q, li, kk):  # rows of 128 B per (producer, head tile, sub-block, head)
+        return (((v * 2 + ht) * 2 + q) * 16 + li) * 8 + (kk ^ (li & 7))
+    pats = {
+        "contiguous": lambda l: l,
+        "stride_32B": lambda l: 2 * l,
+        "stride_64B": lambda l: 4 * l,
+        "rows_160B_apart": lambda l: 10 * l,
+        # current: writer lane (li, lq) of key tile 2, head tile 1; owner lane
+        # 8hh + kk of producer 0 reading producer 1's partials
+        "partial_write": lambda l: cur_slot(0, 1, (l >> 4) & 1, l & 15, 4 + ((l >> 4) >> 1)),
+        "partial_read": lambda l: cur_slot(1, 0, 0, l >> 3, l & 7),
+        # earlier: slot 16lq + (li ^ 4lq) per (producer, key tile, head
+        # tile), owner lane hh + 8kk
+        "partial_write_earlier": lambda l: ((0 * 4 + 2) * 2 + 1) * 64 + 16 * (l >> 4) + ((l & 15) ^ (4 * (l >> 4))),
+        "partial_read_earlier": lambda l: (((l >> 3) >> 1) * 2) * 64 + 16 * (2 * ((l >> 3) & 1))
+                                          + ((l & 7) ^ (4 * (2 * ((l >> 3) & 1)))),
+        # the first layout tried with owner lane 8hh + kk: slot
+        # 16lq + ((li + 4kt + lq) & 15)
+        "partial_read_first_try": lambda l: (((l & 7) >> 1) * 2) * 64 + 16 * (2 * (l & 1))
+                                            + (((l >> 3) + 4 * ((l & 7) >> 1) + 2 * (l & 1)) & 15),
+        "weights_write": lambda l: ((l >> 3) * 160 + 16 * (l & 7)) // 16,
+        "weights_write_earlier": lambda l: ((l & 7) * 160 + 16 * (l >> 3)) // 16,
+        "weights_read": lambda l: ((l & 15) * 160 + 16 * (l >> 4)) // 16,
+    }
+    return {k: [f(l) for l in range(64)] for k, f in pats.items()}
+
+
+def run_lds_patterns(torch):
+    """One read and one write launch per pattern of lds_patterns() (2,048
+    one-wave workgroups, LDS_PATTERN_ITERS accesses per lane), for
+    rocprofv3's SQ_LDS_BANK_CONFLICT; dispatch order = print order."""
+    import ctypes
+    from mxfp4_paged_cache_store_amd import build
+
+    if not os.path.exists(build.PROBE_LIB_PATH):
+        build.build_probes()
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    lib.probe_lds_pattern.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_lds_pattern.restype = ctypes.c_int
+    out = torch.empty(2048 * 64, dtype=torch.int32, device="cuda")
+    st = int(torch.cuda.current_stream().cuda_stream)
+    for name, units in lds_patterns().items():
+        if min(units) < 0 or max(units) >= 4096:
+            raise ValueError(f"pattern {name} leaves the 64 KB probe buffer")
+        dev = torch.tensor(units, dtype=torch.int32, device="cuda")
+        for write in (0, 1):
+            if lib.probe_lds_pattern(dev.data_ptr(), write, 2048, LDS_PATTERN_ITERS, out.data_ptr(), st) != 0:
+                raise RuntimeError("probe launch failed")
+            torch.cuda.synchronize()
+            print(json.dumps({"lds_pattern": name, "access": "write" if write else "read",
+                              "workgroups": 2048, "iters": LDS_PATTERN_ITERS}), flush=True)
+
+
+LDS_PATTERN_ITERS = 1000
 ATTN_WARMUP = 40   # untimed launches of the attention companion before its timed ones
 ATTN_REPS = 20
 
@@ -783,6 +846,10 @@ def main():
         del a, b
         if args.counter_set == "probes":
             run_probes(torch, workloads, n, counters=True)
+            print("[bench] counters run done", file=sys.stderr, flush=True)
+            return
+        if args.counter_set == "lds":
+            run_lds_patterns(torch)
             print("[bench] counters run done", file=sys.stderr, flush=True)
             return
         if args.counter_set == "pads":

@@ -27,6 +27,9 @@
 //                    ds_read_b128, ds_read_b64_tr_b16, ds_write_b128,
 //                    ds_write_b64, or 16x16x32 bf16 MFMAs alone -- the
 //                    budget a kernel that stages operands in LDS works with.
+//   probe_lds_pattern  one ds_read_b128 / ds_write_b128 per lane at a given
+//                    lane -> 16-byte-unit map, repeated: the bank conflicts
+//                    of an access pattern (rocprofv3 SQ_LDS_BANK_CONFLICT).
 //   probe_empty      an empty kernel: the launch floor of a given grid.
 // The written bytes depend on the loaded ones so no load can be dropped; a
 // read-only probe writes one dword only when its checksum hits a constant.
@@ -234,6 +237,31 @@ __global__ __launch_bounds__(1024) void probe_lds_kernel(uint32_t* __restrict__ 
   out[(size_t)blockIdx.x * 1024 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ __float_as_uint(s);
 }
 
+// LDS bank conflicts of one access pattern: one wave per workgroup, 64 KB
+// of LDS; lane l reads or writes the 16-byte unit units[l] (0..4095) `iters`
+// times (ds_read_b128 / ds_write_b128), its offset passing through an empty
+// asm each time.  Run under rocprofv3's SQ_LDS_BANK_CONFLICT counter.
+template <bool kWrite>
+__global__ __launch_bounds__(64) void probe_lds_pattern_kernel(const uint32_t* __restrict__ units,
+                                                               uint32_t* __restrict__ out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[16384];
+  const uint32_t lane = threadIdx.x;
+  for (int i = lane; i < 16384; i += 64) lds[i] = (uint32_t)i;
+  __syncthreads();
+  uint32_t off = (units[lane] & 4095u) * 16u;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(off));
+    if constexpr (kWrite)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(lds) + off) = u32x4{(uint32_t)it, lane, 2u, 1u};
+    else
+      acc ^= *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(lds) + off);
+  }
+  __syncthreads();
+  if constexpr (kWrite) acc[0] = lds[lane];
+  out[(size_t)blockIdx.x * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 __global__ __launch_bounds__(256) void probe_empty_kernel() {}
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -7; }
@@ -348,6 +376,20 @@ int probe_lds(int kind, int64_t blocks, int iters, uint32_t* out, void* stream) 
     case 4: hipLaunchKernelGGL(probe_lds_kernel<4>, grid, block, 0, (hipStream_t)stream, out, iters); break;
     default: return -1;
   }
+  return status(hipGetLastError());
+}
+
+// LDS access-pattern probe: `blocks` one-wave workgroups, each lane l
+// repeating a 16-byte read (write == 0) or write at unit units[l] (a device
+// array of 64 entries in [0, 4096)) `iters` times; `out` holds blocks * 64
+// dwords.
+int probe_lds_pattern(const uint32_t* units, int write, int64_t blocks, int iters, uint32_t* out, void* stream) {
+  if (!units || !out || blocks <= 0 || blocks > 0x7FFFFFFF || iters <= 0) return -1;
+  const dim3 grid((unsigned)blocks), block(64);
+  if (write)
+    hipLaunchKernelGGL(probe_lds_pattern_kernel<true>, grid, block, 0, (hipStream_t)stream, units, out, iters);
+  else
+    hipLaunchKernelGGL(probe_lds_pattern_kernel<false>, grid, block, 0, (hipStream_t)stream, units, out, iters);
   return status(hipGetLastError());
 }
 

@@ -61,5 +61,5 @@ def test_probe_library_exports():
         build.build_probes()
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
     for name in ("probe_read", "probe_write", "probe_copy_rows", "probe_copy_wide", "probe_copy_expand",
-                 "probe_scatter_dwords", "probe_lds", "probe_empty"):
+                 "probe_scatter_dwords", "probe_lds", "probe_lds_pattern", "probe_empty"):
         assert hasattr(lib, name), name
