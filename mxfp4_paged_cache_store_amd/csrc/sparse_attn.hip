@@ -21,14 +21,16 @@
 //            against query fragments of the same dims (B operand, all HB
 //            heads, in registers), so every key is unpacked once.  Each
 //            producer copies its slice of the packed rows to LDS for the
-//            consumer of that slice and writes its partial scores to LDS.
-//            After a barrier producer pd owns heads HB/4*pd .. +HB/4-1 over
-//            all 64 keys: it adds the four partials of its (head, key)
-//            pairs in a fixed order and runs the softmax in base 2 -- the
-//            tile maximum of a head is reduced among the head's lanes, the
-//            running maximum moves only past a slack, and when it moves the
-//            new maxima are published with a flag; weights go to LDS as
-//            bf16.
+//            consumer of that slice and writes its partial scores to LDS
+//            (a skipped key's partial is -inf in producer pd for key tile pd
+//            and an exact 0 elsewhere).  After a barrier producer pd owns
+//            heads HB/4*pd .. +HB/4-1 over all 64 keys: it adds the four
+//            partials of its (head, key) pairs in a fixed order and runs the
+//            softmax in base 2 on those sums, scaled only in the weights'
+//            exponent -- the tile maximum of a head is reduced among the
+//            head's consecutive lanes, the running maximum moves only past a
+//            slack, and when it moves the new maxima are published with a
+//            flag; weights go to LDS as bf16.
 //   consumers (waves 4..7) own output dims 128*(w-4) .. +127 of all HB
 //            heads and compute O += P V for tile s - 1.  The B operand needs
 //            8 consecutive keys of one dim (a transpose of the cache layout):
@@ -188,7 +190,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
   if (threadIdx.x < 2) sm.loop.moved[threadIdx.x] = 0u;  // ordered by the first barrier
 
   // Producers and consumers run separate loops (so their registers are not
-  // live at the same time) with the same barriers: three per step, step s
+  // live at the same time) with the same barriers: two per step, step s
   // producing tile s and consuming tile s - 1, then two in the epilogue.
   // The producer body is instantiated per slice (pd a constant: its LDS
   // offsets and own-tile choice fold away).
@@ -200,7 +202,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // query fragments of those dims for all HB heads (B operand: head li,
       // dims 128pd + 32lq + 8ks .. +7 at k-step ks).  Its MFMAs give partial
       // scores over its 128 dims for all 64 keys; the four partials meet in
-      // LDS, where producer w sums those of key tile w (keys 16w .. +15).
+      // LDS, where each producer sums those of the heads it owns.
       constexpr int pd = decltype(pdc)::value;
       bf16x8 qf[HT][4];
       // After the first barrier of a step producer pd owns heads HPO*pd ..
