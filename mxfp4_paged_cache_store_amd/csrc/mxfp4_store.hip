@@ -25,7 +25,10 @@
 //     quotient carries no sign, and gfx950's v_cvt_scalef32_pk_fp4_f32 (scale
 //     1.0) rounds two quotients to E2M1 codes, nearest-even, sign kept:
 //     four conversions give the lane's 8 codes as one dword, which is code
-//     dword l of the row (low nibble = lower index).
+//     dword l of the row (low nibble = lower index).  For e <= 16 (every
+//     group below 6 * 2^16) the quotient never underflows, and the packed
+//     bf16 values go straight to v_cvt_scalef32_pk_fp4_bf16 with scale 2^e,
+//     zeros' signs cleared first: the same codes (encode8_bf16).
 //   * The 16 scale bytes are gathered with row_shr DPP moves into four
 //     dwords held by lanes 12, 28, 44 and 60.  The row is written as whole
 //     dwords: 64 code dwords + 4 scale dwords.  When a wave's tokens fill
