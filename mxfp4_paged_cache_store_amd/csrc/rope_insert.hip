@@ -226,22 +226,40 @@ struct Nvfp4 {
 
     // r / S without a division.  S has at most 4 significant bits, so in the
     // fp32 normal range r / S is never halfway between two floats and lies
-    // at least 2^-30 (relative) from every such halfway point: r * (1/S) in
-    // fp64, with 1/S known to within 2^-43, rounds to the same float.  1/S
-    // is taken low by 2^-51..2^-43 so that the product is always smaller in
-    // magnitude than r / S; then in the subnormal range, where only the sign
-    // reaches the code, a quotient of exactly half the smallest subnormal
-    // rounds to zero as round-to-nearest-even does.  (1/S: one Newton step
-    // in fp64 from the 1-ulp hardware reciprocal; the step's residual is
-    // exact and leaves the estimate low by its error squared.)
-    const double sd = S, y0 = __builtin_amdgcn_rcpf(S);
-    const double inv_s = __builtin_fma(y0, __builtin_fma(-sd, y0, 1.0), y0) * (1.0 - 0x1p-50);
+    // at least 2^-30 (relative) from every such halfway point.  In fp32:
+    // q0 = r * y0 (y0 the 1-ulp hardware reciprocal), the residual
+    // e = r - q0 * S in one fma (exact: it has at most 6 significant bits
+    // unless it underflows), then q = q0 + e * y0 in one fma, within 2^-45
+    // of r / S: it rounds to the same float.  Where q is not a normal float
+    // (a zero, subnormal, infinite or NaN quotient, or a residual that
+    // underflowed) the lane redoes its 8 values as r * (1/S) in fp64 with
+    // 1/S known to within 2^-43 and taken low by 2^-51..2^-43, so that the
+    // product is always smaller in magnitude than r / S; then in the
+    // subnormal range, where only the sign reaches the code, a quotient of
+    // exactly half the smallest subnormal rounds to zero as
+    // round-to-nearest-even does.  (1/S there: one Newton step in fp64 from
+    // y0; the step's residual is exact and leaves the estimate low by its
+    // error squared.)  A host check restates both and compares the codes
+    // with those of the correctly rounded quotient.
+    const float y0 = __builtin_amdgcn_rcpf(S);
     float y[8];
+    bool slow = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float q = (float)((double)r[i] * inv_s);
-      if (kNaN) q = (q == q) ? q : 0.0f;  // NaN -> code 0 (the converter gives 7)
-      y[i] = q + 0.0f;                    // -0.0 -> +0.0: sign only below zero
+      const float q0 = r[i] * y0;
+      const float e = __builtin_fmaf(-q0, S, r[i]);
+      y[i] = __builtin_fmaf(e, y0, q0);
+      slow |= !__builtin_isnormal(y[i]);
+    }
+    if (slow) {
+      const double sd = S, yd = y0;
+      const double inv_s = __builtin_fma(yd, __builtin_fma(-sd, yd, 1.0), yd) * (1.0 - 0x1p-50);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float q = (float)((double)r[i] * inv_s);
+        if (kNaN) q = (q == q) ? q : 0.0f;  // NaN -> code 0 (the converter gives 7)
+        y[i] = q + 0.0f;                    // -0.0 -> +0.0: sign only below zero
+      }
     }
     // The converter saturates: magnitudes above 6, up to +-Inf, give code 7
     // with the sign (checked on the device), as the E2M1 rule asks.

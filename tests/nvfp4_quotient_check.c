@@ -1,13 +1,21 @@
 /* nvfp4_quotient_check.c -- host-side check of the division-free quotient
  * the NVFP4 RoPE insert kernel uses for y = r / S (S a positive E4M3 value).
  *
- * The kernel forms q = fp32(fp64(r) * inv_s), where
- *   y0    = the hardware fp32 reciprocal of S (within 1 ulp of 1/S),
+ * With y0 the hardware fp32 reciprocal of S (within 1 ulp of 1/S), the
+ * kernel forms, in fp32 with single roundings,
+ *   q0 = r * y0,  e = fma(-q0, S, r)  (exact: at most 6 significant bits),
+ *   q  = fma(e, y0, q0),
+ * and keeps q when it is a normal float.  Otherwise (a zero, subnormal,
+ * infinite or NaN quotient: underflowing residuals, or r too large) it takes
  *   inv_s = fma(y0, fma(-S, y0, 1), y0) * (1 - 2^-50)      (all in fp64),
+ *   q     = fp32(fp64(r) * inv_s),
  * and quantises q to E2M1 (nearest, ties to even, saturating at 6, sign bit
  * only for q < 0).  The NVFP4 definition (DeepSeek-V4.1 insert page, NVFP4
  * branch) quantises the correctly rounded fp32 quotient r / S instead.  This
- * program checks that both give the same 4-bit code.
+ * program checks that both give the same 4-bit code, and counts the kept
+ * quotients of magnitude 2^-100 or more that differ from r / S in any bit
+ * (expected: none; below that only the sign reaches the code, and a kept q
+ * is normal, nonzero and of the quotient's sign).
  *
  * y0 is unknown beyond its 1-ulp bound, so every float within 2 ulps of 1/S
  * is tried.  Scale invariance: for normal quotients the outcome depends on
@@ -44,12 +52,17 @@ static double inv_s_of(float S, float y0f) {
   return fma(y0, fma(-sd, y0, 1.0), y0) * (1.0 - 0x1p-50);
 }
 
-static long long cases, bad;
+static long long cases, bad, bits;
 
-static void check(float r, float S, double inv_s) {
+static void check(float r, float S, float y0) {
   const float truth = r / S;
-  const float q = (float)((double)r * inv_s);
+  const float q0 = r * y0;
+  const float e = fmaf(-q0, S, r);
+  float q = fmaf(e, y0, q0);
+  const int fast = fpclassify(q) == FP_NORMAL;
+  if (!fast) q = (float)((double)r * inv_s_of(S, y0));
   ++cases;
+  if (fast && fabsf(truth) >= 0x1p-100f && u_of(q) != u_of(truth)) ++bits;
   if (e2m1(truth) != e2m1(q)) {
     if (bad < 10)
       fprintf(stderr, "mismatch r=%a S=%a truth=%a q=%a\n", (double)r, (double)S, (double)truth, (double)q);
@@ -78,10 +91,9 @@ int main(int argc, char** argv) {
     float c[5];
     const int nc = candidates(S, c);
     for (int k = 0; k < nc; ++k) {
-      const double inv_s = inv_s_of(S, c[k]);
       for (uint32_t u = lo; u < hi; u += stride) {
-        check(f_of(u), S, inv_s);
-        check(-f_of(u), S, inv_s);
+        check(f_of(u), S, c[k]);
+        check(-f_of(u), S, c[k]);
       }
     }
   }
@@ -93,12 +105,12 @@ int main(int argc, char** argv) {
     float c[5];
     const int nc = candidates(S, c);
     for (int k = 0; k < nc; ++k) {
-      const double inv_s = inv_s_of(S, c[k]);
+      const float y0 = c[k];
       const float specials[] = {0.0f, INFINITY, NAN, 3.4028235e38f, 0x1p-149f, 0x1p-126f, 6.0f * S, 6.5f * S,
                                 5.0f * S, 0.25f * S};
       for (unsigned i = 0; i < sizeof specials / sizeof specials[0]; ++i) {
-        check(specials[i], S, inv_s);
-        check(-specials[i], S, inv_s);
+        check(specials[i], S, y0);
+        check(-specials[i], S, y0);
       }
       /* r near 2^-150 * S (the quotient that rounds to 0 or to 2^-149) */
       const double edge = 0x1p-150 * (double)S;
@@ -106,16 +118,24 @@ int main(int argc, char** argv) {
       for (int d = -4096; d <= 4096; ++d) {
         const float r = f_of(u_of(e) + (uint32_t)d);
         if (!(r > 0.0f)) continue;
-        check(r, S, inv_s);
-        check(-r, S, inv_s);
+        check(r, S, y0);
+        check(-r, S, y0);
       }
       /* every subnormal float as r (quotients far below 2^-126) */
       for (uint32_t u = 1; u < 0x00800000u; u += 97u * stride) {
-        check(f_of(u), S, inv_s);
-        check(-f_of(u), S, inv_s);
+        check(f_of(u), S, y0);
+        check(-f_of(u), S, y0);
+      }
+      /* quotients around the bottom of the normal range (r near S * 2^-126) */
+      const float nb = (float)(0x1p-126 * (double)S);
+      for (int d = -4096; d <= 4096; ++d) {
+        const float r = f_of(u_of(nb) + (uint32_t)d);
+        if (!(r > 0.0f)) continue;
+        check(r, S, y0);
+        check(-r, S, y0);
       }
     }
   }
-  printf("cases %lld mismatches %lld\n", cases, bad);
-  return bad ? 1 : 0;
+  printf("cases %lld mismatches %lld quotients_off_by_bits %lld\n", cases, bad, bits);
+  return bad || bits ? 1 : 0;
 }
