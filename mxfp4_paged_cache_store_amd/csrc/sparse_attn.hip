@@ -181,10 +181,11 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
   const uint32_t blk = kSplit ? blk_all / nsplit : blk_all;
   const int64_t t = blk / nhb;
   const int h0 = (int)(blk % nhb) * HB;
-  const int64_t ntile_all = (a.topk + kTile - 1) / kTile;
-  const int64_t per_split = (ntile_all + nsplit - 1) / nsplit;
-  const int64_t tile0 = (int64_t)split * per_split;
-  const int64_t ntile = kSplit ? (tile0 < ntile_all ? min(per_split, ntile_all - tile0) : 0) : ntile_all;
+  // topk <= 2^24: tile counts fit in 32 bits (and compare in scalar registers)
+  const int32_t ntile_all = (int32_t)((a.topk + kTile - 1) / kTile);
+  const int32_t per_split = (ntile_all + (int32_t)nsplit - 1) / (int32_t)nsplit;
+  const int32_t tile0 = (int32_t)split * per_split;
+  const int32_t ntile = kSplit ? (tile0 < ntile_all ? min(per_split, ntile_all - tile0) : 0) : ntile_all;
 
   const int32_t* idx_row = a.indices + t * a.idx_stride;
   if (threadIdx.x < 2) sm.loop.moved[threadIdx.x] = 0u;  // ordered by the first barrier
@@ -238,8 +239,8 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // through a raw buffer over the tile's listed entries (topk <= 2^24):
       // unconditional (lanes past the list read 0 and return -1) so the
       // compiler's wait counts stay exact.  Loads run only when topk >= 1.
-      auto load_index = [&](int64_t tile) -> int32_t {
-        const int64_t j0 = (tile0 + tile) * kTile, rem = a.topk - j0;
+      auto load_index = [&](int32_t tile) -> int32_t {
+        const int64_t j0 = (int64_t)(tile0 + tile) * kTile, rem = a.topk - j0;
         const uint32_t n = rem <= 0 ? 0u : rem >= kTile ? (uint32_t)kTile : (uint32_t)rem;
         const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_at(idx_row + j0, 4u * n), 4 * lane, 0, 0);
         return (uint32_t)lane < n ? v : -1;
@@ -309,7 +310,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         g_idx = load_index(1);
       }
 
-      for (int64_t step = 0; step <= ntile; ++step) {
+      for (int32_t step = 0; step <= ntile; ++step) {
         const int pb = (int)(step & 1), cb = pb ^ 1;
         uint64_t valid = 0;  // bit k: key k of the tile is listed
         if (step < ntile) {
@@ -479,7 +480,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
     // Tile step - 1 is consumed before the first barrier, beside the
     // producers' scores of tile step (its buffers are rewritten only in the
     // next step).
-    for (int64_t step = 0; step <= ntile; ++step) {
+    for (int32_t step = 0; step <= ntile; ++step) {
       const int cb = (int)(step & 1) ^ 1;
       if (step > 0) {
         // ---- O rows follow the running maxima (re-read only when a
