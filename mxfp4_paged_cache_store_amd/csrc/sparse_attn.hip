@@ -55,9 +55,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kRowBytes = 272;
@@ -70,6 +67,14 @@ __device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+__device__ __forceinline__ u32x4 unpack8(uint32_t codes, uint32_t scale_byte) {
+  const float scale = as_f32(scale_byte << 23);
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3))};
+}
+
 // Byte `sel` of a code dword -> bf16 pair (the selector must be a constant;
 // after unrolling the switch folds away).
 __device__ __forceinline__ uint32_t cvt_byte(uint32_t codes, float scale, int sel) {
@@ -78,47 +83,6 @@ __device__ __forceinline__ uint32_t cvt_byte(uint32_t codes, float scale, int se
     case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
     case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
     default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
-  }
-}
-
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-
-// Four fp32 -> four OCP E4M3 bytes (round to nearest even), a in the low byte.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  i16x2 p = {0, 0};
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, a, b, 1.0f, false);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, c, d, 1.0f, true);
-  return __builtin_bit_cast(uint32_t, p);
-}
-
-// Scale bytes (E8M0) of the two E4M3 terms of a 32-dim query block whose
-// largest magnitude has bf16 bits m (sign cleared), m in [2^E, 2^(E+1)):
-// the high term's scale 2^(E-7) brings the block into [0, 256), the low
-// term's is 2^-4 of it; neither goes below 2^-127.
-__device__ __forceinline__ uint32_t qhi_scale_byte(uint32_t m) { return (uint32_t)max((int)(m >> 7) - 7, 0); }
-__device__ __forceinline__ uint32_t qlo_scale_byte(uint32_t bh) { return bh > 4u ? bh - 4u : 0u; }
-
-// 16 bf16 query values of one block (w; the first in the low half of w[0].x)
-// -> E4M3 bytes of the high term (hi) and of the low term (lo), for scale
-// bytes bh, bl: x = q * 2^(127-bh) (exact, below 256), hi = E4M3(x), and lo =
-// E4M3((x - hi) * 2^(bh-bl)), the remainder being exact in fp32.  A value of
-// 8 significant bits at x >= 2^-6 has a remainder of at most 3 significant
-// bits on the grid of its own last bit, so lo holds it exactly; below that
-// the two terms miss q by at most half of lo's smallest step, 2^(bl-137).
-__device__ __forceinline__ void split_query16(const u32x4 (&w)[2], uint32_t bh, uint32_t bl, uint32_t* hi, uint32_t* lo) {
-  const float down = as_f32((254u - bh) << 23);
-  const float up = as_f32((127u + bh - bl) << 23);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t u0 = w[d >> 1][2 * (d & 1)], u1 = w[d >> 1][2 * (d & 1) + 1];
-    const float x0 = as_f32(u0 << 16) * down, x1 = as_f32(u0 & 0xFFFF0000u) * down;
-    const float x2 = as_f32(u1 << 16) * down, x3 = as_f32(u1 & 0xFFFF0000u) * down;
-    hi[d] = e4m3x4(x0, x1, x2, x3);
-    const f32x2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi[d], 1.0f, false);
-    const f32x2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi[d], 1.0f, true);
-    lo[d] = e4m3x4((x0 - h01[0]) * up, (x1 - h01[1]) * up, (x2 - h23[0]) * up, (x3 - h23[1]) * up);
   }
 }
 
@@ -241,6 +205,7 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
       // scores over its 128 dims for all 64 keys; the four partials meet in
       // LDS, where each producer sums those of the heads it owns.
       constexpr int pd = decltype(pdc)::value;
+      bf16x8 qf[HT][4];
       // After the first barrier of a step producer pd owns heads HPO*pd ..
       // +HPO-1 over all 64 keys: lane (hh, kk) = hh*LPH + kk holds head
       // HPO*pd + hh and keys KPL*kk .. +KPL-1 (a head's lanes are LPH
@@ -255,60 +220,20 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
         return (((v * HT + ht) * NQ + q) * 16 + li) * LPH + (kk ^ (li & (LPH - 1)));
       };
       float m_own = -INFINITY, lsum = 0.0f;
-      // Query terms, the B operand of the block-scaled MFMA (OCP E4M3).  In
-      // that instruction's fp8 layout lane (li, lq) holds, of head 16ht + li,
-      // dims 128pd + 16lq .. +15 in bytes 0..15 and dims 128pd + 64 + 16lq ..
-      // +15 in bytes 16..31, and the scale byte of block lq (dims 128pd + 32lq
-      // .. +31), which the instruction applies to that block's dims in every
-      // lane.  Each bf16 value is the sum of a high and a low E4M3 term with
-      // per-block scales (split_query16): exact from 2^-14 of the block's
-      // largest magnitude up, and otherwise within 2^-21 of that magnitude
-      // (or 2^-137 where the scales reach 2^-127).
-      i32x8 qhi[HT], qlo[HT];
-      uint32_t qsh[HT], qsl[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const uint16_t* qh = a.q + t * a.q_token_stride + (int64_t)(h0 + 16 * ht + li) * a.q_head_stride +
-                             128 * pd + 16 * lq;
-        u32x4 w[2][2];
+                             128 * pd + 32 * lq;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+        for (int ks = 0; ks < 4; ++ks)
+          qf[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 8 * ks));
+      }
+      if (a.q_xor != 0u || a.q_and != ~0u) {  // a negative or zero scale
 #pragma unroll
-          for (int p = 0; p < 2; ++p) w[hf][p] = *reinterpret_cast<const u32x4*>(qh + 64 * hf + 8 * p);
-        if (a.q_xor != 0u || a.q_and != ~0u) {  // a negative or zero scale
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) w[hf][p] = (w[hf][p] ^ a.q_xor) & a.q_and;
-        }
-        // Largest magnitude (bf16 bits) of each half, then of each block:
-        // half hf of lanes (li, 2j) and (li, 2j + 1) makes up block 2hf + j.
-        uint32_t m[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          uint32_t x = 0u;
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) x = pk_max_u16(x, w[hf][p][c] & 0x7FFF7FFFu);
-          x = max(x & 0xFFFFu, x >> 16);
-          const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-          m[hf] = max(sw[0], sw[1]);
-        }
-        // Block lq's maximum, for the lane's scale operands.
-        const auto b01 = __builtin_amdgcn_permlane32_swap(m[0], m[0], false, false);
-        const auto b23 = __builtin_amdgcn_permlane32_swap(m[1], m[1], false, false);
-        const uint32_t mb = lq == 0 ? b01[0] : lq == 1 ? b01[1] : lq == 2 ? b23[0] : b23[1];
-        qsh[ht] = qhi_scale_byte(mb);
-        qsl[ht] = qlo_scale_byte(qsh[ht]);
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const uint32_t bh = qhi_scale_byte(m[hf]);
-          split_query16(w[hf], bh, qlo_scale_byte(bh), hi + 4 * hf, lo + 4 * hf);
-        }
-        qhi[ht] = i32x8{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3], (int)hi[4], (int)hi[5], (int)hi[6], (int)hi[7]};
-        qlo[ht] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)lo[4], (int)lo[5], (int)lo[6], (int)lo[7]};
+          for (int ks = 0; ks < 4; ++ks)
+            qf[ht][ks] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, qf[ht][ks]) ^ a.q_xor) & a.q_and);
       }
       // Slot index of key 16lq + li (one load per lane covers the tile),
       // through a raw buffer over the tile's listed entries (topk <= 2^24):
@@ -418,17 +343,14 @@ void sparse_mla_attn_kernel(const AttnArgs a) {
             f32x4 s[HT];
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) s[ht] = kt == pd ? bias : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            // A operand: the key's 32 E2M1 codes of dims 128pd + 32lq .. +31
-            // and their E8M0 byte (the instruction's fp4 layout is the
-            // cache's), against both query terms.
-            const i32x8 kc = {(int)g_cw[kt][0], (int)g_cw[kt][1], (int)g_cw[kt][2], (int)g_cw[kt][3], 0, 0, 0, 0};
-            const int sbyte = (int)g_sb[kt];
+            const uint32_t sbyte = g_sb[kt];
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-              s[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, qhi[ht], s[ht], 4, 0, 0, sbyte, 0, (int)qsh[ht]);
+            for (int ks = 0; ks < 4; ++ks) {
+              const bf16x8 kf = __builtin_bit_cast(bf16x8, unpack8(g_cw[kt][ks], sbyte));
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-              s[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, qlo[ht], s[ht], 4, 0, 0, sbyte, 0, (int)qsl[ht]);
+              for (int ht = 0; ht < HT; ++ht)
+                s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ht][ks], s[ht], 0, 0, 0);
+            }
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
               sm.loop.sp[sp_at(pd, ht, ((16 * kt + 4 * lq) % KPL) / 4, li, (16 * kt + 4 * lq) / KPL)] = s[ht];
