@@ -29,9 +29,12 @@
 //     group below 6 * 2^16) the quotient never underflows, and the packed
 //     bf16 values go straight to v_cvt_scalef32_pk_fp4_bf16 with scale 2^e,
 //     zeros' signs cleared first: the same codes (encode8_bf16).
-//   * The 16 scale bytes are gathered with row_shr DPP moves into four
-//     dwords held by lanes 12, 28, 44 and 60.  The row is written as whole
-//     dwords: 64 code dwords + 4 scale dwords.  When a wave's tokens fill
+//   * The scatter form with one token per pass writes a row as 64 code
+//     dwords and one byte store of the 16 scale bytes (each lane stores its
+//     group's byte; the four lanes of a group write the same byte).  Where a
+//     pass holds several tokens, and in the slot-order form, the scale bytes
+//     are gathered with row_shr DPP moves into four dwords held by lanes 12,
+//     28, 44 and 60, and the row is written as whole dwords.  When a wave's tokens fill
 //     consecutive slots, or the whole batch's rows fit in the Infinity
 //     Cache, the stores are plain (L2 and that cache merge neighbouring rows
 //     into whole lines); other scattered rows use non-temporal stores.
@@ -133,16 +136,16 @@ __device__ __forceinline__ uint32_t encode8_bf16(const u32x4 w, float scale) {
 }
 
 // Quantizes the 512-value slice held by the wave (16 bytes per lane):
-// returns the lane's code dword (codes of its 8 values) and, in `sdw`, the
-// scale dword that the lanes 12 mod 16 store (scale bytes of groups
-// 4k..4k+3 for lane 16k+12).
-__device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw) {
+// returns the lane's code dword (codes of its 8 values) and, in
+// `scale_byte`, the scale byte of the lane's group (lanes 4g .. 4g+3 hold
+// group g).
+__device__ __forceinline__ uint32_t quantize_slice_sb(const u32x4 w, uint32_t& scale_byte) {
   const uint32_t amax = group_amax_bits(w);
   const bool nonfinite = amax >= 0x7F80u;
   int e = (int)(amax >> 7) - 129 + ((amax & 0x7Fu) > 64u ? 1 : 0);
   e = max(e, -126);
   if (amax == 0u || nonfinite) e = 0;
-  const uint32_t scale_byte = nonfinite ? 0xFFu : (uint32_t)(e + 127);
+  scale_byte = nonfinite ? 0xFFu : (uint32_t)(e + 127);
   uint32_t codes;
   if (e <= kBf16MaxE) {
     codes = encode8_bf16(w, as_f32((uint32_t)(127 + e) << 23));  // 2^e
@@ -150,8 +153,15 @@ __device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw)
     codes = encode8(w, as_f32((uint32_t)(127 - e) << 23));  // 2^-e, e in [17, 126]
   }
   if (nonfinite) codes = 0u;
+  return codes;
+}
 
-  // Scale dword k = groups 4k..4k+3 = lanes 16k, 16k+4, 16k+8, 16k+12.
+// As quantize_slice_sb, with the scale bytes gathered into the scale dword
+// that the lanes 12 mod 16 store: dword k = groups 4k..4k+3 = lanes 16k,
+// 16k+4, 16k+8, 16k+12.
+__device__ __forceinline__ uint32_t quantize_slice(const u32x4 w, uint32_t& sdw) {
+  uint32_t scale_byte;
+  const uint32_t codes = quantize_slice_sb(w, scale_byte);
   sdw = dpp<kRowShr12>(scale_byte) | (dpp<kRowShr8>(scale_byte) << 8) |
         (dpp<kRowShr4>(scale_byte) << 16) | (scale_byte << 24);
   return codes;
@@ -274,26 +284,25 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void mxfp4_store_kernel(con
   for (int p = 0; p < kTokensPerWave; ++p) {
     if constexpr (kToksPerPass == 1) {
       // Raw buffer over the token's row (empty when skipped): the hardware
-      // range check drops the stores of a skipped token and of every lane
-      // but the scale lanes at the out-of-range offset kDrop.  The two cache
-      // policies are distinct instructions, so they stay separate.
-      constexpr uint32_t kDrop = 0x7FFFFFF0u;
+      // range check drops the stores of a skipped token.  Every lane stores
+      // its group's scale byte (the four lanes of a group the same byte at
+      // the same offset), one byte store per slice.  The two cache policies
+      // are distinct instructions, so they stay separate.
       const bool ok = row_off[p] >= 0;
       const __amdgpu_buffer_rsrc_t rs =
           buffer_at(a.cache + (ok ? row_off[p] : 0), ok ? (uint32_t)kPitch : 0u);
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub) {
-        uint32_t sdw;
-        const uint32_t codes = quantize_slice(v[p][sub], sdw);
+        uint32_t sb;
+        const uint32_t codes = quantize_slice_sb(v[p][sub], sb);
         const uint32_t code_off = sub * 256 + lane_in_tok * 4;
-        const uint32_t scale_off =
-            (lane_in_tok & 15) == 12 ? LATENT / 2 + sub * 16 + (lane_in_tok >> 4) * 4 : kDrop;
+        const uint32_t scale_off = LATENT / 2 + sub * 16 + (lane_in_tok >> 2);
         if (run) {
           __builtin_amdgcn_raw_buffer_store_b32(codes, rs, code_off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, scale_off, 0, 0);
         } else {
           __builtin_amdgcn_raw_buffer_store_b32(codes, rs, code_off, 0, kBufNT);
-          __builtin_amdgcn_raw_buffer_store_b32(sdw, rs, scale_off, 0, kBufNT);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, scale_off, 0, kBufNT);
         }
       }
     } else {
